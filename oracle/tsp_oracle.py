@@ -1,0 +1,162 @@
+"""fp64 CPU oracle for one rank's gated-MLP block under TSP weight sharding.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import or call
+this module: only the tests, the smoke check in ``__graft_entry__`` and the
+CPU-baseline leg of ``bench.py`` use it. It shares no code with the HIP path
+and imports nothing from the package.
+
+What it computes, and where that is stated:
+
+* "Folding Tensor and Sequence Parallelism for Memory-Efficient Transformer
+  Training & Inference", Abstract: TSP gives each rank one weight shard and
+  one sequence shard; in the gated MLP the weight shards travel round a ring
+  and each rank adds every shard's partial output into its own local result.
+  On one rank that is: for ring step k = 0..P-1, take shard ``order[k]``,
+  compute its partial output for the rank's tokens X, and add it into Y.
+* "Tensor Parallelism: Splitting the Math", section "One transformer MLP,
+  split across two GPUs (Megatron-style)", steps 2-6: the first weight
+  matrix is cut into column blocks, the nonlinearity is applied to each
+  block's output on its own, the second matrix is cut into the row blocks
+  that match, and the per-block products are partial sums whose total is the
+  output of the unsplit MLP.
+* Same page, section "Why the column-then-row split": the split has to be
+  by columns of the first matrix because the nonlinearity is elementwise and
+  does not distribute over a sum.
+
+Readings where the pages are silent (each also listed in the design doc):
+
+* gated activation = SwiGLU, h = SiLU(x.Wg) * (x.Wu) with SiLU(g) = g/(1+e^-g);
+* the non-gated block uses the tanh form of GeLU,
+  0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3)));
+* no bias terms; shard s owns hidden columns [s*F, (s+1)*F), F = f/P, for the
+  gate, up (or first) matrices and the same rows of the down (or second)
+  matrix;
+* ring order is the rotation order[k] = (r0 + k) mod P; any permutation of
+  the shards is accepted and gives the same result up to rounding;
+* orientation is Y = X W with W stored input x output.
+
+Every matrix product below is numpy's float64 matmul used as a library step;
+there is no blocking and no fusion beyond the shard loop the method itself
+describes. Inputs are promoted exactly to float64 (bf16 and fp32 values are
+representable exactly).
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+
+SQRT_2_OVER_PI = float(np.sqrt(2.0 / np.pi))
+GELU_TANH_CUBIC = 0.044715
+
+
+def f64(a) -> np.ndarray:
+    """Exact promotion of an fp32 (or already fp64) array to float64."""
+    return np.asarray(a, dtype=np.float64)
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    """SiLU (Swish with beta = 1): g / (1 + exp(-g)).
+
+    For very negative g, exp(-g) overflows to +inf and the quotient is -0.0,
+    which is the function's limit; the overflow warning is silenced.
+    """
+    g = f64(g)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def gelu_tanh(u: np.ndarray) -> np.ndarray:
+    """GeLU in its tanh form: 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3)))."""
+    u = f64(u)
+    return 0.5 * u * (1.0 + np.tanh(SQRT_2_OVER_PI * (u + GELU_TANH_CUBIC * u * u * u)))
+
+
+def ring_order(P: int, r0: int = 0) -> list:
+    """Rotated ring order: at step k the rank holds shard (r0 + k) mod P."""
+    return [(r0 + k) % P for k in range(P)]
+
+
+def _check_order(order: Sequence[int], P: int) -> list:
+    order = [int(s) for s in order]
+    if sorted(order) != list(range(P)):
+        raise ValueError(f"order {order} is not a permutation of 0..{P - 1}")
+    return order
+
+
+def shard_hidden(X, w_gate, w_up, s: int, F: int, act: str) -> np.ndarray:
+    """Hidden activations of shard s: the block's columns [s*F, (s+1)*F).
+
+    Column-parallel step (Megatron walk-through, steps 2-3): each shard owns
+    complete columns of X.W, so the nonlinearity is exact on its own block.
+    """
+    cols = slice(s * F, (s + 1) * F)
+    u = f64(X) @ f64(w_up[:, cols])
+    if act == "swiglu":
+        g = f64(X) @ f64(w_gate[:, cols])
+        return silu(g) * u
+    if act == "gelu_tanh":
+        return gelu_tanh(u)
+    raise ValueError(f"unknown activation {act!r}")
+
+
+def shard_partial(X, w_gate, w_up, w_down, s: int, F: int, act: str) -> np.ndarray:
+    """Shard s's partial output H_s . W_down[rows of shard s, :] (walk-through steps 4-5)."""
+    h = shard_hidden(X, w_gate, w_up, s, F, act)
+    return h @ f64(w_down[s * F:(s + 1) * F, :])
+
+
+def mlp_forward(X, w_gate, w_up, w_down, P: int, order: Optional[Sequence[int]] = None,
+                act: str = "swiglu", rows=None) -> np.ndarray:
+    """One rank's TSP gated-MLP forward in float64.
+
+    X: T x d; w_gate, w_up: d x f (w_gate None for gelu_tanh, where w_up is the
+    first matrix A); w_down: d x f's partner, f x d. P must divide f. The rank
+    visits shard order[k] at ring step k and adds its partial output into the
+    local fp64 accumulator Y (TSP abstract; walk-through step 6 with the
+    all-reduce replaced by this local sum). ``rows`` restricts the token rows
+    (rows are independent: the block is applied token by token).
+    """
+    X = f64(X)
+    if rows is not None:
+        X = X[np.asarray(rows)]
+    T, d = X.shape
+    f = w_up.shape[1]
+    if w_up.shape[0] != d or w_down.shape != (f, d):
+        raise ValueError("shape mismatch")
+    if act == "swiglu" and (w_gate is None or w_gate.shape != (d, f)):
+        raise ValueError("swiglu needs a d x f gate matrix")
+    if P < 1 or f % P:
+        raise ValueError(f"P={P} must divide f={f}")
+    F = f // P
+    order = _check_order(ring_order(P) if order is None else order, P)
+    Y = np.zeros((T, d), dtype=np.float64)
+    for s in order:
+        Y += shard_partial(X, w_gate, w_up, w_down, s, F, act)
+    return Y
+
+
+def tsp_simulate(X_full, w_gate, w_up, w_down, P: int, act: str = "swiglu",
+                 r0: int = 0) -> np.ndarray:
+    """All P ranks of a TSP group, simulated one after another.
+
+    The sequence (S tokens) is cut into P contiguous sequence shards; rank r
+    holds tokens [r*S/P, (r+1)*S/P) and, since the shards circulate, visits
+    weight shard (r + r0 + k) mod P at step k. Returns the ranks' outputs
+    concatenated in sequence order. P must divide S.
+    """
+    X_full = f64(X_full)
+    S = X_full.shape[0]
+    if S % P:
+        raise ValueError("P must divide the sequence length")
+    n = S // P
+    outs = []
+    for r in range(P):
+        outs.append(mlp_forward(X_full[r * n:(r + 1) * n], w_gate, w_up, w_down, P,
+                                ring_order(P, (r + r0) % P), act))
+    return np.concatenate(outs, axis=0)
+
+
+def flops(T: int, d: int, f: int, act: str) -> int:
+    """GEMM flops of one forward: 2 per multiply-add, three matrices (two for GeLU)."""
+    return 2 * (3 if act == "swiglu" else 2) * T * d * f
