@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Throughput of one rank's TSP gated-MLP block on one MI355X.
+
+A step is one full forward of the block over one batch of synthetic tokens:
+the fused gate/up kernel over every weight shard (visited in ring order) and
+the down kernel that accumulates all shards' partial outputs into the fp32 Y.
+Inputs, packed weights and workspace are resident in HBM before timing.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line. The default workload is the Llama-3-8B-shaped SwiGLU
+block (T=4096 tokens, d=4096, f=14336, P=8 shards, ring start 3), reported in
+TFLOP/s; ``--workload decode70b`` runs the T=16 weight-streaming workload,
+reported in GB/s. The ``roofline`` object is for the dominant kernel, timed
+with HIP events recorded by the library on the stream the kernel runs on.
+``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
+workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sharded gated-MLP TFLOP/s + % bf16 MFMA peak (large T); HBM GB/s % peak (T=16)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector / MFMA, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+KERNEL_SOURCES = {
+    "gateup_tiled": ["gemm_tiled.hip", "common.h"],
+    "down_tiled": ["gemm_tiled.hip", "common.h"],
+    "skinny_gateup": ["gemm_skinny.hip", "common.h"],
+    "skinny_down": ["gemm_skinny.hip", "common.h"],
+    "gateup_f32": ["gemm_f32.hip", "common.h"],
+    "down_f32": ["gemm_f32.hip", "common.h"],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "sharded_transformer_mlp_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_work(w, kernel: str, T: int):
+    """Algorithmic (flops, bytes) of one launch of `kernel` on workload w."""
+    es = 2 if w.dtype == "bf16" else 4
+    n_gu = 2 if w.act == "swiglu" else 1
+    if kernel in ("gateup_tiled", "skinny_gateup", "gateup_f32"):
+        flops = 2 * T * w.d * w.f * n_gu
+        byts = n_gu * w.d * w.f * es + T * w.d * es + T * w.f * es      # W_gu, X, H out
+    else:
+        flops = 2 * T * w.f * w.d
+        byts = w.f * w.d * es + T * w.f * es + T * w.d * 4                 # W_d, H in, Y out
+    return flops, byts
+
+
+def read_traffic(workload_name: str, kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel source has changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload_name}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, inp, budget_s: float):
+    """Time the fp64 oracle on the first n token rows, n sized to ~budget_s."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    x = inp.x.float().numpy()
+    wg = None if inp.w_gate is None else inp.w_gate.float().numpy()
+    wu, wd = inp.w_up.float().numpy(), inp.w_down.float().numpy()
+    order = w.order()
+
+    def run(n):
+        t = time.perf_counter()
+        oracle.mlp_forward(x[:n], wg, wu, wd, w.P, order, w.act)
+        return time.perf_counter() - t
+
+    n = min(w.T, 16)
+    dt = run(n)
+    while dt < 0.25 * budget_s and n < w.T:
+        n = min(w.T, max(n + 1, int(n * min(8.0, 0.6 * budget_s / max(dt, 1e-3)))))
+        dt = run(n)
+    if w.T <= 64:                               # decode-like: report bytes streamed per second
+        value = w.bytes(n) / dt / 1e9
+        unit = "GB/s"
+    else:
+        value = w.flops(n) / dt / 1e12
+        unit = "TFLOP/s"
+    return {"value": value, "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": f"first {n} of {w.T} token rows, full weights, fp64 numpy oracle, {dt:.2f} s"}
+
+
+def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    a.fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} copies of {nbytes} bytes")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true", help="only run the copy kernel used to scale counters")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(multi-GPU ring transfer is not part of this build)", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    import torch
+    from sharded_transformer_mlp_amd.binding import TspMLP
+    from sharded_transformer_mlp_amd.inputs import make_inputs, workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = workload(args.workload)
+    dev = torch.device("cuda:0")
+    log(f"workload {w.name}: generating inputs")
+    inp = make_inputs(w)
+    x = inp.x.to(dev)
+    wg = None if inp.w_gate is None else inp.w_gate.to(dev)
+    wu, wd = inp.w_up.to(dev), inp.w_down.to(dev)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    mlp = TspMLP(wg, wu, wd, w.P, order=w.order(), act=w.act, T_max=w.T)
+    pack_ms = (time.perf_counter() - t) * 1e3
+    del wg, wu, wd
+    y = torch.empty(w.T, w.d, dtype=torch.float32, device=dev)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        mlp.forward(x, y)
+    torch.cuda.synchronize()
+    mlp.read_timing()                        # discard warmup
+    mlp.set_timing(True)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        mlp.forward(x, y)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    mlp.set_timing(False)
+    ms = ev0.elapsed_time(ev1) / args.steps
+    kt = mlp.read_timing()
+    kernels = {k: v[0] / max(v[1], 1) for k, v in kt.items()}
+    log(f"ms/step {ms:.4f}; kernels {kernels}")
+
+    decode = w.T <= 64
+    if decode:
+        value, unit = w.bytes() / (ms * 1e-3) / 1e9, "GB/s"
+    else:
+        value, unit = w.flops() / (ms * 1e-3) / 1e12, "TFLOP/s"
+
+    dom = max(kernels, key=lambda k: kernels[k])
+    flops, byts = kernel_work(w, dom, w.T)
+    dom_s = kernels[dom] * 1e-3
+    if decode:
+        roof = {"bound": "hbm", "achieved": byts / dom_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        roof = {"bound": "mfma", "achieved": flops / dom_s / 1e12, "peak": peak, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = read_traffic(w.name, dom)
+    roof["kernel"] = dom
+    roof["kernel_ms"] = kernels[dom]
+    roof["algorithmic_bytes"] = byts
+    roof["algorithmic_flops"] = flops
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normal tokens and weights, bf16-rounded)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "P": w.P, "act": w.act,
+                   "ring_order": w.order(), "parallelism": "one TSP rank (shard loop on one GPU)"},
+        "pct_of_peak": (value / (PEAK_HBM_GBS if decode else PEAK_BF16_TFLOPS)) * 100.0,
+        "kernels_ms": kernels,
+        "pack_ms": pack_ms,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    mlp.close()
+    del x, y
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle)")
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

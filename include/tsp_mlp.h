@@ -1,0 +1,163 @@
+/*
+ * tsp_mlp.h -- C ABI of the MI355X (gfx950) hot path of one rank's gated-MLP
+ * block under tensor-and-sequence-parallel (TSP) weight sharding.
+ *
+ * What the library computes
+ * -------------------------
+ * "Folding Tensor and Sequence Parallelism for Memory-Efficient Transformer
+ * Training & Inference", Abstract: every rank holds one sequence shard of the
+ * tokens and, in the gated MLP, the weight shards travel round a ring while
+ * each rank adds every shard's partial output into its own local result.
+ * "Tensor Parallelism: Splitting the Math", section "One transformer MLP,
+ * split across two GPUs (Megatron-style)": shard s is a block of columns of
+ * the first matrix (here the gate and up projections) and the matching block
+ * of rows of the second (the down projection); the shards' products are
+ * partial sums whose total is the unsplit MLP.
+ *
+ * On one GPU the ring becomes a loop over shards resident in HBM. For the
+ * rank's T tokens X (T x d) and P shards of F = f / P hidden columns each,
+ *
+ *   Y = sum_{k=0..P-1} H_{order[k]} . Wd[rows of shard order[k], :]
+ *   H_s = SiLU(X . Wg[:, cols of s]) * (X . Wu[:, cols of s])     (SwiGLU)
+ *   H_s = GeLU_tanh(X . A[:, cols of s])                           (GeLU; A is w_up)
+ *
+ * with SiLU(g) = g / (1 + e^-g) and GeLU_tanh(u) = 0.5 u (1 + tanh(sqrt(2/pi)
+ * (u + 0.044715 u^3))). Shard s owns hidden columns [s*F, (s+1)*F). There are
+ * no biases. Products accumulate in fp32; Y is fp32. In the bf16 path the
+ * hidden activations are rounded to bf16 (round to nearest even) before the
+ * down projection.
+ *
+ * Layouts: all matrices are dense row-major with no padding. X is T x d in the
+ * handle's dtype, Y is T x d fp32, w_gate / w_up are d x f and w_down is f x d
+ * (orientation Y = X W, input x output).
+ *
+ * Errors: every call returns a tsp_status_t and nothing else crosses the ABI
+ * (no exceptions, no aborts). Arguments are checked before any HIP call; on a
+ * failed check nothing is launched and nothing is allocated.
+ * tsp_last_error() returns a message for the calling thread's last failure.
+ */
+#ifndef TSP_MLP_H
+#define TSP_MLP_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TSP_OK = 0,
+    TSP_ERR_INVALID_ARG = 1,   /* null pointer, bad size, order not a permutation, ... */
+    TSP_ERR_UNSUPPORTED = 2,   /* a shape the kernels do not tile (see tsp_mlp_validate) */
+    TSP_ERR_OOM = 3,           /* device allocation failed; nothing is leaked */
+    TSP_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} tsp_status_t;
+
+typedef enum { TSP_ACT_SWIGLU = 0, TSP_ACT_GELU_TANH = 1 } tsp_act_t;
+
+/* storage type of X and the weights; Y is always fp32 */
+typedef enum { TSP_DTYPE_F32 = 0, TSP_DTYPE_BF16 = 1 } tsp_dtype_t;
+
+/* forward path selection (tsp_mlp_set_path) */
+typedef enum { TSP_PATH_AUTO = 0, TSP_PATH_TILED = 1, TSP_PATH_SKINNY = 2 } tsp_path_t;
+
+typedef struct tsp_mlp* tsp_mlp_t;   /* opaque handle */
+
+/*
+ * Pure host check of a create() argument set; makes no HIP call.
+ * has_gate: 1 if a gate matrix will be passed. order: host array of P entries
+ * or NULL (NULL means 0, 1, ..., P-1).
+ * Returns TSP_ERR_INVALID_ARG when: T_max < 1, d < 1, f < 1, P < 1, P does not
+ * divide f, act or dtype unknown, order not a permutation of 0..P-1, has_gate
+ * differs from (act == SWIGLU).
+ * Returns TSP_ERR_UNSUPPORTED (bf16 only) when d or F = f/P is not a multiple
+ * of 64. The fp32 path takes any shape.
+ */
+tsp_status_t tsp_mlp_validate(int64_t T_max, int64_t d, int64_t f, int32_t P,
+                              int32_t act, int32_t dtype, const int32_t* order,
+                              int32_t has_gate);
+
+/*
+ * Create a handle for one rank's block and copy the weights into the
+ * library's packed layout. Shards are packed one after another, each as one
+ * contiguous record (gate/up columns of the shard, then its down rows), which
+ * is the unit a ring step would move between ranks.
+ *
+ * out      : receives the handle; set to NULL on any failure.
+ * T_max    : largest T any forward on this handle will pass (sizes the
+ *            workspace that holds the hidden activations, T_max x f).
+ * d, f, P  : hidden size, FFN width, number of weight shards.
+ * act      : tsp_act_t.   dtype: tsp_dtype_t.
+ * order    : host array of P int32, the ring order (order[k] = shard used at
+ *            step k), a permutation of 0..P-1; NULL = 0..P-1. Copied.
+ * w_gate   : device pointer, d x f row-major, dtype; must be NULL for GeLU.
+ * w_up     : device pointer, d x f row-major (the matrix A for GeLU).
+ * w_down   : device pointer, f x d row-major (the matrix B for GeLU).
+ * stream   : HIP stream for the packing kernels; create synchronises it
+ *            before returning, so the caller may then free its weights.
+ *            It is also the default stream of later forwards.
+ * Ownership: the caller keeps its weight buffers; the library owns the packed
+ * copy and the workspace until tsp_mlp_destroy. Weight pointers must be
+ * 16-byte aligned device memory on the current device.
+ */
+tsp_status_t tsp_mlp_create(tsp_mlp_t* out, int64_t T_max, int64_t d, int64_t f,
+                            int32_t P, int32_t act, int32_t dtype,
+                            const int32_t* order, const void* w_gate,
+                            const void* w_up, const void* w_down,
+                            hipStream_t stream);
+
+/*
+ * Y = block(X) for T tokens, visiting the shards in the handle's ring order.
+ * X: device, T x d row-major, dtype. Y: device, T x d row-major fp32,
+ * overwritten (not accumulated into). Both 16-byte aligned; Y must not
+ * overlap X. 0 <= T <= T_max; T == 0 is a no-op.
+ * stream: where the kernels run; NULL means the stream given to create.
+ * Asynchronous: returns once the kernels are queued. One forward at a time
+ * per handle (the hidden-activation workspace is per handle); use one handle
+ * per concurrent stream.
+ */
+tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y,
+                             hipStream_t stream);
+
+/* Synchronise the handle's stream and free everything it owns. NULL is a no-op. */
+tsp_status_t tsp_mlp_destroy(tsp_mlp_t h);
+
+/* Choose the forward path: AUTO (skinny when T <= 16 in bf16), TILED or SKINNY.
+ * SKINNY needs bf16 and T <= 16 at forward time (TSP_ERR_UNSUPPORTED otherwise). */
+tsp_status_t tsp_mlp_set_path(tsp_mlp_t h, int32_t path);
+
+/* Tuning and test hook for the bf16 tiled path: fix the tile shape of the
+ * gate/up and down kernels (-1 = choose per forward from T and the shape).
+ * Shapes: 0 = 256 features x 256 tokens, 1 = 256 x 128, 2 = 128 x 128,
+ * 3 = 64 x 128. TSP_ERR_UNSUPPORTED if the shape does not divide the shard's
+ * packed width (gate/up) or d (down), or for an fp32 handle. */
+tsp_status_t tsp_mlp_set_tiles(tsp_mlp_t h, int32_t gateup_tile, int32_t down_tile);
+
+/* Read back the packed weights' size in bytes and the workspace size in bytes. */
+tsp_status_t tsp_mlp_sizes(tsp_mlp_t h, int64_t* packed_bytes, int64_t* workspace_bytes);
+
+/*
+ * Kernel timing, for measurement. When enabled, each forward records a pair of
+ * HIP events around every kernel it launches, on the stream the kernel runs
+ * on. tsp_mlp_read_timing synchronises the handle's event pool, adds up the
+ * elapsed time per kernel name since the last read, and resets the sums.
+ * names: caller array of max_kernels char buffers of 64 bytes each;
+ * total_ms / launches: caller arrays of max_kernels entries; *n_kernels gets
+ * the number of distinct kernels filled in.
+ */
+tsp_status_t tsp_mlp_set_timing(tsp_mlp_t h, int32_t enable);
+tsp_status_t tsp_mlp_read_timing(tsp_mlp_t h, int32_t max_kernels, char (*names)[64],
+                                 double* total_ms, int64_t* launches, int32_t* n_kernels);
+
+/* Static text for a status code. */
+const char* tsp_status_string(tsp_status_t s);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* tsp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSP_MLP_H */

@@ -1,0 +1,167 @@
+"""ctypes binding over libtsp_mlp.so (argument marshalling only).
+
+Every step of the forward runs in the library's HIP kernels; this module only
+turns torch tensors into device pointers and the current torch stream into a
+hipStream_t. It raises if the library is missing: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsp_mlp.so")
+
+TSP_OK, TSP_ERR_INVALID_ARG, TSP_ERR_UNSUPPORTED, TSP_ERR_OOM, TSP_ERR_HIP = range(5)
+ACT = {"swiglu": 0, "gelu_tanh": 1}
+DTYPE = {"f32": 0, "bf16": 1}
+PATH = {"auto": 0, "tiled": 1, "skinny": 2}
+
+# Every symbol the header declares, with its ctypes signature.
+_i64, _i32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+SIGNATURES = {
+    "tsp_mlp_validate": (_i32, [_i64, _i64, _i64, _i32, _i32, _i32, ctypes.POINTER(_i32), _i32]),
+    "tsp_mlp_create": (_i32, [ctypes.POINTER(_vp), _i64, _i64, _i64, _i32, _i32, _i32,
+                              ctypes.POINTER(_i32), _vp, _vp, _vp, _vp]),
+    "tsp_mlp_forward": (_i32, [_vp, _i64, _vp, _vp, _vp]),
+    "tsp_mlp_destroy": (_i32, [_vp]),
+    "tsp_mlp_set_path": (_i32, [_vp, _i32]),
+    "tsp_mlp_set_tiles": (_i32, [_vp, _i32, _i32]),
+    "tsp_mlp_sizes": (_i32, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+    "tsp_mlp_set_timing": (_i32, [_vp, _i32]),
+    "tsp_mlp_read_timing": (_i32, [_vp, _i32, _vp, ctypes.POINTER(ctypes.c_double),
+                                   ctypes.POINTER(_i64), ctypes.POINTER(_i32)]),
+    "tsp_status_string": (ctypes.c_char_p, [_i32]),
+    "tsp_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class TspError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[status {status}] {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sharded_transformer_mlp_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != TSP_OK:
+        raise TspError(status, lib().tsp_last_error().decode())
+
+
+def _order_array(order: Optional[Sequence[int]]):
+    if order is None:
+        return None
+    arr = (_i32 * len(order))(*[int(s) for s in order])
+    return ctypes.cast(arr, ctypes.POINTER(_i32)), arr
+
+
+def validate(T_max, d, f, P, act="swiglu", dtype="bf16", order=None, has_gate=None) -> int:
+    """Pure host check (no HIP call); returns the status code."""
+    a = ACT.get(act, act) if isinstance(act, str) else act
+    t = DTYPE.get(dtype, dtype) if isinstance(dtype, str) else dtype
+    if has_gate is None:
+        has_gate = a == ACT["swiglu"]
+    o = _order_array(order)
+    return lib().tsp_mlp_validate(T_max, d, f, P, a, t, o[0] if o else None, int(bool(has_gate)))
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+class TspMLP:
+    """One rank's sharded gated-MLP block on the GPU.
+
+    w_gate / w_up: d x f, w_down: f x d, CUDA tensors of the storage dtype
+    (torch.float32 or torch.bfloat16), row-major contiguous. w_gate is None
+    for the GeLU block. ``order`` is the ring order (default 0..P-1).
+    """
+
+    def __init__(self, w_gate, w_up, w_down, P: int, order=None, act: str = "swiglu",
+                 T_max: int = 1, stream=None):
+        import torch
+        self.dtype = {torch.float32: "f32", torch.bfloat16: "bf16"}[w_up.dtype]
+        self.tdtype = w_up.dtype
+        self.d, self.f = w_up.shape
+        self.P, self.act = P, act
+        self.order = list(range(P)) if order is None else [int(s) for s in order]
+        for w in (w_gate, w_up, w_down):
+            if w is not None:
+                if not (w.is_cuda and w.is_contiguous() and w.dtype == self.tdtype):
+                    raise ValueError("weights must be contiguous CUDA tensors of one dtype")
+        o = _order_array(self.order)
+        h = _vp()
+        self._stream = _stream_ptr(stream)
+        check(lib().tsp_mlp_create(ctypes.byref(h), int(T_max), int(self.d), int(self.f), int(P),
+                                   ACT[act], DTYPE[self.dtype], o[0],
+                                   None if w_gate is None else w_gate.data_ptr(),
+                                   w_up.data_ptr(), w_down.data_ptr(), self._stream))
+        self.handle = h
+        self.T_max = int(T_max)
+
+    def set_path(self, path: str) -> None:
+        check(lib().tsp_mlp_set_path(self.handle, PATH[path]))
+
+    def set_tiles(self, gateup: int = -1, down: int = -1) -> None:
+        check(lib().tsp_mlp_set_tiles(self.handle, int(gateup), int(down)))
+
+    def forward(self, x, y=None, stream=None):
+        import torch
+        T = x.shape[0]
+        if x.dtype != self.tdtype or not x.is_cuda or not x.is_contiguous() or x.shape[1] != self.d:
+            raise ValueError("x must be a contiguous CUDA tensor T x d of the handle's dtype")
+        if y is None:
+            y = torch.empty(T, self.d, dtype=torch.float32, device=x.device)
+        elif y.dtype != torch.float32 or not y.is_contiguous() or tuple(y.shape) != (T, self.d):
+            raise ValueError("y must be a contiguous fp32 T x d tensor")
+        check(lib().tsp_mlp_forward(self.handle, T, x.data_ptr(), y.data_ptr(), _stream_ptr(stream)))
+        return y
+
+    __call__ = forward
+
+    def sizes(self):
+        p, w = _i64(), _i64()
+        check(lib().tsp_mlp_sizes(self.handle, ctypes.byref(p), ctypes.byref(w)))
+        return p.value, w.value
+
+    def set_timing(self, enable: bool) -> None:
+        check(lib().tsp_mlp_set_timing(self.handle, int(bool(enable))))
+
+    def read_timing(self, max_kernels: int = 8):
+        """{kernel name: (total ms, launches)} since the last read."""
+        names = (ctypes.c_char * 64 * max_kernels)()
+        ms = (ctypes.c_double * max_kernels)()
+        n_l = (_i64 * max_kernels)()
+        n = _i32()
+        check(lib().tsp_mlp_read_timing(self.handle, max_kernels, names, ms, n_l, ctypes.byref(n)))
+        return {bytes(names[i]).split(b"\0")[0].decode(): (ms[i], n_l[i]) for i in range(n.value)}
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            check(lib().tsp_mlp_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

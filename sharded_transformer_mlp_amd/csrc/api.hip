@@ -1,0 +1,394 @@
+// C ABI of the sharded gated-MLP hot path: argument checks, the per-handle
+// packed weights and workspace, and the per-forward launch plan.
+#include "tsp_mlp.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tsp_status_t fail(tsp_status_t s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+tsp_status_t hip_fail(hipError_t e, const char* what) {
+    return fail(TSP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int kMaxTimingPairs = 8192;
+
+struct KernelTotal {
+    std::string name;
+    double ms = 0.0;
+    int64_t launches = 0;
+};
+
+struct EventPair {
+    hipEvent_t start = nullptr, stop = nullptr;
+    int slot = 0;
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+struct tsp_mlp {
+    int64_t T_max = 0, d = 0, f = 0, F = 0;
+    int32_t P = 0, act = 0, dtype = 0;
+    std::vector<int32_t> order;
+    int device = 0;
+    hipStream_t stream = nullptr;
+    int32_t* order_dev = nullptr;
+    void* packed = nullptr;
+    int64_t packed_bytes = 0, shard_elems = 0, down_off = 0;
+    void* work = nullptr;
+    int64_t work_bytes = 0;
+    int32_t path = TSP_PATH_AUTO;
+    int32_t cfg_gateup = -1, cfg_down = -1;   // tiled shapes; -1 = chosen per forward
+    // kernel timing
+    bool timing = false;
+    std::vector<EventPair> pool;
+    size_t used = 0;
+    std::vector<KernelTotal> totals;
+};
+
+namespace {
+
+int timing_slot(tsp_mlp* h, const char* name) {
+    for (size_t i = 0; i < h->totals.size(); ++i)
+        if (h->totals[i].name == name) return (int)i;
+    h->totals.push_back(KernelTotal{name, 0.0, 0});
+    return (int)h->totals.size() - 1;
+}
+
+tsp_status_t drain_timing(tsp_mlp* h) {
+    for (size_t i = 0; i < h->used; ++i) {
+        EventPair& e = h->pool[i];
+        hipError_t err = hipEventSynchronize(e.stop);
+        if (err != hipSuccess) return hip_fail(err, "hipEventSynchronize");
+        float ms = 0.f;
+        err = hipEventElapsedTime(&ms, e.start, e.stop);
+        if (err != hipSuccess) return hip_fail(err, "hipEventElapsedTime");
+        h->totals[e.slot].ms += ms;
+        h->totals[e.slot].launches += 1;
+    }
+    h->used = 0;
+    return TSP_OK;
+}
+
+// Runs `launch` on `st`, bracketed by events when timing is on.
+template <class Fn>
+tsp_status_t timed_launch(tsp_mlp* h, const char* name, hipStream_t st, Fn&& launch) {
+    EventPair* ep = nullptr;
+    if (h->timing) {
+        if (h->used == h->pool.size()) {
+            if (h->pool.size() < (size_t)kMaxTimingPairs) {
+                EventPair e;
+                hipError_t err = hipEventCreate(&e.start);
+                if (err == hipSuccess) err = hipEventCreate(&e.stop);
+                if (err != hipSuccess) return hip_fail(err, "hipEventCreate");
+                h->pool.push_back(e);
+            } else {
+                tsp_status_t s = drain_timing(h);   // pool full: fold the finished pairs in
+                if (s != TSP_OK) return s;
+            }
+        }
+        ep = &h->pool[h->used++];
+        ep->slot = timing_slot(h, name);
+        hipError_t err = hipEventRecord(ep->start, st);
+        if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
+    }
+    hipError_t err = launch();
+    if (err != hipSuccess) return fail(TSP_ERR_HIP, "launch of %s: %s", name, hipGetErrorString(err));
+    if (ep) {
+        err = hipEventRecord(ep->stop, st);
+        if (err != hipSuccess) return hip_fail(err, "hipEventRecord");
+    }
+    return TSP_OK;
+}
+
+void release(tsp_mlp* h) {
+    if (!h) return;
+    for (EventPair& e : h->pool) {
+        if (e.start) (void)hipEventDestroy(e.start);
+        if (e.stop) (void)hipEventDestroy(e.stop);
+    }
+    if (h->order_dev) (void)hipFree(h->order_dev);
+    if (h->packed) (void)hipFree(h->packed);
+    if (h->work) (void)hipFree(h->work);
+    delete h;
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = true;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) { ok = false; return; }
+        if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* tsp_status_string(tsp_status_t s) {
+    switch (s) {
+        case TSP_OK: return "ok";
+        case TSP_ERR_INVALID_ARG: return "invalid argument";
+        case TSP_ERR_UNSUPPORTED: return "unsupported shape";
+        case TSP_ERR_OOM: return "out of device memory";
+        case TSP_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char* tsp_last_error(void) { return g_last_error.c_str(); }
+
+tsp_status_t tsp_mlp_validate(int64_t T_max, int64_t d, int64_t f, int32_t P, int32_t act,
+                              int32_t dtype, const int32_t* order, int32_t has_gate) {
+    if (T_max < 1 || T_max > kMaxDim) return fail(TSP_ERR_INVALID_ARG, "T_max=%lld out of [1, 2^30]", (long long)T_max);
+    if (d < 1 || d > kMaxDim) return fail(TSP_ERR_INVALID_ARG, "d=%lld out of [1, 2^30]", (long long)d);
+    if (f < 1 || f > kMaxDim) return fail(TSP_ERR_INVALID_ARG, "f=%lld out of [1, 2^30]", (long long)f);
+    if (P < 1 || P > f) return fail(TSP_ERR_INVALID_ARG, "P=%d out of [1, f]", P);
+    if (f % P) return fail(TSP_ERR_INVALID_ARG, "P=%d does not divide f=%lld", P, (long long)f);
+    if (act != TSP_ACT_SWIGLU && act != TSP_ACT_GELU_TANH) return fail(TSP_ERR_INVALID_ARG, "unknown activation %d", act);
+    if (dtype != TSP_DTYPE_F32 && dtype != TSP_DTYPE_BF16) return fail(TSP_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if ((has_gate != 0) != (act == TSP_ACT_SWIGLU))
+        return fail(TSP_ERR_INVALID_ARG, act == TSP_ACT_SWIGLU ? "SwiGLU needs a gate matrix" : "GeLU takes no gate matrix");
+    if (order) {
+        std::vector<char> seen((size_t)P, 0);
+        for (int32_t k = 0; k < P; ++k) {
+            const int32_t s = order[k];
+            if (s < 0 || s >= P || seen[(size_t)s]) return fail(TSP_ERR_INVALID_ARG, "order is not a permutation of 0..P-1 (entry %d = %d)", k, s);
+            seen[(size_t)s] = 1;
+        }
+    }
+    const int64_t F = f / P;
+    if (dtype == TSP_DTYPE_BF16 && (d % 64 || F % 64))
+        return fail(TSP_ERR_UNSUPPORTED, "bf16 path needs d and F = f/P to be multiples of 64 (d=%lld, F=%lld)", (long long)d, (long long)F);
+    const int64_t es = dtype == TSP_DTYPE_BF16 ? 2 : 4;
+    if (T_max * f > (int64_t(1) << 40) / es)      // workspace bound keeps every index in range
+        return fail(TSP_ERR_UNSUPPORTED, "T_max * f too large");
+    return TSP_OK;
+}
+
+tsp_status_t tsp_mlp_create(tsp_mlp_t* out, int64_t T_max, int64_t d, int64_t f, int32_t P,
+                            int32_t act, int32_t dtype, const int32_t* order, const void* w_gate,
+                            const void* w_up, const void* w_down, hipStream_t stream) {
+    if (!out) return fail(TSP_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    tsp_status_t s = tsp_mlp_validate(T_max, d, f, P, act, dtype, order, w_gate != nullptr);
+    if (s != TSP_OK) return s;
+    if (!w_up || !w_down) return fail(TSP_ERR_INVALID_ARG, "weight pointer is NULL");
+    if (!aligned16(w_up) || !aligned16(w_down) || (w_gate && !aligned16(w_gate)))
+        return fail(TSP_ERR_INVALID_ARG, "weight pointers must be 16-byte aligned");
+
+    tsp_mlp* h = new (std::nothrow) tsp_mlp;
+    if (!h) return fail(TSP_ERR_OOM, "host allocation failed");
+    h->T_max = T_max; h->d = d; h->f = f; h->P = P; h->F = f / P;
+    h->act = act; h->dtype = dtype; h->stream = stream;
+    h->order.resize((size_t)P);
+    for (int32_t k = 0; k < P; ++k) h->order[(size_t)k] = order ? order[k] : k;
+    hipError_t e = hipGetDevice(&h->device);
+    if (e != hipSuccess) { release(h); return hip_fail(e, "hipGetDevice"); }
+
+    const bool swiglu = act == TSP_ACT_SWIGLU;
+    const int64_t F = h->F;
+    int64_t es;
+    if (dtype == TSP_DTYPE_BF16) {
+        const int64_t ngu = swiglu ? 2 * F : F;
+        h->down_off = ngu * d;
+        h->shard_elems = ngu * d + d * F;
+        es = 2;
+    } else {
+        h->down_off = (swiglu ? 2 : 1) * d * F;
+        h->shard_elems = (swiglu ? 3 : 2) * d * F;
+        es = 4;
+    }
+    h->packed_bytes = h->shard_elems * P * es;
+    h->work_bytes = T_max * f * es;
+
+    if ((e = hipMalloc(&h->order_dev, sizeof(int32_t) * (size_t)P)) != hipSuccess ||
+        (e = hipMalloc(&h->packed, (size_t)h->packed_bytes)) != hipSuccess ||
+        (e = hipMalloc(&h->work, (size_t)h->work_bytes)) != hipSuccess) {
+        const bool oom = e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation;
+        release(h);
+        (void)hipGetLastError();
+        return oom ? fail(TSP_ERR_OOM, "device allocation of packed weights / workspace failed")
+                   : hip_fail(e, "hipMalloc");
+    }
+    e = hipMemcpyAsync(h->order_dev, h->order.data(), sizeof(int32_t) * (size_t)P, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) { release(h); return hip_fail(e, "hipMemcpyAsync(order)"); }
+    if (dtype == TSP_DTYPE_BF16)
+        e = tsp::launch_pack_bf16(w_gate, w_up, w_down, h->packed, h->shard_elems, h->down_off, (int)d,
+                                  (int)f, (int)F, P, swiglu ? 1 : 0, stream);
+    else
+        e = tsp::launch_pack_f32(w_gate, w_up, w_down, h->packed, h->shard_elems, (int)d, (int)f,
+                                 (int)F, P, swiglu ? 1 : 0, stream);
+    if (e != hipSuccess) { release(h); return hip_fail(e, "pack launch"); }
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) { release(h); return hip_fail(e, "hipStreamSynchronize after packing"); }
+    *out = h;
+    return TSP_OK;
+}
+
+tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y, hipStream_t stream) {
+    if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
+    if (T < 0 || T > h->T_max) return fail(TSP_ERR_INVALID_ARG, "T=%lld out of [0, T_max=%lld]", (long long)T, (long long)h->T_max);
+    if (T == 0) return TSP_OK;
+    if (!X || !Y) return fail(TSP_ERR_INVALID_ARG, "X or Y is NULL");
+    if (!aligned16(X) || !aligned16(Y)) return fail(TSP_ERR_INVALID_ARG, "X and Y must be 16-byte aligned");
+    const int64_t es = h->dtype == TSP_DTYPE_BF16 ? 2 : 4;
+    const uintptr_t x0 = reinterpret_cast<uintptr_t>(X), x1 = x0 + (uintptr_t)(T * h->d * es);
+    const uintptr_t y0 = reinterpret_cast<uintptr_t>(Y), y1 = y0 + (uintptr_t)(T * h->d * 4);
+    if (x0 < y1 && y0 < x1) return fail(TSP_ERR_INVALID_ARG, "Y overlaps X");
+    hipStream_t st = stream ? stream : h->stream;
+    const bool swiglu = h->act == TSP_ACT_SWIGLU;
+
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return fail(TSP_ERR_HIP, "cannot select the handle's device");
+
+    tsp_status_t s;
+    if (h->dtype == TSP_DTYPE_BF16) {
+        tsp::Bf16Args a;
+        a.packed = static_cast<const uint16_t*>(h->packed);
+        a.x = static_cast<const uint16_t*>(X);
+        a.h = static_cast<uint16_t*>(h->work);
+        a.y = Y;
+        a.order = h->order_dev;
+        a.shard_elems = h->shard_elems;
+        a.down_off = h->down_off;
+        a.T = (int)T; a.d = (int)h->d; a.f = (int)h->f; a.F = (int)h->F; a.P = h->P;
+        a.swiglu = swiglu ? 1 : 0;
+        const bool sk_ok = T <= 16 && tsp::skinny_supported(a.d, a.F, a.P);
+        bool skinny = false;
+        if (h->path == TSP_PATH_SKINNY) {
+            if (!sk_ok) return fail(TSP_ERR_UNSUPPORTED, "skinny path needs T <= 16, d %% 1024 == 0 and P*F %% 1024 == 0");
+            skinny = true;
+        } else if (h->path == TSP_PATH_AUTO) {
+            skinny = sk_ok;
+        }
+        if (skinny) {
+            s = timed_launch(h, "skinny_gateup", st, [&] { return tsp::launch_gateup_skinny(a, st); });
+            if (s != TSP_OK) return s;
+            return timed_launch(h, "skinny_down", st, [&] { return tsp::launch_down_skinny(a, st); });
+        }
+        const int cg = h->cfg_gateup >= 0 ? h->cfg_gateup : tsp::choose_gateup_cfg(a.T, a.d, a.F, a.P, a.swiglu);
+        const int cd = h->cfg_down >= 0 ? h->cfg_down : tsp::choose_down_cfg(a.T, a.d, a.F);
+        const int64_t n_tok_tiles = (T + 63) / 64;
+        if (n_tok_tiles * (int64_t)(2 * a.f / 64 + a.d / 64) > INT32_MAX / 2)
+            return fail(TSP_ERR_UNSUPPORTED, "grid too large");
+        if (cg < 0 || cd < 0) return fail(TSP_ERR_UNSUPPORTED, "no tile shape fits d=%d F=%d", a.d, a.F);
+        s = timed_launch(h, "gateup_tiled", st, [&] { return tsp::launch_gateup_tiled(a, cg, st); });
+        if (s != TSP_OK) return s;
+        return timed_launch(h, "down_tiled", st, [&] { return tsp::launch_down_tiled(a, cd, st); });
+    }
+    if (h->path == TSP_PATH_SKINNY) return fail(TSP_ERR_UNSUPPORTED, "skinny path is bf16 only");
+    tsp::F32Args a;
+    a.packed = static_cast<const float*>(h->packed);
+    a.x = static_cast<const float*>(X);
+    a.h = static_cast<float*>(h->work);
+    a.y = Y;
+    a.order = h->order_dev;
+    a.shard_elems = h->shard_elems;
+    a.T = (int)T; a.d = (int)h->d; a.f = (int)h->f; a.F = (int)h->F; a.P = h->P;
+    a.swiglu = swiglu ? 1 : 0;
+    s = timed_launch(h, "gateup_f32", st, [&] { return tsp::launch_gateup_f32(a, st); });
+    if (s != TSP_OK) return s;
+    return timed_launch(h, "down_f32", st, [&] { return tsp::launch_down_f32(a, st); });
+}
+
+tsp_status_t tsp_mlp_destroy(tsp_mlp_t h) {
+    if (!h) return TSP_OK;
+    tsp_status_t s = TSP_OK;
+    {
+        DeviceGuard guard(h->device);
+        hipError_t e = hipStreamSynchronize(h->stream);
+        if (e != hipSuccess) s = hip_fail(e, "hipStreamSynchronize in destroy");
+        for (size_t i = 0; i < h->used; ++i) (void)hipEventSynchronize(h->pool[i].stop);
+        release(h);
+    }
+    return s;
+}
+
+tsp_status_t tsp_mlp_set_path(tsp_mlp_t h, int32_t path) {
+    if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
+    if (path != TSP_PATH_AUTO && path != TSP_PATH_TILED && path != TSP_PATH_SKINNY)
+        return fail(TSP_ERR_INVALID_ARG, "unknown path %d", path);
+    h->path = path;
+    return TSP_OK;
+}
+
+tsp_status_t tsp_mlp_set_tiles(tsp_mlp_t h, int32_t gateup_tile, int32_t down_tile) {
+    if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
+    if (h->dtype != TSP_DTYPE_BF16) return fail(TSP_ERR_UNSUPPORTED, "tile shapes apply to the bf16 path");
+    const bool swiglu = h->act == TSP_ACT_SWIGLU;
+    if (gateup_tile >= 0 && !tsp::gateup_cfg_fits(gateup_tile, (int)h->d, (int)h->F, swiglu))
+        return fail(TSP_ERR_UNSUPPORTED, "gate/up tile shape %d does not divide the shard", gateup_tile);
+    if (down_tile >= 0 && !tsp::down_cfg_fits(down_tile, (int)h->d, (int)h->F))
+        return fail(TSP_ERR_UNSUPPORTED, "down tile shape %d does not divide d", down_tile);
+    if (gateup_tile < -1 || down_tile < -1) return fail(TSP_ERR_INVALID_ARG, "tile shape < -1");
+    h->cfg_gateup = gateup_tile;
+    h->cfg_down = down_tile;
+    return TSP_OK;
+}
+
+tsp_status_t tsp_mlp_sizes(tsp_mlp_t h, int64_t* packed_bytes, int64_t* workspace_bytes) {
+    if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
+    if (packed_bytes) *packed_bytes = h->packed_bytes;
+    if (workspace_bytes) *workspace_bytes = h->work_bytes;
+    return TSP_OK;
+}
+
+tsp_status_t tsp_mlp_set_timing(tsp_mlp_t h, int32_t enable) {
+    if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
+    h->timing = enable != 0;
+    return TSP_OK;
+}
+
+tsp_status_t tsp_mlp_read_timing(tsp_mlp_t h, int32_t max_kernels, char (*names)[64], double* total_ms,
+                                 int64_t* launches, int32_t* n_kernels) {
+    if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
+    if (max_kernels < 0 || (max_kernels > 0 && (!names || !total_ms || !launches)) || !n_kernels)
+        return fail(TSP_ERR_INVALID_ARG, "bad output arrays");
+    DeviceGuard guard(h->device);
+    tsp_status_t s = drain_timing(h);
+    if (s != TSP_OK) return s;
+    int32_t n = 0;
+    for (KernelTotal& kt : h->totals) {
+        if (kt.launches == 0) continue;
+        if (n < max_kernels) {
+            snprintf(names[n], 64, "%s", kt.name.c_str());
+            total_ms[n] = kt.ms;
+            launches[n] = kt.launches;
+        }
+        ++n;
+        kt.ms = 0.0;
+        kt.launches = 0;
+    }
+    *n_kernels = n < max_kernels ? n : max_kernels;
+    return TSP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Device-side helpers shared by the gfx950 kernels of the sharded MLP path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// The packed bf16 weight layout is built from 16 x 32 "fragment blocks":
+// 16 output features (MFMA rows) by 32 reduction indices. A block is 512
+// elements (1 KiB) stored in the order the 64 lanes of a wavefront consume
+// them as the A operand of v_mfma_f32_16x16x32_bf16: lane l holds feature
+// l % 16 and the 8 consecutive reduction indices 8 * (l / 16) .. + 7, so a
+// wave reads one block with a single contiguous 16-byte-per-lane load.
+constexpr int FRAG_ELEMS = 512;
+
+__host__ __device__ inline int64_t frag_offset(int64_t n, int64_t k, int64_t kblocks) {
+    // element (feature n, reduction index k) in a matrix whose blocks run
+    // k-fastest: block (n / 16, k / 32) is at ((n / 16) * kblocks + k / 32).
+    return ((n >> 4) * kblocks + (k >> 5)) * FRAG_ELEMS + (((k & 31) >> 3) * 16 + (n & 15)) * 8 + (k & 7);
+}
+
+// SwiGLU packing interleaves gate and up in groups of 16 features: packed
+// feature j of a shard is gate column 16 * (j / 32) + j % 16 when j % 32 < 16,
+// and the up column of the same index otherwise. A 16-feature MFMA block is
+// thus all-gate or all-up, and blocks 2q and 2q + 1 pair up element by element.
+
+// Wavefront-uniform workgroup id remapped so that consecutive logical ids run
+// on the same XCD: the dispatcher hands workgroup i to XCD i % 8, and tiles
+// that share operands should share an L2.
+__device__ inline int xcd_remap(int bid, int nwg) {
+    const int q = nwg >> 3, r = nwg & 7;
+    const int xcd = bid & 7, local = bid >> 3;
+    return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
+}
+
+__device__ inline float silu_f(float g) {
+    // g / (1 + e^-g); e^-g overflows to +inf for very negative g, giving -0.
+    return g / (1.0f + __expf(-g));
+}
+
+__device__ inline float gelu_tanh_f(float u) {
+    // 0.5 u (1 + tanh(z)) == u / (1 + e^{-2z}), z = sqrt(2/pi) (u + 0.044715 u^3)
+    const float z2 = 1.5957691216057308f * (u + 0.044715f * u * u * u);
+    return u / (1.0f + __expf(-z2));
+}
+
+__device__ inline uint16_t bf16_bits(float x) {
+    __bf16 b = static_cast<__bf16>(x);    // round to nearest even
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ inline uint2 pack4_bf16(float a, float b, float c, float d) {
+    uint2 r;
+    r.x = (uint32_t)bf16_bits(a) | ((uint32_t)bf16_bits(b) << 16);
+    r.y = (uint32_t)bf16_bits(c) | ((uint32_t)bf16_bits(d) << 16);
+    return r;
+}
+
+}  // namespace tsp

@@ -1,0 +1,61 @@
+// Internal launchers (C++ linkage, not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace tsp {
+
+// Per-forward description shared by the bf16 kernels.
+struct Bf16Args {
+    const uint16_t* packed;   // packed weights (all shard records)
+    const uint16_t* x;        // T x d tokens
+    uint16_t* h;              // T x f hidden activations (workspace)
+    float* y;                 // T x d output
+    const int32_t* order;     // device copy of the ring order (P entries)
+    int64_t shard_elems;      // elements per shard record
+    int64_t down_off;         // offset of the down part inside a record
+    int T, d, f, F, P;
+    int swiglu;
+};
+
+struct F32Args {
+    const float* packed;
+    const float* x;
+    float* h;
+    float* y;
+    const int32_t* order;
+    int64_t shard_elems;
+    int T, d, f, F, P;
+    int swiglu;
+};
+
+hipError_t launch_pack_bf16(const void* wg, const void* wu, const void* wd, void* dst,
+                            int64_t shard_elems, int64_t down_off, int d, int f, int F, int P,
+                            int swiglu, hipStream_t st);
+hipError_t launch_pack_f32(const void* wg, const void* wu, const void* wd, void* dst,
+                           int64_t shard_elems, int d, int f, int F, int P, int swiglu,
+                           hipStream_t st);
+
+// Tiled MFMA path. Each returns the launch status; `cfg` picks a tile shape.
+hipError_t launch_gateup_tiled(const Bf16Args& a, int cfg, hipStream_t st);
+hipError_t launch_down_tiled(const Bf16Args& a, int cfg, hipStream_t st);
+// Tile-shape choice for a shape (host logic; -1 = none fits).
+int choose_gateup_cfg(int T, int d, int F, int P, int swiglu);
+int choose_down_cfg(int T, int d, int F);
+const char* tiled_cfg_name(int cfg);
+bool gateup_cfg_fits(int cfg, int d, int F, int swiglu);
+bool down_cfg_fits(int cfg, int d, int F);
+
+// Skinny (T <= 16) weight-streaming path.
+hipError_t launch_gateup_skinny(const Bf16Args& a, hipStream_t st);
+hipError_t launch_down_skinny(const Bf16Args& a, hipStream_t st);
+bool skinny_supported(int d, int F, int P);
+
+// fp32 path.
+hipError_t launch_gateup_f32(const F32Args& a, hipStream_t st);
+hipError_t launch_down_f32(const F32Args& a, hipStream_t st);
+
+}  // namespace tsp

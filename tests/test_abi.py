@@ -1,0 +1,100 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute call).
+
+* the library loads and exports every function include/tsp_mlp.h declares;
+* argument validation returns the documented status before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sharded_transformer_mlp_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "tsp_mlp.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tsp_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("tsp_mlp_create", "tsp_mlp_forward", "tsp_mlp_destroy", "tsp_mlp_validate"):
+        assert n in names
+    assert set(names) == set(B.SIGNATURES), "binding and header disagree"
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    lib = B.lib()
+    assert lib.tsp_status_string(0) == b"ok"
+    assert lib.tsp_status_string(2) == b"unsupported shape"
+    assert lib.tsp_status_string(99) == b"unknown status"
+
+
+OK, INV, UNS = B.TSP_OK, B.TSP_ERR_INVALID_ARG, B.TSP_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(T_max=4096, d=4096, f=14336, P=8), OK),
+    (dict(T_max=16, d=8192, f=28672, P=8, order=[3, 4, 5, 6, 7, 0, 1, 2]), OK),
+    (dict(T_max=2048, d=4096, f=16384, P=2, act="gelu_tanh"), OK),
+    (dict(T_max=3, d=5, f=12, P=4, dtype="f32"), OK),            # fp32 takes any shape
+    (dict(T_max=0, d=64, f=128, P=2), INV),
+    (dict(T_max=1, d=0, f=128, P=2), INV),
+    (dict(T_max=1, d=64, f=0, P=2), INV),
+    (dict(T_max=1, d=64, f=128, P=0), INV),
+    (dict(T_max=1, d=64, f=192, P=5), INV),                        # P does not divide f
+    (dict(T_max=1, d=64, f=128, P=2, act=7), INV),
+    (dict(T_max=1, d=64, f=128, P=2, dtype=9), INV),
+    (dict(T_max=1, d=64, f=256, P=4, order=[0, 1, 1, 3]), INV),    # not a permutation
+    (dict(T_max=1, d=64, f=256, P=4, order=[0, 1, 2, 4]), INV),
+    (dict(T_max=1, d=64, f=256, P=4, order=[0, 1, 2, -1]), INV),
+    (dict(T_max=1, d=64, f=128, P=2, has_gate=False), INV),        # SwiGLU without gate
+    (dict(T_max=1, d=64, f=128, P=2, act="gelu_tanh", has_gate=True), INV),
+    (dict(T_max=1, d=96, f=128, P=2), UNS),                        # bf16 needs d % 64
+    (dict(T_max=1, d=64, f=192, P=2), UNS),                        # bf16 needs F % 64
+    (dict(T_max=1 << 31, d=64, f=128, P=2), INV),
+])
+def test_validate(kw, want):
+    assert B.validate(**kw) == want
+
+
+def test_create_rejects_before_touching_the_device():
+    lib = B.lib()
+    h = ctypes.c_void_p(1234)
+    fake = ctypes.c_void_p(0x1000)
+    # bad order: rejected by validation, *out cleared
+    order = (ctypes.c_int32 * 2)(0, 0)
+    st = lib.tsp_mlp_create(ctypes.byref(h), 16, 64, 128, 2, 0, 1,
+                            ctypes.cast(order, ctypes.POINTER(ctypes.c_int32)), fake, fake, fake, None)
+    assert st == INV and h.value is None
+    assert b"permutation" in lib.tsp_last_error()
+    # null weights
+    st = lib.tsp_mlp_create(ctypes.byref(h), 16, 64, 128, 2, 0, 1, None, fake, None, fake, None)
+    assert st == INV
+    # misaligned weights
+    odd = ctypes.c_void_p(0x1002)
+    st = lib.tsp_mlp_create(ctypes.byref(h), 16, 64, 128, 2, 0, 1, None, fake, odd, fake, None)
+    assert st == INV and b"aligned" in lib.tsp_last_error()
+    # null out pointer
+    assert lib.tsp_mlp_create(None, 16, 64, 128, 2, 0, 1, None, fake, fake, fake, None) == INV
+
+
+def test_null_handle_calls():
+    lib = B.lib()
+    assert lib.tsp_mlp_destroy(None) == OK
+    assert lib.tsp_mlp_forward(None, 1, None, None, None) == INV
+    assert lib.tsp_mlp_set_path(None, 0) == INV
+    assert lib.tsp_mlp_set_timing(None, 1) == INV
+    n = ctypes.c_int32()
+    assert lib.tsp_mlp_read_timing(None, 0, None, None, None, ctypes.byref(n)) == INV

@@ -1,0 +1,273 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Every case runs the library on seeded inputs from the shared generator and
+compares with ``oracle.mlp_forward`` on the same (bf16-rounded) values:
+
+* fp32 storage: max|dY| / max|Y*| <= 1e-4;
+* bf16 storage (fp32 accumulate): ||dY||_2 / ||Y*||_2 <= 3e-3 and
+  max|dY| <= 2e-2 * max|Y*|.
+
+Small cases are compared in full (several tiles and a ragged token tail);
+the full-size workloads run in the launch configuration the bench times and
+are compared on sampled token rows, which the oracle computes independently
+(rows of the block do not interact).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sharded_transformer_mlp_amd.inputs import WORKLOADS, Workload, make_inputs, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+FP32_EMAX = 1e-4
+BF16_EL2 = 3e-3
+BF16_EMAX = 2e-2
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sharded_transformer_mlp_amd import binding
+    binding.lib()       # loud failure if the library is missing
+
+
+def _np(t):
+    return None if t is None else t.float().numpy()
+
+
+def run_gpu(w: Workload, inp, path="auto", tiles=None, T=None, order=None, reuse=None):
+    from sharded_transformer_mlp_amd.binding import TspMLP
+    x = inp.x if T is None else inp.x[:T]
+    dev = torch.device("cuda:0")
+    mlp = reuse
+    if mlp is None:
+        mlp = TspMLP(None if inp.w_gate is None else inp.w_gate.to(dev), inp.w_up.to(dev),
+                     inp.w_down.to(dev), w.P, order=w.order() if order is None else order,
+                     act=w.act, T_max=max(1, x.shape[0]))
+        mlp.set_path(path)
+        if tiles is not None:
+            mlp.set_tiles(*tiles)
+    y = mlp.forward(x.to(dev).contiguous())
+    torch.cuda.synchronize()
+    return y.cpu().double().numpy(), mlp
+
+
+def ref(w: Workload, inp, rows=None, T=None, order=None):
+    x = _np(inp.x if T is None else inp.x[:T])
+    return oracle.mlp_forward(x, _np(inp.w_gate), _np(inp.w_up), _np(inp.w_down), w.P,
+                              w.order() if order is None else order, w.act, rows=rows)
+
+
+def check(w: Workload, y, yref, tag=""):
+    dy = y - yref
+    scale = np.max(np.abs(yref))
+    emax = float(np.max(np.abs(dy)) / scale)
+    if w.dtype == "f32":
+        assert emax <= FP32_EMAX, f"{tag} fp32 e_max={emax:.3e}"
+        return emax, None
+    el2 = float(np.linalg.norm(dy) / np.linalg.norm(yref))
+    assert el2 <= BF16_EL2, f"{tag} bf16 e_L2={el2:.3e}"
+    assert emax <= BF16_EMAX, f"{tag} bf16 e_max={emax:.3e}"
+    return emax, el2
+
+
+SMALL = {
+    # several tiles in every direction plus a ragged token tail
+    "bf16-swiglu-T300-d512-f2048-P4-r1": Workload("s", T=300, d=512, f=2048, P=4, act="swiglu",
+                                                 dtype="bf16", seed=11, r0=1),
+    "bf16-gelu-T200-d256-f1024-P2": Workload("g", T=200, d=256, f=1024, P=2, act="gelu_tanh",
+                                             dtype="bf16", seed=12),
+    "bf16-swiglu-T37-d192-f384-P3": Workload("o", T=37, d=192, f=384, P=3, act="swiglu",
+                                             dtype="bf16", seed=13, r0=2),
+    "f32-swiglu-T70-d96-f200-P4": Workload("f", T=70, d=96, f=200, P=4, act="swiglu",
+                                           dtype="f32", seed=14, r0=3),
+    "f32-gelu-T33-d40-f60-P5": Workload("h", T=33, d=40, f=60, P=5, act="gelu_tanh",
+                                        dtype="f32", seed=15),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_full_parity(name):
+    w = SMALL[name]
+    say(f"[gpu] small parity {name}")
+    inp = make_inputs(w)
+    y, _ = run_gpu(w, inp)
+    check(w, y, ref(w, inp), name)
+
+
+@pytest.mark.parametrize("gcfg,dcfg", [(0, 0), (1, 1), (2, 2), (3, 3), (0, 3), (3, 0)])
+def test_every_tile_shape(gcfg, dcfg):
+    w = Workload("t", T=290, d=512, f=2048, P=2, act="swiglu", dtype="bf16", seed=21, r0=1)
+    say(f"[gpu] tile shapes gateup={gcfg} down={dcfg}")
+    inp = make_inputs(w)
+    y, _ = run_gpu(w, inp, path="tiled", tiles=(gcfg, dcfg))
+    check(w, y, ref(w, inp), f"tiles {gcfg}/{dcfg}")
+
+
+@pytest.mark.parametrize("gcfg", [0, 1, 2])
+def test_every_tile_shape_gelu(gcfg):
+    w = Workload("t", T=130, d=256, f=1024, P=2, act="gelu_tanh", dtype="bf16", seed=22)
+    say(f"[gpu] gelu tile shape {gcfg}")
+    inp = make_inputs(w)
+    y, _ = run_gpu(w, inp, path="tiled", tiles=(gcfg, gcfg))
+    check(w, y, ref(w, inp), f"gelu tiles {gcfg}")
+
+
+@pytest.mark.parametrize("T", [1, 5, 16])
+@pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
+def test_skinny_parity(T, act):
+    w = Workload("k", T=T, d=1024, f=2048, P=4, act=act, dtype="bf16", seed=31, r0=2)
+    say(f"[gpu] skinny T={T} {act}")
+    inp = make_inputs(w)
+    y, _ = run_gpu(w, inp, path="skinny")
+    check(w, y, ref(w, inp), f"skinny T={T}")
+    y2, _ = run_gpu(w, inp, path="tiled")          # the tiled path at the same small T
+    check(w, y2, ref(w, inp), f"tiled T={T}")
+
+
+def test_ring_orders():
+    """Every rotation and the reversed ring give the oracle's result."""
+    w = Workload("r", T=100, d=256, f=1024, P=4, act="swiglu", dtype="bf16", seed=41)
+    inp = make_inputs(w)
+    yref = ref(w, inp)
+    orders = [[(r + k) % 4 for k in range(4)] for r in range(4)] + [[3, 2, 1, 0], [2, 0, 3, 1]]
+    for order in orders:
+        say(f"[gpu] ring order {order}")
+        y, _ = run_gpu(w, inp, order=order)
+        check(w, y, yref, f"order {order}")
+
+
+def test_p_independence():
+    """The same weights cut into P = 1, 2, 4, 8 shards give the same block."""
+    base = Workload("p", T=64, d=256, f=2048, P=1, act="swiglu", dtype="bf16", seed=42)
+    inp = make_inputs(base)
+    yref = ref(base, inp)
+    for P in (1, 2, 4, 8):
+        w = base.with_(P=P)
+        say(f"[gpu] P={P}")
+        y, _ = run_gpu(w, inp)
+        check(w, y, yref, f"P={P}")
+
+
+def test_empty_and_ragged_T():
+    w = Workload("e", T=257, d=256, f=512, P=2, act="swiglu", dtype="bf16", seed=43)
+    inp = make_inputs(w)
+    from sharded_transformer_mlp_amd.binding import TspMLP
+    dev = torch.device("cuda:0")
+    mlp = TspMLP(inp.w_gate.to(dev), inp.w_up.to(dev), inp.w_down.to(dev), w.P, act=w.act, T_max=w.T)
+    say("[gpu] T = 0 leaves Y untouched")
+    y = torch.full((0, w.d), 7.0, device=dev)
+    mlp.forward(inp.x[:0].to(dev), y)
+    for T in (1, 2, 17, 100, 255, 256, 257):
+        say(f"[gpu] ragged T={T}")
+        y, _ = run_gpu(w, inp, T=T, reuse=mlp)
+        check(w, y, ref(w, inp, T=T), f"T={T}")
+    with pytest.raises(Exception):
+        mlp.forward(torch.zeros(w.T + 1, w.d, dtype=torch.bfloat16, device=dev))   # T > T_max
+
+
+def test_identity_weights_fp32_pins_the_activations():
+    """d = f, all weights I: Y = SiLU(X) * X, or Y = GeLU_tanh(X), elementwise.
+    At 1e-6 this separates the tanh form of GeLU from the erf form (they
+    differ by up to 4.7e-4 on [-6, 6])."""
+    d = 64
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(48, d, generator=g) * 3
+    eye = torch.eye(d)
+    for act in ("swiglu", "gelu_tanh"):
+        for P in (1, 4):
+            w = Workload("i", T=48, d=d, f=d, P=P, act=act, dtype="f32", seed=0)
+            from sharded_transformer_mlp_amd.inputs import MLPInputs
+            inp = MLPInputs(x, eye if act == "swiglu" else None, eye, eye)
+            say(f"[gpu] identity weights {act} P={P}")
+            y, _ = run_gpu(w, inp)
+            xd = x.double().numpy()
+            want = oracle.silu(xd) * xd if act == "swiglu" else oracle.gelu_tanh(xd)
+            assert np.max(np.abs(y - want)) <= 1e-6 * max(1.0, np.max(np.abs(want)))
+
+
+def test_identity_weights_bf16_layout():
+    """bf16 identity weights: each output equals bf16(act(x)) of its own
+    token and feature, which fails loudly on any lane / fragment mix-up."""
+    d = 256
+    g = torch.Generator().manual_seed(6)
+    x = (torch.randn(40, d, generator=g) * 2).to(torch.bfloat16)
+    eye = torch.eye(d).to(torch.bfloat16)
+    from sharded_transformer_mlp_amd.inputs import MLPInputs
+    for path in ("tiled", "skinny"):
+        T = 40 if path == "tiled" else 16
+        w = Workload("i", T=T, d=d, f=d, P=4, act="swiglu", dtype="bf16", seed=0, r0=1)
+        if path == "skinny":
+            w = w.with_(d=1024, f=1024)
+            x = (torch.randn(16, 1024, generator=g) * 2).to(torch.bfloat16)
+            eye = torch.eye(1024).to(torch.bfloat16)
+        inp = MLPInputs(x[:T], eye, eye, eye)
+        say(f"[gpu] bf16 identity layout {path}")
+        y, _ = run_gpu(w, inp, path=path)
+        xd = x[:T].double().numpy()
+        want = torch.from_numpy(oracle.silu(xd) * xd).to(torch.bfloat16).double().numpy()
+        assert np.max(np.abs(y - want)) <= 1e-2 * np.max(np.abs(want)) + 1e-6
+        assert np.max(np.abs(y - want) / (np.abs(want) + 1e-3)) <= 1e-2
+
+
+def test_scaling_by_two_is_bitwise_and_deterministic():
+    w = Workload("d", T=96, d=256, f=1024, P=4, act="swiglu", dtype="bf16", seed=44, r0=1)
+    inp = make_inputs(w)
+    say("[gpu] determinism")
+    y1, mlp = run_gpu(w, inp)
+    for _ in range(3):
+        y2, _ = run_gpu(w, inp, reuse=mlp)
+        assert np.array_equal(y1, y2)
+    say("[gpu] 2 * Wd gives 2 * Y exactly")
+    inp2 = make_inputs(w)
+    inp2.w_down = (inp.w_down.float() * 2).to(torch.bfloat16)
+    y3, _ = run_gpu(w, inp2)
+    assert np.array_equal(y3, 2 * y1)
+
+
+# --------------------------------------------------------------- full sizes
+
+def _full(name, n_rows):
+    w = WORKLOADS[name]
+    say(f"[gpu] full-size {name}: generating inputs")
+    inp = make_inputs(w)
+    say(f"[gpu] full-size {name}: forward on the GPU")
+    y, mlp = run_gpu(w, inp)
+    must = inp.outlier_rows if len(inp.outlier_rows) else None
+    rows = sample_rows(w.T, n_rows, seed=w.seed + 1000, must_include=must)
+    say(f"[gpu] full-size {name}: oracle on {len(rows)} rows")
+    yref = ref(w, inp, rows=rows.numpy())
+    emax, el2 = check(w, y[rows.numpy()], yref, name)
+    say(f"[gpu] full-size {name}: e_max={emax:.3e} e_L2={el2}")
+    assert np.all(np.isfinite(y))
+    mlp.close()
+
+
+def test_full_tiny_fp32():
+    _full("tiny-f32-swiglu-T64-d256-f1024-P2", 64)
+
+
+def test_full_megatron_gelu():
+    _full("megatron-gelu-bf16-T2048-d4096-f16384-P2", 256)
+
+
+def test_full_llama8b():
+    _full("llama3-8b-swiglu-bf16-T4096-d4096-f14336-P8", 256)
+
+
+def test_full_decode70b():
+    _full("70b-decode-swiglu-bf16-T16-d8192-f28672-P8", 16)
+
+
+def test_full_long70b():
+    _full("70b-long-swiglu-bf16-T16384-d8192-f28672-P8", 200)   # includes all 164 outlier rows
