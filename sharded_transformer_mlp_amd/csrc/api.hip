@@ -241,11 +241,11 @@ tsp_status_t tsp_mlp_create(tsp_mlp_t* out, int64_t T_max, int64_t d, int64_t f,
     e = hipMemcpyAsync(h->order_dev, h->order.data(), sizeof(int32_t) * (size_t)P, hipMemcpyHostToDevice, stream);
     if (e != hipSuccess) { release(h); return hip_fail(e, "hipMemcpyAsync(order)"); }
     if (dtype == TSP_DTYPE_BF16)
-        e = tsp::launch_pack_bf16(w_gate, w_up, w_down, h->packed, h->shard_elems, h->down_off, (int)d,
-                                  (int)f, (int)F, P, swiglu ? 1 : 0, stream);
+        e = tsp::launch_pack_bf16(w_gate, w_up, w_down, h->packed, h->order_dev, h->shard_elems,
+                                  h->down_off, (int)d, (int)f, (int)F, P, swiglu ? 1 : 0, stream);
     else
-        e = tsp::launch_pack_f32(w_gate, w_up, w_down, h->packed, h->shard_elems, (int)d, (int)f,
-                                 (int)F, P, swiglu ? 1 : 0, stream);
+        e = tsp::launch_pack_f32(w_gate, w_up, w_down, h->packed, h->order_dev, h->shard_elems,
+                                 (int)d, (int)f, (int)F, P, swiglu ? 1 : 0, stream);
     if (e != hipSuccess) { release(h); return hip_fail(e, "pack launch"); }
     e = hipStreamSynchronize(stream);
     if (e != hipSuccess) { release(h); return hip_fail(e, "hipStreamSynchronize after packing"); }
@@ -276,7 +276,6 @@ tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y, hi
         a.x = static_cast<const uint16_t*>(X);
         a.h = static_cast<uint16_t*>(h->work);
         a.y = Y;
-        a.order = h->order_dev;
         a.shard_elems = h->shard_elems;
         a.down_off = h->down_off;
         a.T = (int)T; a.d = (int)h->d; a.f = (int)h->f; a.F = (int)h->F; a.P = h->P;
@@ -310,7 +309,6 @@ tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y, hi
     a.x = static_cast<const float*>(X);
     a.h = static_cast<float*>(h->work);
     a.y = Y;
-    a.order = h->order_dev;
     a.shard_elems = h->shard_elems;
     a.T = (int)T; a.d = (int)h->d; a.f = (int)h->f; a.F = (int)h->F; a.P = h->P;
     a.swiglu = swiglu ? 1 : 0;

@@ -5,7 +5,8 @@
 // applied on the shard's own columns, then the down products accumulated
 // over the shards in ring order into an fp32 Y.
 // Per-shard fp32 record: [gate d x F][up d x F][down F x d], row-major
-// (GeLU: [A d x F][B F x d]).
+// (GeLU: [A d x F][B F x d]); records and the hidden columns of the
+// workspace are stored in ring order, record k holding shard order[k].
 #include "common.h"
 #include "launch.h"
 
@@ -18,7 +19,7 @@ __global__ __launch_bounds__(256) void gateup_f32(F32Args a) {
     __shared__ float xs[FT][FT + 1];
     __shared__ float gs[FT][FT + 1];
     __shared__ float us[FT][FT + 1];
-    const int s = a.order[blockIdx.z];
+    const int s = blockIdx.z;                            // ring step = packed record
     const int c0 = blockIdx.x * FT;                      // local hidden column
     const int t0 = blockIdx.y * FT;
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256) void down_f32(F32Args a) {
     const int64_t down_off = (a.swiglu ? 2 : 1) * dF;
     float y[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
     for (int step = 0; step < a.P; ++step) {
-        const int s = a.order[step];
+        const int s = step;                              // records in ring order
         const float* wd = a.packed + (int64_t)s * a.shard_elems + down_off;   // F x d
         for (int k0 = 0; k0 < a.F; k0 += FT) {
             for (int i = threadIdx.x; i < FT * FT; i += 256) {

@@ -6,9 +6,10 @@
 // fully coalesced 16 bytes per lane, and the tokens (one 16-column MFMA block,
 // zero-padded past T) come from L2.
 //
-// skinny_gateup: one workgroup per 16 hidden columns of one shard (shards
-//   taken in ring order). Its NW waves split the model dimension, each keeps
-//   fp32 gate and up accumulators, the partial sums are added in LDS in wave
+// skinny_gateup: one workgroup per 16 hidden columns of one shard (records
+//   and the hidden columns they produce are both stored in ring order). Its
+//   NW waves split the model dimension, each keeps fp32 gate and up
+//   accumulators, the partial sums are added in LDS in wave
 //   order, and wave 0 applies the activation and writes 16 tokens x 16
 //   hidden bf16 values.
 // skinny_down: one workgroup per 16 output features. The reduction runs over
@@ -38,9 +39,8 @@ template <int ACT>
 __global__ __launch_bounds__(SK_NW * 64) void skinny_gateup(Bf16Args a) {
     __shared__ f32x4 red[SK_NW][2][64];
     const int groups = a.F >> 4;                       // 16-column hidden groups per shard
-    const int step = blockIdx.x / groups;
-    const int grp = blockIdx.x - step * groups;
-    const int s = a.order[step];
+    const int s = blockIdx.x / groups;                  // ring step = packed record
+    const int grp = blockIdx.x - s * groups;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int kb_total = a.d >> 5;
     const int kb_per = kb_total / SK_NW;
@@ -107,11 +107,10 @@ __global__ __launch_bounds__(SK_NW * 64) void skinny_down(Bf16Args a) {
         bf16x8 wv[SK_U], hv[SK_U];
 #pragma unroll
         for (int u = 0; u < SK_U; ++u) {
-            const int q = kb + u;
+            const int q = kb + u;                       // records and H are in ring order
             const int k = q / kbF, lk = q - k * kbF;
-            const int s = a.order[k];
-            wv[u] = load_frag(base + (int64_t)s * a.shard_elems + (int64_t)lk * 512);
-            hv[u] = token_frag(a.h, a.f, (int64_t)s * a.F + lk * 32, lane, a.T);
+            wv[u] = load_frag(base + (int64_t)k * a.shard_elems + (int64_t)lk * 512);
+            hv[u] = token_frag(a.h, a.f, (int64_t)q * 32, lane, a.T);
         }
 #pragma unroll
         for (int u = 0; u < SK_U; ++u)

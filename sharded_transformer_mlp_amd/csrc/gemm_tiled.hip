@@ -6,39 +6,47 @@
 // features of one token, so the epilogue writes H (bf16) and Y (fp32) rows
 // straight from registers.
 //
-// gateup_tiled: H[:, cols of shard s] = act(X . W_s) for every shard, the
+// gateup_tiled: H_k = act(X . W_{order[k]}) for every ring step k, the
 //   SwiGLU or GeLU epilogue applied in registers ("Tensor Parallelism:
 //   Splitting the Math", section "Why the column-then-row split": the
-//   nonlinearity is exact on a shard's own columns). Tiles of the shard
-//   visited at ring step k are dispatched before those of step k + 1.
-// down_tiled:   Y = sum_k H_{order[k]} . Wd_{order[k]}; the reduction loop
-//   walks the shards in ring order and keeps the fp32 Y tile in registers
-//   for the whole walk, so Y is written once ("Folding Tensor and Sequence
+//   nonlinearity is exact on a shard's own columns). Packed records and the
+//   hidden columns of the workspace are both in ring order, so H_k occupies
+//   columns [k*F, (k+1)*F). Tiles of ring step k are dispatched before those
+//   of step k + 1.
+// down_tiled:   Y = sum_k H_k . Wd_{order[k]}; the reduction loop walks the
+//   records in ring order and keeps the fp32 Y tile in registers for the
+//   whole walk, so Y is written once ("Folding Tensor and Sequence
 //   Parallelism ...", Abstract: partial outputs accumulate locally).
 //
-// Main loop: a BM x 64 slab of packed weights and a BN x 64 slab of tokens
-// per step, staged through registers into double-buffered LDS laid out in
-// fragment blocks (1 KiB per 16 rows x 32 reduction indices, lane-ordered),
-// so every LDS read of an operand fragment is one contiguous 16-byte-per-lane
-// access. One barrier per step.
+// Main loop: 32 reduction indices per stage, a 4-deep LDS ring filled by
+// global_load_lds_dwordx4 (global memory straight into LDS, no register
+// staging). Loads for stage t + 3 are issued right after the barrier of
+// stage t, so each stage's loads have three stages of MFMA work to land. LDS
+// is laid out in fragment blocks (1 KiB per 16 rows x 32 reduction indices,
+// lane-ordered), so every operand fragment read is one contiguous
+// 16-byte-per-lane access.
 #include "common.h"
 #include "launch.h"
 
 namespace tsp {
 
+#define TSP_LDS __attribute__((address_space(3)))
+
 template <int BM_, int BN_, int WM_, int WN_>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-    static constexpr int NT = WM * WN * 64;            // threads
-    static constexpr int TM = BM / WM / 16;             // MFMA blocks per wave along features
-    static constexpr int TN = BN / WN / 16;             // MFMA blocks per wave along tokens
-    static constexpr int CA = BM * 8 / NT;              // 16-byte chunks per thread per step (A)
-    static constexpr int CB = BN * 8 / NT;              // (B)
-    static constexpr int A_ELEMS = BM * 64;             // bf16 elements per stage
-    static constexpr int B_ELEMS = BN * 64;
-    static constexpr int STAGE = A_ELEMS + B_ELEMS;
+    static constexpr int NW = WM * WN;                   // waves
+    static constexpr int NT = NW * 64;                   // threads
+    static constexpr int TM = BM / WM / 16;              // MFMA blocks per wave along features
+    static constexpr int TN = BN / WN / 16;              // MFMA blocks per wave along tokens
+    static constexpr int A_BLK = BM / 16;                // 1 KiB fragment blocks per stage (A)
+    static constexpr int B_BLK = BN / 16;                // (B)
+    static constexpr int LOADS = (A_BLK + B_BLK) / NW;   // DMA loads per wave per stage
+    static constexpr int STAGE = (A_BLK + B_BLK) * 512;  // bf16 elements per stage (32-deep)
+    static constexpr int NS = 4;                         // stages in the LDS ring
     static_assert(TM >= 1 && TN >= 1, "wave tile");
-    static_assert(CA * NT == BM * 8 && CB * NT == BN * 8, "loader split");
+    static_assert(LOADS * NW == A_BLK + B_BLK, "loader split");
+    static_assert(NS * STAGE * 2 <= 160 * 1024, "LDS");
 };
 
 // Token-tile-grouped raster over a (tokens x features) tile grid: GT token
@@ -53,110 +61,153 @@ __device__ inline void raster(int L, int n_f, int n_t, int& ttile, int& flin) {
     flin = rem / gt;
 }
 
+// One pipeline stage = 32 reduction indices of the A slab (BM packed weight
+// rows, 16-row fragment blocks) and the B slab (BN tokens). Each wave moves
+// LOADS whole 1 KiB blocks with global_load_lds_dwordx4: the 64 lanes' 16-byte
+// pieces land contiguously in LDS, already in fragment order. Token rows past
+// T are clamped to row T - 1 (their outputs are never stored).
 template <class C>
-__device__ __forceinline__ void load_a(const uint16_t* __restrict__ a_base, int64_t a_rs,
-                                       uint4 (&ra)[C::CA]) {
-    const int tid = threadIdx.x;
+__device__ __forceinline__ void issue_stage(uint16_t* lds_stage, const uint16_t* __restrict__ a_base,
+                                            int64_t a_rs, const uint16_t* __restrict__ b_src, int ldb,
+                                            int64_t b_koff, int t0, int T, int w, int lane) {
 #pragma unroll
-    for (int i = 0; i < C::CA; ++i) {
-        const int q = i * C::NT + tid;
-        const int blk = q >> 6, lane = q & 63;
-        ra[i] = *reinterpret_cast<const uint4*>(a_base + (blk >> 1) * a_rs + (blk & 1) * 512 + lane * 8);
-    }
-}
-
-template <class C>
-__device__ __forceinline__ void load_b(const uint16_t* __restrict__ b_src, int ldb, int64_t b_koff,
-                                       int t0, int T, uint4 (&rb)[C::CB]) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < C::CB; ++i) {
-        const int q = i * C::NT + tid;
-        const int blk = q >> 6, lane = q & 63;
-        const int tok = t0 + (blk >> 1) * 16 + (lane & 15);
-        if (tok < T) {
-            rb[i] = *reinterpret_cast<const uint4*>(b_src + (int64_t)tok * ldb + b_koff +
-                                                   (blk & 1) * 32 + (lane >> 4) * 8);
+    for (int r = 0; r < C::LOADS; ++r) {
+        const int b = r * C::NW + w;                     // wave-uniform block id
+        const uint16_t* g;
+        if (b < C::A_BLK) {
+            g = a_base + b * a_rs + lane * 8;
         } else {
-            rb[i] = make_uint4(0u, 0u, 0u, 0u);
+            const int tok = min(t0 + (b - C::A_BLK) * 16 + (lane & 15), T - 1);
+            g = b_src + (int64_t)tok * ldb + b_koff + (lane >> 4) * 8;
         }
+        __builtin_amdgcn_global_load_lds(g, (TSP_LDS void*)(lds_stage + b * 512), 16, 0, 0);
     }
 }
 
+// Wait until at most `newer` stages of this wave's DMA loads are outstanding.
 template <class C>
-__device__ __forceinline__ void store_stage(uint16_t* lds_stage, const uint4 (&ra)[C::CA],
-                                            const uint4 (&rb)[C::CB]) {
-    uint4* as = reinterpret_cast<uint4*>(lds_stage);
-    uint4* bs = reinterpret_cast<uint4*>(lds_stage + C::A_ELEMS);
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < C::CA; ++i) as[i * C::NT + tid] = ra[i];
-#pragma unroll
-    for (int i = 0; i < C::CB; ++i) bs[i * C::NT + tid] = rb[i];
+__device__ __forceinline__ void wait_stages(int newer) {
+    // s_waitcnt with vmcnt = newer * LOADS, expcnt / lgkmcnt left at their maximum
+#define TSP_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+    if (newer >= 3) TSP_VMCNT(3 * C::LOADS);
+    else if (newer == 2) TSP_VMCNT(2 * C::LOADS);
+    else if (newer == 1) TSP_VMCNT(C::LOADS);
+    else TSP_VMCNT(0);
+#undef TSP_VMCNT
+}
+
+// Workgroup barrier that orders LDS traffic without waiting for the DMA
+// loads still in flight for later stages (__syncthreads would drain them).
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 template <class C>
-__device__ __forceinline__ void compute_stage(const uint16_t* lds_stage, f32x4 (&acc)[C::TM][C::TN],
-                                              int wm, int wn, int lane) {
+__device__ __forceinline__ void read_frags(const uint16_t* lds_stage, bf16x8 (&af)[C::TM],
+                                           bf16x8 (&bv)[C::TN], int wm, int wn, int lane) {
     const bf16x8* as = reinterpret_cast<const bf16x8*>(lds_stage);
-    const bf16x8* bs = reinterpret_cast<const bf16x8*>(lds_stage + C::A_ELEMS);
+    const bf16x8* bs = reinterpret_cast<const bf16x8*>(lds_stage + C::A_BLK * 512);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 af[C::TM], bv[C::TN];
+    for (int i = 0; i < C::TM; ++i) af[i] = as[(wm * C::TM + i) * 64 + lane];
 #pragma unroll
-        for (int i = 0; i < C::TM; ++i) af[i] = as[((wm * C::TM + i) * 2 + kk) * 64 + lane];
+    for (int j = 0; j < C::TN; ++j) bv[j] = bs[(wn * C::TN + j) * 64 + lane];
+}
+
+template <class C>
+__device__ __forceinline__ void mfma_stage(f32x4 (&acc)[C::TM][C::TN], const bf16x8 (&af)[C::TM],
+                                           const bf16x8 (&bv)[C::TN]) {
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j) bv[j] = bs[((wn * C::TN + j) * 2 + kk) * 64 + lane];
+    for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-        for (int i = 0; i < C::TM; ++i)
+        for (int j = 0; j < C::TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bv[j], acc[i][j], 0, 0, 0);
+}
+
+// The reduction loop shared by both kernels. `src(t, a_base, b_koff)` gives
+// step t's A slab start and B reduction offset (32 indices per step).
+//
+// Ping-pong schedule: the waves form two groups (waves 0..NW/2-1 and the
+// rest), one wave of each group per SIMD. Each step t is a memory phase M(t)
+// (issue the DMA loads of stage t + 3, read stage t's fragments from LDS) and
+// a compute phase C(t) (the MFMAs). Group 1 runs one phase behind group 0,
+// and every phase boundary is a workgroup barrier, so on each SIMD one wave
+// computes while the other does its memory work.
+//
+// Barrier b_{2t} opens group 0's M(t) (group 1's C(t-1)); b_{2t+1} opens
+// group 0's C(t) (group 1's M(t)). Every wave makes its own stage-t loads
+// complete before b_{2t}, so stage t is visible to both groups' M(t). The
+// DMA of stage t + 3 goes into stage t - 1's buffer, whose last reader
+// (group 1's M(t-1), which drains its LDS reads before b_{2t}) is done.
+template <class C, class Src>
+__device__ __forceinline__ void mainloop(uint16_t* lds, f32x4 (&acc)[C::TM][C::TN], int ksteps,
+                                         int64_t a_rs, const uint16_t* b_src, int ldb, int t0, int T,
+                                         Src&& src) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w / C::WN, wn = w % C::WN;
+    const bool g1 = w >= C::NW / 2;
 #pragma unroll
-            for (int j = 0; j < C::TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bv[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto issue = [&](int t) {
+        const uint16_t* ab;
+        int64_t bk;
+        src(t, ab, bk);
+        issue_stage<C>(lds + (t % C::NS) * C::STAGE, ab, a_rs, b_src, ldb, bk, t0, T, w, lane);
+    };
+    constexpr int AHEAD = C::NS - 1;                    // stages in flight ahead of the reader
+    const int pro = min(AHEAD, ksteps);
+    for (int t = 0; t < pro; ++t) issue(t);
+    wait_stages<C>(pro - 1);                            // own stage-0 loads landed
+    if (g1) stage_barrier();                            // b_0: group 1 sits out phase 0
+    bf16x8 af[C::TM], bv[C::TN];
+    for (int t = 0; t < ksteps; ++t) {
+        stage_barrier();                                // g0: b_{2t}, g1: b_{2t+1}
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + AHEAD < ksteps) issue(t + AHEAD);
+        read_frags<C>(lds + (t % C::NS) * C::STAGE, af, bv, wm, wn, lane);
+        __builtin_amdgcn_s_waitcnt((15 & 15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+        // stage t + 1 must be complete before b_{2t+2}: group 1 reaches it
+        // at the end of this memory phase, group 0 after its compute phase
+        const int newer = min(t + AHEAD, ksteps - 1) - (t + 1);
+        if (g1) wait_stages<C>(newer);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_barrier();                                // g0: b_{2t+1}, g1: b_{2t+2}
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+        mfma_stage<C>(acc, af, bv);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!g1) wait_stages<C>(newer);
     }
+    if (!g1) stage_barrier();                           // b_{2K}: group 0 matches group 1's count
 }
 
 // act: 1 = SwiGLU (packed blocks alternate gate / up), 2 = GeLU (tanh form)
 template <int BM, int BN, int WM, int WN, int ACT>
 __global__ __launch_bounds__(WM * WN * 64) void gateup_tiled(Bf16Args a, int n_ft_shard, int n_tt) {
     using C = TileCfg<BM, BN, WM, WN>;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
 
     int ttile, flin;
     raster(xcd_remap(blockIdx.x, gridDim.x), a.P * n_ft_shard, n_tt, ttile, flin);
-    const int step = flin / n_ft_shard;                 // ring step
-    const int ftile = flin - step * n_ft_shard;
-    const int s = a.order[step];                        // shard held at that step
-    const int kblocks = a.d >> 5;
-    const int64_t a_rs = (int64_t)kblocks * 512;
+    const int s = flin / n_ft_shard;                    // ring step = packed record
+    const int ftile = flin - s * n_ft_shard;
+    const int64_t a_rs = (int64_t)(a.d >> 5) * 512;     // elements per 16-row block row
     const uint16_t* a_tile = a.packed + (int64_t)s * a.shard_elems + (int64_t)(ftile * (BM / 16)) * a_rs;
     const int t0 = ttile * BN;
-    const int ksteps = a.d >> 6;
-
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int wm = wid / WN, wn = wid % WN;
 
     f32x4 acc[C::TM][C::TN];
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mainloop<C>(lds, acc, a.d >> 5, a_rs, a.x, a.d, t0, a.T,
+                [&](int t, const uint16_t*& ab, int64_t& bk) {
+                    ab = a_tile + (int64_t)t * 512;
+                    bk = (int64_t)t * 32;
+                });
 
-    uint4 ra[C::CA], rb[C::CB];
-    load_a<C>(a_tile, a_rs, ra);
-    load_b<C>(a.x, a.d, 0, t0, a.T, rb);
-    store_stage<C>(lds, ra, rb);
-    __syncthreads();
-    for (int t = 0; t < ksteps; ++t) {
-        const int cur = t & 1;
-        if (t + 1 < ksteps) {
-            load_a<C>(a_tile + (int64_t)(t + 1) * 1024, a_rs, ra);
-            load_b<C>(a.x, a.d, (int64_t)(t + 1) * 64, t0, a.T, rb);
-        }
-        compute_stage<C>(lds + cur * C::STAGE, acc, wm, wn, lane);
-        if (t + 1 < ksteps) store_stage<C>(lds + (cur ^ 1) * C::STAGE, ra, rb);
-        __syncthreads();
-    }
-
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w / WN, wn = w % WN;
     if constexpr (ACT == 1) {
 #pragma unroll
         for (int p = 0; p < C::TM / 2; ++p) {
@@ -194,47 +245,27 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_tiled(Bf16Args a, int n_f
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) void down_tiled(Bf16Args a, int n_ft, int n_tt) {
     using C = TileCfg<BM, BN, WM, WN>;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
 
     int ttile, ftile;
     raster(xcd_remap(blockIdx.x, gridDim.x), n_ft, n_tt, ttile, ftile);
-    const int kbF = a.F >> 5;
-    const int spp = a.F >> 6;                           // steps per shard
-    const int ksteps = a.P * spp;
-    const int64_t a_rs = (int64_t)kbF * 512;
+    const int spp = a.F >> 5;                           // steps per shard
+    const int64_t a_rs = (int64_t)spp * 512;
     const uint16_t* a_ft = a.packed + a.down_off + (int64_t)(ftile * (BM / 16)) * a_rs;
     const int t0 = ttile * BN;
 
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int wm = wid / WN, wn = wid % WN;
-
     f32x4 acc[C::TM][C::TN];
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Reduction step t is local step t % spp of ring step t / spp; records
+    // and H columns are both stored in ring order, so this is a linear walk.
+    mainloop<C>(lds, acc, a.P * spp, a_rs, a.h, a.f, t0, a.T,
+                [&](int t, const uint16_t*& ab, int64_t& bk) {
+                    const int k = t / spp, ls = t - k * spp;
+                    ab = a_ft + (int64_t)k * a.shard_elems + (int64_t)ls * 512;
+                    bk = (int64_t)t * 32;
+                });
 
-    uint4 ra[C::CA], rb[C::CB];
-    {
-        const int s = a.order[0];
-        load_a<C>(a_ft + (int64_t)s * a.shard_elems, a_rs, ra);
-        load_b<C>(a.h, a.f, (int64_t)s * a.F, t0, a.T, rb);
-    }
-    store_stage<C>(lds, ra, rb);
-    __syncthreads();
-    for (int t = 0; t < ksteps; ++t) {
-        const int cur = t & 1;
-        if (t + 1 < ksteps) {
-            const int k = (t + 1) / spp, ls = (t + 1) - k * spp;
-            const int s = a.order[k];
-            load_a<C>(a_ft + (int64_t)s * a.shard_elems + (int64_t)ls * 1024, a_rs, ra);
-            load_b<C>(a.h, a.f, (int64_t)s * a.F + ls * 64, t0, a.T, rb);
-        }
-        compute_stage<C>(lds + cur * C::STAGE, acc, wm, wn, lane);
-        if (t + 1 < ksteps) store_stage<C>(lds + (cur ^ 1) * C::STAGE, ra, rb);
-        __syncthreads();
-    }
-
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w / WN, wn = w % WN;
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {
         const int n = ftile * BM + (wm * C::TM + i) * 16 + (lane >> 4) * 4;

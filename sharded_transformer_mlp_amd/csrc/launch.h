@@ -12,10 +12,9 @@ namespace tsp {
 struct Bf16Args {
     const uint16_t* packed;   // packed weights (all shard records)
     const uint16_t* x;        // T x d tokens
-    uint16_t* h;              // T x f hidden activations (workspace)
+    uint16_t* h;              // T x f hidden activations (workspace), columns in ring-step order
     float* y;                 // T x d output
-    const int32_t* order;     // device copy of the ring order (P entries)
-    int64_t shard_elems;      // elements per shard record
+    int64_t shard_elems;      // elements per shard record (records in ring order)
     int64_t down_off;         // offset of the down part inside a record
     int T, d, f, F, P;
     int swiglu;
@@ -26,18 +25,18 @@ struct F32Args {
     const float* x;
     float* h;
     float* y;
-    const int32_t* order;
     int64_t shard_elems;
     int T, d, f, F, P;
     int swiglu;
 };
 
+// Pack the weights into P records in ring order (record k = shard order[k]).
 hipError_t launch_pack_bf16(const void* wg, const void* wu, const void* wd, void* dst,
-                            int64_t shard_elems, int64_t down_off, int d, int f, int F, int P,
-                            int swiglu, hipStream_t st);
+                            const int32_t* order, int64_t shard_elems, int64_t down_off, int d,
+                            int f, int F, int P, int swiglu, hipStream_t st);
 hipError_t launch_pack_f32(const void* wg, const void* wu, const void* wd, void* dst,
-                           int64_t shard_elems, int d, int f, int F, int P, int swiglu,
-                           hipStream_t st);
+                           const int32_t* order, int64_t shard_elems, int d, int f, int F, int P,
+                           int swiglu, hipStream_t st);
 
 // Tiled MFMA path. Each returns the launch status; `cfg` picks a tile shape.
 hipError_t launch_gateup_tiled(const Bf16Args& a, int cfg, hipStream_t st);

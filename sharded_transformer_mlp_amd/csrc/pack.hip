@@ -6,6 +6,9 @@
 // ("Tensor Parallelism: Splitting the Math", Megatron walk-through steps 2-5:
 // column blocks of the first matrix, matching row blocks of the second).
 // Each shard is one contiguous record, so a ring step would move one record.
+// Records are stored in ring order: record k holds shard order[k], the shard
+// a rank holds at ring step k. The forward kernels then walk records 0..P-1
+// and never look the order up.
 //
 // bf16 record of shard s (all in 16 x 32 fragment blocks, see common.h):
 //   [gate/up part]  NGU x d, NGU = 2F (SwiGLU, gate and up interleaved in
@@ -20,10 +23,12 @@
 namespace tsp {
 
 __global__ void pack_gateup_bf16(const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
-                                 uint16_t* __restrict__ dst, int64_t shard_elems, int d, int f,
-                                 int F, int swiglu, int64_t chunks_per_shard) {
+                                 uint16_t* __restrict__ dst, const int32_t* __restrict__ order,
+                                 int64_t shard_elems, int d, int f, int F, int swiglu,
+                                 int64_t chunks_per_shard) {
     const int64_t total = chunks_per_shard;
-    const int s = blockIdx.y;
+    const int rec = blockIdx.y;
+    const int s = order[rec];
     const int kblocks = d >> 5;
     for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
          c += (int64_t)gridDim.x * blockDim.x) {
@@ -50,14 +55,15 @@ __global__ void pack_gateup_bf16(const uint16_t* __restrict__ wg, const uint16_t
         o.y = v[2] | ((uint32_t)v[3] << 16);
         o.z = v[4] | ((uint32_t)v[5] << 16);
         o.w = v[6] | ((uint32_t)v[7] << 16);
-        *reinterpret_cast<uint4*>(dst + (int64_t)s * shard_elems + c * 8) = o;
+        *reinterpret_cast<uint4*>(dst + (int64_t)rec * shard_elems + c * 8) = o;
     }
 }
 
 __global__ void pack_down_bf16(const uint16_t* __restrict__ wd, uint16_t* __restrict__ dst,
-                               int64_t shard_elems, int64_t down_off, int d, int F,
-                               int64_t chunks_per_shard) {
-    const int s = blockIdx.y;
+                               const int32_t* __restrict__ order, int64_t shard_elems,
+                               int64_t down_off, int d, int F, int64_t chunks_per_shard) {
+    const int rec = blockIdx.y;
+    const int s = order[rec];
     const int kblocks = F >> 5;
     for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks_per_shard;
          c += (int64_t)gridDim.x * blockDim.x) {
@@ -75,7 +81,7 @@ __global__ void pack_down_bf16(const uint16_t* __restrict__ wd, uint16_t* __rest
         o.y = v[2] | ((uint32_t)v[3] << 16);
         o.z = v[4] | ((uint32_t)v[5] << 16);
         o.w = v[6] | ((uint32_t)v[7] << 16);
-        *reinterpret_cast<uint4*>(dst + (int64_t)s * shard_elems + down_off + c * 8) = o;
+        *reinterpret_cast<uint4*>(dst + (int64_t)rec * shard_elems + down_off + c * 8) = o;
     }
 }
 
@@ -83,8 +89,10 @@ __global__ void pack_down_bf16(const uint16_t* __restrict__ wd, uint16_t* __rest
 //   [gate cols d x F][up cols d x F][down rows F x d]  (GeLU: no gate part).
 __global__ void pack_f32(const float* __restrict__ wg, const float* __restrict__ wu,
                          const float* __restrict__ wd, float* __restrict__ dst,
-                         int64_t shard_elems, int d, int f, int F, int swiglu) {
-    const int s = blockIdx.y;
+                         const int32_t* __restrict__ order, int64_t shard_elems, int d, int f,
+                         int F, int swiglu) {
+    const int rec = blockIdx.y;
+    const int s = order[rec];
     const int64_t dF = (int64_t)d * F;
     const int64_t parts = swiglu ? 3 : 2;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < parts * dF;
@@ -100,35 +108,35 @@ __global__ void pack_f32(const float* __restrict__ wg, const float* __restrict__
             const int64_t row = r / d, col = r - row * d;
             v = wd[((int64_t)s * F + row) * d + col];
         }
-        dst[(int64_t)s * shard_elems + i] = v;
+        dst[(int64_t)rec * shard_elems + i] = v;
     }
 }
 
 hipError_t launch_pack_bf16(const void* wg, const void* wu, const void* wd, void* dst,
-                            int64_t shard_elems, int64_t down_off, int d, int f, int F, int P,
-                            int swiglu, hipStream_t st) {
+                            const int32_t* order, int64_t shard_elems, int64_t down_off, int d,
+                            int f, int F, int P, int swiglu, hipStream_t st) {
     const int64_t ngu = swiglu ? 2LL * F : (int64_t)F;
     const int64_t gu_chunks = ngu * d / 8, dn_chunks = (int64_t)d * F / 8;
     dim3 blk(256);
     dim3 g1((unsigned)std::min<int64_t>((gu_chunks + 255) / 256, 4096), P);
     hipLaunchKernelGGL(pack_gateup_bf16, g1, blk, 0, st, (const uint16_t*)wg,
-                       (const uint16_t*)wu, (uint16_t*)dst, shard_elems, d, f, F, swiglu,
+                       (const uint16_t*)wu, (uint16_t*)dst, order, shard_elems, d, f, F, swiglu,
                        gu_chunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 g2((unsigned)std::min<int64_t>((dn_chunks + 255) / 256, 4096), P);
-    hipLaunchKernelGGL(pack_down_bf16, g2, blk, 0, st, (const uint16_t*)wd, (uint16_t*)dst,
+    hipLaunchKernelGGL(pack_down_bf16, g2, blk, 0, st, (const uint16_t*)wd, (uint16_t*)dst, order,
                        shard_elems, down_off, d, F, dn_chunks);
     return hipGetLastError();
 }
 
 hipError_t launch_pack_f32(const void* wg, const void* wu, const void* wd, void* dst,
-                           int64_t shard_elems, int d, int f, int F, int P, int swiglu,
-                           hipStream_t st) {
+                           const int32_t* order, int64_t shard_elems, int d, int f, int F, int P,
+                           int swiglu, hipStream_t st) {
     const int64_t n = (swiglu ? 3 : 2) * (int64_t)d * F;
     dim3 g((unsigned)std::min<int64_t>((n + 255) / 256, 4096), P);
     hipLaunchKernelGGL(pack_f32, g, dim3(256), 0, st, (const float*)wg, (const float*)wu,
-                       (const float*)wd, (float*)dst, shard_elems, d, f, F, swiglu);
+                       (const float*)wd, (float*)dst, order, shard_elems, d, f, F, swiglu);
     return hipGetLastError();
 }
 
