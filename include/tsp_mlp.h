@@ -123,14 +123,18 @@ tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y,
 /* Synchronise the handle's stream and free everything it owns. NULL is a no-op. */
 tsp_status_t tsp_mlp_destroy(tsp_mlp_t h);
 
-/* Choose the forward path: AUTO (skinny when T <= 16 in bf16), TILED or SKINNY.
- * SKINNY needs bf16 and T <= 16 at forward time (TSP_ERR_UNSUPPORTED otherwise). */
+/* Choose the forward path: AUTO (the weight-streaming skinny kernels when
+ * T <= 32 and the shape suits them, bf16 only), TILED or SKINNY. SKINNY needs
+ * bf16, T <= 32, d % 512 == 0 and P * F % 1024 == 0 at forward time
+ * (TSP_ERR_UNSUPPORTED otherwise). */
 tsp_status_t tsp_mlp_set_path(tsp_mlp_t h, int32_t path);
 
 /* Tuning and test hook for the bf16 tiled path: fix the tile shape of the
  * gate/up and down kernels (-1 = choose per forward from T and the shape).
- * Shapes: 0 = 256 features x 256 tokens, 1 = 256 x 128, 2 = 128 x 128,
- * 3 = 64 x 128. TSP_ERR_UNSUPPORTED if the shape does not divide the shard's
+ * Shapes (features x tokens): 0 = 256 x 256, 1 = 256 x 128, 2 = 128 x 128,
+ * 3 = 64 x 128, 4 = 256 x 256 with one wave per SIMD, 5 = 256 x 256 with
+ * 16x16x32 MFMAs over global-to-LDS loads (the automatic choice at large T).
+ * TSP_ERR_UNSUPPORTED if the shape does not divide the shard's
  * packed width (gate/up) or d (down), or for an fp32 handle. */
 tsp_status_t tsp_mlp_set_tiles(tsp_mlp_t h, int32_t gateup_tile, int32_t down_tile);
 

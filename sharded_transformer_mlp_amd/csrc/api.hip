@@ -280,10 +280,10 @@ tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y, hi
         a.down_off = h->down_off;
         a.T = (int)T; a.d = (int)h->d; a.f = (int)h->f; a.F = (int)h->F; a.P = h->P;
         a.swiglu = swiglu ? 1 : 0;
-        const bool sk_ok = T <= 16 && tsp::skinny_supported(a.d, a.F, a.P);
+        const bool sk_ok = T <= 32 && tsp::skinny_supported(a.d, a.F, a.P);
         bool skinny = false;
         if (h->path == TSP_PATH_SKINNY) {
-            if (!sk_ok) return fail(TSP_ERR_UNSUPPORTED, "skinny path needs T <= 16, d %% 1024 == 0 and P*F %% 1024 == 0");
+            if (!sk_ok) return fail(TSP_ERR_UNSUPPORTED, "skinny path needs T <= 32, d %% 512 == 0 and P*F %% 1024 == 0");
             skinny = true;
         } else if (h->path == TSP_PATH_AUTO) {
             skinny = sk_ok;

@@ -9,23 +9,31 @@ namespace tsp {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// The packed bf16 weight layout is built from 16 x 32 "fragment blocks":
-// 16 output features (MFMA rows) by 32 reduction indices. A block is 512
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+// Native 16-byte vector: copies are plain loads and stores (HIP's uint4 is a
+// struct whose copies can become memcpy and defeat register promotion).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// The packed bf16 weight layout is built from 32 x 16 "fragment blocks":
+// 32 output features (MFMA rows) by 16 reduction indices. A block is 512
 // elements (1 KiB) stored in the order the 64 lanes of a wavefront consume
-// them as the A operand of v_mfma_f32_16x16x32_bf16: lane l holds feature
-// l % 16 and the 8 consecutive reduction indices 8 * (l / 16) .. + 7, so a
-// wave reads one block with a single contiguous 16-byte-per-lane load.
+// them as the A operand of v_mfma_f32_32x32x16_bf16: lane l holds feature
+// l % 32 and the 8 consecutive reduction indices 8 * (l / 32) .. + 7, so a
+// wave reads one block with a single contiguous 16-byte-per-lane load. The
+// token operand uses the same lane map (lane l: token l % 32). The 32 x 32
+// fp32 result leaves lane l with token l % 32 and, in register 4 * q + r,
+// feature 8 * q + 4 * (l / 32) + r (q, r = 0..3).
 constexpr int FRAG_ELEMS = 512;
 
 __host__ __device__ inline int64_t frag_offset(int64_t n, int64_t k, int64_t kblocks) {
     // element (feature n, reduction index k) in a matrix whose blocks run
-    // k-fastest: block (n / 16, k / 32) is at ((n / 16) * kblocks + k / 32).
-    return ((n >> 4) * kblocks + (k >> 5)) * FRAG_ELEMS + (((k & 31) >> 3) * 16 + (n & 15)) * 8 + (k & 7);
+    // k-fastest: block (n / 32, k / 16) is at ((n / 32) * kblocks + k / 16).
+    return ((n >> 5) * kblocks + (k >> 4)) * FRAG_ELEMS + (((k & 15) >> 3) * 32 + (n & 31)) * 8 + (k & 7);
 }
 
-// SwiGLU packing interleaves gate and up in groups of 16 features: packed
-// feature j of a shard is gate column 16 * (j / 32) + j % 16 when j % 32 < 16,
-// and the up column of the same index otherwise. A 16-feature MFMA block is
+// SwiGLU packing interleaves gate and up in groups of 32 features: packed
+// feature j of a shard is gate column 32 * (j / 64) + j % 32 when j % 64 < 32,
+// and the up column of the same index otherwise. A 32-feature MFMA block is
 // thus all-gate or all-up, and blocks 2q and 2q + 1 pair up element by element.
 
 // Wavefront-uniform workgroup id remapped so that consecutive logical ids run

@@ -2,9 +2,9 @@
 //
 // Both products run with the weights as the MFMA A operand (rows = output
 // features) and the tokens as the B operand (columns = tokens), using
-// v_mfma_f32_16x16x32_bf16. Each lane then holds 4 consecutive output
-// features of one token, so the epilogue writes H (bf16) and Y (fp32) rows
-// straight from registers.
+// v_mfma_f32_32x32x16_bf16. Each lane then holds, per 32 x 32 block, four
+// runs of 4 consecutive output features of one token, so the epilogue writes
+// H (bf16) and Y (fp32) rows straight from registers.
 //
 // gateup_tiled: H_k = act(X . W_{order[k]}) for every ring step k, the
 //   SwiGLU or GeLU epilogue applied in registers ("Tensor Parallelism:
@@ -18,13 +18,16 @@
 //   whole walk, so Y is written once ("Folding Tensor and Sequence
 //   Parallelism ...", Abstract: partial outputs accumulate locally).
 //
-// Main loop: 32 reduction indices per stage, a 4-deep LDS ring filled by
-// global_load_lds_dwordx4 (global memory straight into LDS, no register
-// staging). Loads for stage t + 3 are issued right after the barrier of
-// stage t, so each stage's loads have three stages of MFMA work to land. LDS
-// is laid out in fragment blocks (1 KiB per 16 rows x 32 reduction indices,
-// lane-ordered), so every operand fragment read is one contiguous
-// 16-byte-per-lane access.
+// Main loop: 32 reduction indices per stage. Global memory is loaded into
+// registers two stages ahead and written to a 3-deep LDS ring laid out in
+// fragment blocks, so every operand fragment read is one contiguous (or
+// XOR-swizzled) 16-byte-per-lane access without bank conflicts. The waves
+// run a two-group ping-pong (see mainloop): on every SIMD one wave issues
+// MFMAs while the other moves data. Measured on this part, plain vector
+// loads overlap with MFMA issue on the same SIMD, while global-to-LDS DMA
+// loads (global_load_lds) largely serialise with it; and one wave issuing
+// 32x32x16 MFMAs back to back keeps the matrix pipe busy, which the 16x16x32
+// form does not.
 #include "common.h"
 #include "launch.h"
 
@@ -37,15 +40,16 @@ struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int NW = WM * WN;                   // waves
     static constexpr int NT = NW * 64;                   // threads
-    static constexpr int TM = BM / WM / 16;              // MFMA blocks per wave along features
-    static constexpr int TN = BN / WN / 16;              // MFMA blocks per wave along tokens
-    static constexpr int A_BLK = BM / 16;                // 1 KiB fragment blocks per stage (A)
+    static constexpr int TM = BM / WM / 32;              // 32-row MFMA blocks per wave (features)
+    static constexpr int TN = BN / WN / 32;              // 32-column MFMA blocks per wave (tokens)
+    static constexpr int A_BLK = BM / 16;                // 1 KiB blocks per stage (A)
     static constexpr int B_BLK = BN / 16;                // (B)
-    static constexpr int LOADS = (A_BLK + B_BLK) / NW;   // DMA loads per wave per stage
+    static constexpr int LA = A_BLK / NW;                // A blocks each wave loads per stage
+    static constexpr int LB = B_BLK / NW;                // B blocks each wave loads per stage
     static constexpr int STAGE = (A_BLK + B_BLK) * 512;  // bf16 elements per stage (32-deep)
-    static constexpr int NS = 4;                         // stages in the LDS ring
+    static constexpr int NS = 3;                         // stages in the LDS ring
     static_assert(TM >= 1 && TN >= 1, "wave tile");
-    static_assert(LOADS * NW == A_BLK + B_BLK, "loader split");
+    static_assert(LA * NW == A_BLK && LB * NW == B_BLK, "loader split");
     static_assert(NS * STAGE * 2 <= 160 * 1024, "LDS");
 };
 
@@ -61,43 +65,73 @@ __device__ inline void raster(int L, int n_f, int n_t, int& ttile, int& flin) {
     flin = rem / gt;
 }
 
-// One pipeline stage = 32 reduction indices of the A slab (BM packed weight
-// rows, 16-row fragment blocks) and the B slab (BN tokens). Each wave moves
-// LOADS whole 1 KiB blocks with global_load_lds_dwordx4: the 64 lanes' 16-byte
-// pieces land contiguously in LDS, already in fragment order. Token rows past
-// T are clamped to row T - 1 (their outputs are never stored).
+// LDS layout of one stage (32 reduction indices):
+//   A blocks are the packed 32 x 16 fragment blocks, already in MFMA order:
+//   stage block b < A_BLK is (row block b / 2, reduction block b % 2).
+//   B blocks hold 16 tokens x the stage's 32 reduction indices, so one wave
+//   load reads 16 whole 64-byte row pieces of X (or H). Inside a block, token
+//   r's 8-index chunk c sits in 16-byte slot 4 r + (c ^ ((r >> 2) & 3)); the
+//   XOR keeps both the writes and the MFMA fragment reads (16 tokens x one
+//   chunk per lane group) free of LDS bank conflicts.
+__device__ __forceinline__ int tok_slot(int r, int c) { return 4 * r + (c ^ ((r >> 2) & 3)); }
+
+// One stage's share of global data for one thread: up to two A and two B
+// 16-byte pieces, as named members (register arrays of two elements are not
+// reliably kept in registers by the compiler).
+struct StageRegs {
+    u32x4 a0, a1, b0, b1;
+};
+
+// Global loads of one stage into registers. Each wave loads whole 1 KiB
+// blocks (block i * NW + w). Token rows past T are clamped to row T - 1
+// (their outputs are never stored).
 template <class C>
-__device__ __forceinline__ void issue_stage(uint16_t* lds_stage, const uint16_t* __restrict__ a_base,
-                                            int64_t a_rs, const uint16_t* __restrict__ b_src, int ldb,
-                                            int64_t b_koff, int t0, int T, int w, int lane) {
-#pragma unroll
-    for (int r = 0; r < C::LOADS; ++r) {
-        const int b = r * C::NW + w;                     // wave-uniform block id
-        const uint16_t* g;
-        if (b < C::A_BLK) {
-            g = a_base + b * a_rs + lane * 8;
-        } else {
-            const int tok = min(t0 + (b - C::A_BLK) * 16 + (lane & 15), T - 1);
-            g = b_src + (int64_t)tok * ldb + b_koff + (lane >> 4) * 8;
-        }
-        __builtin_amdgcn_global_load_lds(g, (TSP_LDS void*)(lds_stage + b * 512), 16, 0, 0);
-    }
+__device__ __forceinline__ void load_stage(StageRegs& r, const uint16_t* __restrict__ a_base, int64_t a_rs,
+                                           const uint16_t* __restrict__ b_src, int ldb, int64_t b_koff,
+                                           int t0, int T, int w, int lane) {
+    static_assert(C::LA >= 1 && C::LA <= 2 && C::LB >= 1 && C::LB <= 2, "stage split");
+    auto a_ptr = [&](int i) {
+        const int b = i * C::NW + w;
+        return reinterpret_cast<const u32x4*>(a_base + (b >> 1) * a_rs + (b & 1) * 512 + lane * 8);
+    };
+    auto b_ptr = [&](int i) {
+        const int bb = i * C::NW + w;
+        const int tok = min(t0 + bb * 16 + (lane >> 2), T - 1);
+        return reinterpret_cast<const u32x4*>(b_src + (int64_t)tok * ldb + b_koff + (lane & 3) * 8);
+    };
+    r.a0 = *a_ptr(0);
+    if constexpr (C::LA > 1) r.a1 = *a_ptr(1);
+    r.b0 = *b_ptr(0);
+    if constexpr (C::LB > 1) r.b1 = *b_ptr(1);
 }
 
-// Wait until at most `newer` stages of this wave's DMA loads are outstanding.
 template <class C>
-__device__ __forceinline__ void wait_stages(int newer) {
-    // s_waitcnt with vmcnt = newer * LOADS, expcnt / lgkmcnt left at their maximum
-#define TSP_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-    if (newer >= 3) TSP_VMCNT(3 * C::LOADS);
-    else if (newer == 2) TSP_VMCNT(2 * C::LOADS);
-    else if (newer == 1) TSP_VMCNT(C::LOADS);
-    else TSP_VMCNT(0);
-#undef TSP_VMCNT
+__device__ __forceinline__ void store_stage(uint16_t* lds_stage, const StageRegs& r, int w, int lane) {
+    u32x4* as = reinterpret_cast<u32x4*>(lds_stage);
+    u32x4* bs = reinterpret_cast<u32x4*>(lds_stage + C::A_BLK * 512);
+    const int slot = tok_slot(lane >> 2, lane & 3);
+    as[w * 64 + lane] = r.a0;
+    if constexpr (C::LA > 1) as[(C::NW + w) * 64 + lane] = r.a1;
+    bs[w * 64 + slot] = r.b0;
+    if constexpr (C::LB > 1) bs[(C::NW + w) * 64 + slot] = r.b1;
 }
 
-// Workgroup barrier that orders LDS traffic without waiting for the DMA
-// loads still in flight for later stages (__syncthreads would drain them).
+__device__ __forceinline__ void vmcnt_le(int n) {
+    // s_waitcnt with vmcnt = n (n <= 15), expcnt / lgkmcnt left at their maximum
+    if (n >= 8) __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8));
+    else if (n >= 4) __builtin_amdgcn_s_waitcnt(4 | (7 << 4) | (15 << 8));
+    else if (n >= 3) __builtin_amdgcn_s_waitcnt(3 | (7 << 4) | (15 << 8));
+    else if (n >= 2) __builtin_amdgcn_s_waitcnt(2 | (7 << 4) | (15 << 8));
+    else if (n >= 1) __builtin_amdgcn_s_waitcnt(1 | (7 << 4) | (15 << 8));
+    else __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void lgkm_zero() {
+    __builtin_amdgcn_s_waitcnt((15 & 15) | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+// Workgroup barrier that orders LDS traffic without draining the global
+// loads still in flight for later stages (__syncthreads would wait for them).
 __device__ __forceinline__ void stage_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -105,137 +139,379 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 template <class C>
-__device__ __forceinline__ void read_frags(const uint16_t* lds_stage, bf16x8 (&af)[C::TM],
-                                           bf16x8 (&bv)[C::TN], int wm, int wn, int lane) {
+__device__ __forceinline__ void read_frags(const uint16_t* lds_stage, bf16x8 (&af)[2][C::TM],
+                                           bf16x8 (&bv)[2][C::TN], int wm, int wn, int lane) {
     const bf16x8* as = reinterpret_cast<const bf16x8*>(lds_stage);
     const bf16x8* bs = reinterpret_cast<const bf16x8*>(lds_stage + C::A_BLK * 512);
+    // B fragment (32 tokens x 16 indices): lane l takes token l % 32, i.e.
+    // block 2 j' + (l / 16) % 2, row l % 16, chunk 2 kk + l / 32.
+    const int r = lane & 15, half = (lane >> 4) & 1, hi = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i) af[i] = as[(wm * C::TM + i) * 64 + lane];
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) bv[j] = bs[(wn * C::TN + j) * 64 + lane];
+        for (int i = 0; i < C::TM; ++i) af[kk][i] = as[((wm * C::TM + i) * 2 + kk) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+            bv[kk][j] = bs[((wn * C::TN + j) * 2 + half) * 64 + tok_slot(r, 2 * kk + hi)];
+    }
 }
 
 template <class C>
-__device__ __forceinline__ void mfma_stage(f32x4 (&acc)[C::TM][C::TN], const bf16x8 (&af)[C::TM],
-                                           const bf16x8 (&bv)[C::TN]) {
+__device__ __forceinline__ void mfma_stage(f32x16 (&acc)[C::TM][C::TN], const bf16x8 (&af)[2][C::TM],
+                                           const bf16x8 (&bv)[2][C::TN]) {
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i)
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bv[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bv[kk][j], acc[i][j], 0, 0, 0);
 }
 
 // The reduction loop shared by both kernels. `src(t, a_base, b_koff)` gives
 // step t's A slab start and B reduction offset (32 indices per step).
 //
 // Ping-pong schedule: the waves form two groups (waves 0..NW/2-1 and the
-// rest), one wave of each group per SIMD. Each step t is a memory phase M(t)
-// (issue the DMA loads of stage t + 3, read stage t's fragments from LDS) and
+// rest), one wave of each group per SIMD. Step t is a memory phase M(t) and
 // a compute phase C(t) (the MFMAs). Group 1 runs one phase behind group 0,
 // and every phase boundary is a workgroup barrier, so on each SIMD one wave
-// computes while the other does its memory work.
+// computes while the other does its memory work. Barrier b_{2t} opens group
+// 0's M(t); b_{2t+1} opens group 0's C(t) and group 1's M(t).
 //
-// Barrier b_{2t} opens group 0's M(t) (group 1's C(t-1)); b_{2t+1} opens
-// group 0's C(t) (group 1's M(t)). Every wave makes its own stage-t loads
-// complete before b_{2t}, so stage t is visible to both groups' M(t). The
-// DMA of stage t + 3 goes into stage t - 1's buffer, whose last reader
-// (group 1's M(t-1), which drains its LDS reads before b_{2t}) is done.
+// M(t): wait for the registers holding stage t + 2 (loaded in M(t-2)), write
+// them to LDS buffer (t + 2) % 3, load stage t + 4 into them, read stage t's
+// fragments, and drain the LDS traffic (lgkmcnt 0) before the next barrier.
+// Exactly one stage of loads is issued per step, so "stage t + 2 landed" is
+// always vmcnt <= loads-per-stage.
+// Stage t + 2's buffer was last read by M(t-1) of both groups, which ended
+// before b_{2t}; stage t was written in M(t-2) of both groups, which ended
+// before b_{2t-1}. Two register sets hold the stages in flight, so the loop
+// is unrolled by two.
+// One step of the ping-pong loop for the register set rr that holds stage
+// t + 2 (see mainloop).
 template <class C, class Src>
-__device__ __forceinline__ void mainloop(uint16_t* lds, f32x4 (&acc)[C::TM][C::TN], int ksteps,
+__device__ __forceinline__ void pp_step(int t, int K, uint16_t* lds, StageRegs& rr,
+                                        f32x16 (&acc)[C::TM][C::TN], int64_t a_rs, const uint16_t* b_src,
+                                        int ldb, int t0, int T, int w, int wm, int wn, int lane, Src& src) {
+    constexpr int LPS = C::LA + C::LB;                  // global loads per stage per thread
+    bf16x8 af[2][C::TM], bv[2][C::TN];
+    stage_barrier();                                    // g0: b_{2t}, g1: b_{2t+1}
+    __builtin_amdgcn_sched_barrier(0);
+    // Unconditional: past the end the loads fetch the last stage again and
+    // the stores fill a free buffer that is never read, so the compiler sees
+    // one fixed load order and keeps the two stages in flight.
+    vmcnt_le(LPS);                                      // stage t + 2 landed in rr
+    store_stage<C>(lds + ((t + 2) % C::NS) * C::STAGE, rr, w, lane);
+    {
+        const uint16_t* ab;
+        int64_t bk;
+        src(min(t + 4, K - 1), ab, bk);
+        load_stage<C>(rr, ab, a_rs, b_src, ldb, bk, t0, T, w, lane);
+    }
+    read_frags<C>(lds + (t % C::NS) * C::STAGE, af, bv, wm, wn, lane);
+    lgkm_zero();
+    __builtin_amdgcn_sched_barrier(0);
+    stage_barrier();                                    // g0: b_{2t+1}, g1: b_{2t+2}
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    mfma_stage<C>(acc, af, bv);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The reduction loop shared by both kernels. `src(t, a_base, b_koff)` gives
+// step t's A slab start and B reduction offset (32 indices per step).
+//
+// Ping-pong schedule: the waves form two groups (waves 0..NW/2-1 and the
+// rest), one wave of each group per SIMD. Step t is a memory phase M(t) and
+// a compute phase C(t) (the MFMAs). Group 1 runs one phase behind group 0,
+// and every phase boundary is a workgroup barrier, so on each SIMD one wave
+// computes while the other does its memory work. Barrier b_{2t} opens group
+// 0's M(t); b_{2t+1} opens group 0's C(t) and group 1's M(t).
+//
+// M(t): wait for the registers holding stage t + 2 (loaded in M(t-2)), write
+// them to LDS buffer (t + 2) % 3, load stage t + 4 into them, read stage t's
+// fragments, and drain the LDS traffic (lgkmcnt 0) before the next barrier.
+// Exactly one stage of loads is issued per step, so "stage t + 2 landed" is
+// always vmcnt <= loads-per-stage.
+// Stage t + 2's buffer was last read by M(t-1) of both groups, which ended
+// before b_{2t}; stage t was written in M(t-2) of both groups, which ended
+// before b_{2t-1}. Two register sets hold the stages in flight, so the loop
+// is unrolled by two.
+template <class C, class Src>
+__device__ __forceinline__ void mainloop(uint16_t* lds, f32x16 (&acc)[C::TM][C::TN], int K,
                                          int64_t a_rs, const uint16_t* b_src, int ldb, int t0, int T,
-                                         Src&& src) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+                                         Src src) {
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int wm = w / C::WN, wn = w % C::WN;
     const bool g1 = w >= C::NW / 2;
+    constexpr int LPS = C::LA + C::LB;
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto issue = [&](int t) {
-        const uint16_t* ab;
-        int64_t bk;
-        src(t, ab, bk);
-        issue_stage<C>(lds + (t % C::NS) * C::STAGE, ab, a_rs, b_src, ldb, bk, t0, T, w, lane);
-    };
-    constexpr int AHEAD = C::NS - 1;                    // stages in flight ahead of the reader
-    const int pro = min(AHEAD, ksteps);
-    for (int t = 0; t < pro; ++t) issue(t);
-    wait_stages<C>(pro - 1);                            // own stage-0 loads landed
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    StageRegs r0, r1;
+    const uint16_t* ab;
+    int64_t bk;
+    // prologue: stages 0 and 1 go to LDS, stages 2 and 3 stay in registers
+    // (stage indices past the end are clamped; that data is never read)
+    src(0, ab, bk);
+    load_stage<C>(r0, ab, a_rs, b_src, ldb, bk, t0, T, w, lane);
+    src(min(1, K - 1), ab, bk);
+    load_stage<C>(r1, ab, a_rs, b_src, ldb, bk, t0, T, w, lane);
+    vmcnt_le(LPS);
+    store_stage<C>(lds, r0, w, lane);
+    vmcnt_le(0);
+    store_stage<C>(lds + C::STAGE, r1, w, lane);
+    // keep the issue order r0 then r1: the loop's waits count on it
+    __builtin_amdgcn_sched_barrier(0);
+    src(min(2, K - 1), ab, bk);
+    load_stage<C>(r0, ab, a_rs, b_src, ldb, bk, t0, T, w, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    src(min(3, K - 1), ab, bk);
+    load_stage<C>(r1, ab, a_rs, b_src, ldb, bk, t0, T, w, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    lgkm_zero();
     if (g1) stage_barrier();                            // b_0: group 1 sits out phase 0
-    bf16x8 af[C::TM], bv[C::TN];
-    for (int t = 0; t < ksteps; ++t) {
-        stage_barrier();                                // g0: b_{2t}, g1: b_{2t+1}
-        __builtin_amdgcn_sched_barrier(0);
-        if (t + AHEAD < ksteps) issue(t + AHEAD);
-        read_frags<C>(lds + (t % C::NS) * C::STAGE, af, bv, wm, wn, lane);
-        __builtin_amdgcn_s_waitcnt((15 & 15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
-        // stage t + 1 must be complete before b_{2t+2}: group 1 reaches it
-        // at the end of this memory phase, group 0 after its compute phase
-        const int newer = min(t + AHEAD, ksteps - 1) - (t + 1);
-        if (g1) wait_stages<C>(newer);
-        __builtin_amdgcn_sched_barrier(0);
-        stage_barrier();                                // g0: b_{2t+1}, g1: b_{2t+2}
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_setprio(1);
-        mfma_stage<C>(acc, af, bv);
-        __builtin_amdgcn_s_setprio(0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (!g1) wait_stages<C>(newer);
+    // K is even (d and F are multiples of 64): both unrolled steps always
+    // run, so no path through the loop skips a load, and the compiler's
+    // wait analysis sees the same load order on every edge.
+    for (int t = 0; t < K; t += 2) {
+        pp_step<C>(t, K, lds, r0, acc, a_rs, b_src, ldb, t0, T, w, wm, wn, lane, src);
+        pp_step<C>(t + 1, K, lds, r1, acc, a_rs, b_src, ldb, t0, T, w, wm, wn, lane, src);
     }
     if (!g1) stage_barrier();                           // b_{2K}: group 0 matches group 1's count
 }
 
-// act: 1 = SwiGLU (packed blocks alternate gate / up), 2 = GeLU (tanh form)
+// ---- one wave per SIMD: 4 waves, each a 128 x 128 sub-tile ----------------
+//
+// Single instruction stream per SIMD: the wave keeps 256 fp32 accumulators
+// (16 blocks of 32 x 32, in AGPRs) and interleaves everything else with its
+// MFMAs. Per step t (32 reduction indices, two 16-wide halves):
+//   barrier                       stage t + 1 visible, stage t - 1 free
+//   MFMAs of stage t, half 0      (fragments read during step t - 1)
+//     + read half 1 of stage t, write the registers holding stage t + 2 to
+//       LDS buffer (t + 2) % 3, load stage t + 4 into those registers
+//   MFMAs of stage t, half 1
+//     + read half 0 of stage t + 1
+//   drain LDS traffic (lgkmcnt 0)
+// Global data is loaded two steps before it is written to LDS; two register
+// sets alternate, so the loop is unrolled by two (K is even).
+template <class C>
+struct StageRegs8 {
+    static constexpr int N = (C::A_BLK + C::B_BLK) / C::NW;   // 16-byte pieces per thread
+    u32x4 v[N];
+};
+
+template <class C>
+__device__ __forceinline__ void load_stage8(StageRegs8<C>& r, const uint16_t* __restrict__ a_base, int64_t a_rs,
+                                            const uint16_t* __restrict__ b_src, int ldb, int64_t b_koff,
+                                            int t0, int T, int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < StageRegs8<C>::N; ++i) {
+        const int b = i * C::NW + w;
+        if (b < C::A_BLK) {
+            r.v[i] = *reinterpret_cast<const u32x4*>(a_base + (b >> 1) * a_rs + (b & 1) * 512 + lane * 8);
+        } else {
+            const int bb = b - C::A_BLK;
+            const int tok = min(t0 + bb * 16 + (lane >> 2), T - 1);
+            r.v[i] = *reinterpret_cast<const u32x4*>(b_src + (int64_t)tok * ldb + b_koff + (lane & 3) * 8);
+        }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void store_stage8(uint16_t* lds_stage, const StageRegs8<C>& r, int w, int lane) {
+    u32x4* as = reinterpret_cast<u32x4*>(lds_stage);
+    u32x4* bs = reinterpret_cast<u32x4*>(lds_stage + C::A_BLK * 512);
+    const int slot = tok_slot(lane >> 2, lane & 3);
+#pragma unroll
+    for (int i = 0; i < StageRegs8<C>::N; ++i) {
+        const int b = i * C::NW + w;
+        if (b < C::A_BLK) as[b * 64 + lane] = r.v[i];
+        else bs[(b - C::A_BLK) * 64 + slot] = r.v[i];
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void read_half(const uint16_t* lds_stage, int kk, bf16x8 (&af)[C::TM],
+                                          bf16x8 (&bv)[C::TN], int wm, int wn, int lane) {
+    const bf16x8* as = reinterpret_cast<const bf16x8*>(lds_stage);
+    const bf16x8* bs = reinterpret_cast<const bf16x8*>(lds_stage + C::A_BLK * 512);
+    const int r = lane & 15, half = (lane >> 4) & 1, hi = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) af[i] = as[((wm * C::TM + i) * 2 + kk) * 64 + lane];
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) bv[j] = bs[((wn * C::TN + j) * 2 + half) * 64 + tok_slot(r, 2 * kk + hi)];
+}
+
+template <class C>
+__device__ __forceinline__ void mfma_half(f32x16 (&acc)[C::TM][C::TN], const bf16x8 (&af)[C::TM],
+                                          const bf16x8 (&bv)[C::TN]) {
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bv[j], acc[i][j], 0, 0, 0);
+}
+
+template <class C, class Src>
+__device__ __forceinline__ void w4_step(int t, int K, uint16_t* lds, StageRegs8<C>& rr,
+                                        f32x16 (&acc)[C::TM][C::TN], bf16x8 (&a0)[C::TM], bf16x8 (&b0)[C::TN],
+                                        bf16x8 (&a1)[C::TM], bf16x8 (&b1)[C::TN], int64_t a_rs,
+                                        const uint16_t* b_src, int ldb, int t0, int T, int w, int wm, int wn,
+                                        int lane, Src& src) {
+    constexpr int NLD = StageRegs8<C>::N;
+    stage_barrier();
+    // half 0 of stage t (in a0, b0) while reading half 1 and moving stage t + 2
+    read_half<C>(lds + (t % C::NS) * C::STAGE, 1, a1, b1, wm, wn, lane);
+    vmcnt_le(NLD);                                      // stage t + 2 landed in rr
+    store_stage8<C>(lds + ((t + 2) % C::NS) * C::STAGE, rr, w, lane);
+    {
+        const uint16_t* ab;
+        int64_t bk;
+        src(min(t + 4, K - 1), ab, bk);                 // past the end: refetch, never read
+        load_stage8<C>(rr, ab, a_rs, b_src, ldb, bk, t0, T, w, lane);
+    }
+    mfma_half<C>(acc, a0, b0);
+#pragma unroll
+    for (int r = 0; r < C::TM + C::TN; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    }
+#pragma unroll
+    for (int r = 0; r < NLD; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    }
+    // half 1 of stage t while reading half 0 of stage t + 1 (visible since
+    // the barrier: it was written during step t - 1)
+    read_half<C>(lds + ((t + 1) % C::NS) * C::STAGE, 0, a0, b0, wm, wn, lane);
+    mfma_half<C>(acc, a1, b1);
+#pragma unroll
+    for (int r = 0; r < C::TM + C::TN; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    lgkm_zero();
+}
+
+template <class C, class Src>
+__device__ __forceinline__ void mainloop_4w(uint16_t* lds, f32x16 (&acc)[C::TM][C::TN], int K,
+                                            int64_t a_rs, const uint16_t* b_src, int ldb, int t0, int T,
+                                            Src src) {
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = w / C::WN, wn = w % C::WN;
+    constexpr int NLD = StageRegs8<C>::N;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    StageRegs8<C> r0, r1;
+    const uint16_t* ab;
+    int64_t bk;
+    src(0, ab, bk);
+    load_stage8<C>(r0, ab, a_rs, b_src, ldb, bk, t0, T, w, lane);
+    src(min(1, K - 1), ab, bk);
+    load_stage8<C>(r1, ab, a_rs, b_src, ldb, bk, t0, T, w, lane);
+    vmcnt_le(NLD);
+    store_stage8<C>(lds, r0, w, lane);
+    vmcnt_le(0);
+    store_stage8<C>(lds + C::STAGE, r1, w, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    src(min(2, K - 1), ab, bk);
+    load_stage8<C>(r0, ab, a_rs, b_src, ldb, bk, t0, T, w, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    src(min(3, K - 1), ab, bk);
+    load_stage8<C>(r1, ab, a_rs, b_src, ldb, bk, t0, T, w, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    lgkm_zero();
+    stage_barrier();
+    bf16x8 a0[C::TM], b0[C::TN], a1[C::TM], b1[C::TN];
+    read_half<C>(lds, 0, a0, b0, wm, wn, lane);
+    lgkm_zero();
+    for (int t = 0; t < K; t += 2) {                    // K is even
+        w4_step<C>(t, K, lds, r0, acc, a0, b0, a1, b1, a_rs, b_src, ldb, t0, T, w, wm, wn, lane, src);
+        w4_step<C>(t + 1, K, lds, r1, acc, a0, b0, a1, b1, a_rs, b_src, ldb, t0, T, w, wm, wn, lane, src);
+    }
+}
+
+template <class C, class Src>
+__device__ __forceinline__ void run_mainloop(uint16_t* lds, f32x16 (&acc)[C::TM][C::TN], int K,
+                                             int64_t a_rs, const uint16_t* b_src, int ldb, int t0, int T,
+                                             Src src) {
+    if constexpr (C::NW == 4 && C::TM == 4 && C::TN == 4)
+        mainloop_4w<C>(lds, acc, K, a_rs, b_src, ldb, t0, T, src);
+    else
+        mainloop<C>(lds, acc, K, a_rs, b_src, ldb, t0, T, src);
+}
+
+// act: 1 = SwiGLU (packed 32-row blocks alternate gate / up), 2 = GeLU (tanh form)
 template <int BM, int BN, int WM, int WN, int ACT>
-__global__ __launch_bounds__(WM * WN * 64) void gateup_tiled(Bf16Args a, int n_ft_shard, int n_tt) {
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void gateup_tiled(Bf16Args a, int n_ft_shard, int n_tt) {
     using C = TileCfg<BM, BN, WM, WN>;
+    static_assert(ACT != 1 || C::TM % 2 == 0, "SwiGLU pairs gate and up blocks inside a wave");
     __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
 
     int ttile, flin;
     raster(xcd_remap(blockIdx.x, gridDim.x), a.P * n_ft_shard, n_tt, ttile, flin);
     const int s = flin / n_ft_shard;                    // ring step = packed record
     const int ftile = flin - s * n_ft_shard;
-    const int64_t a_rs = (int64_t)(a.d >> 5) * 512;     // elements per 16-row block row
-    const uint16_t* a_tile = a.packed + (int64_t)s * a.shard_elems + (int64_t)(ftile * (BM / 16)) * a_rs;
+    const int64_t a_rs = (int64_t)(a.d >> 4) * 512;     // elements per 32-row block row
+    const uint16_t* a_tile = a.packed + (int64_t)s * a.shard_elems + (int64_t)(ftile * (BM / 32)) * a_rs;
     const int t0 = ttile * BN;
 
-    f32x4 acc[C::TM][C::TN];
-    mainloop<C>(lds, acc, a.d >> 5, a_rs, a.x, a.d, t0, a.T,
+    f32x16 acc[C::TM][C::TN];
+    run_mainloop<C>(lds, acc, a.d >> 5, a_rs, a.x, a.d, t0, a.T,
                 [&](int t, const uint16_t*& ab, int64_t& bk) {
-                    ab = a_tile + (int64_t)t * 512;
+                    ab = a_tile + (int64_t)t * 1024;
                     bk = (int64_t)t * 32;
                 });
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w / WN, wn = w % WN;
+    const int fsub = 4 * (lane >> 5);                   // feature offset inside each run of 8
     if constexpr (ACT == 1) {
 #pragma unroll
         for (int p = 0; p < C::TM / 2; ++p) {
-            const int gb = ftile * (BM / 16) + wm * C::TM + 2 * p;     // gate block (even)
-            const int hcol = s * a.F + (gb >> 1) * 16 + (lane >> 4) * 4;
+            const int gb = ftile * (BM / 32) + wm * C::TM + 2 * p;     // gate block (even)
+            const int hbase = s * a.F + (gb >> 1) * 32 + fsub;
 #pragma unroll
             for (int j = 0; j < C::TN; ++j) {
-                const int tok = t0 + (wn * C::TN + j) * 16 + (lane & 15);
+                const int tok = t0 + (wn * C::TN + j) * 32 + (lane & 31);
                 if (tok < a.T) {
-                    const f32x4 g = acc[2 * p][j], u = acc[2 * p + 1][j];
-                    *reinterpret_cast<uint2*>(a.h + (int64_t)tok * a.f + hcol) =
-                        pack4_bf16(silu_f(g[0]) * u[0], silu_f(g[1]) * u[1],
-                                   silu_f(g[2]) * u[2], silu_f(g[3]) * u[3]);
+                    const f32x16 g = acc[2 * p][j], u = acc[2 * p + 1][j];
+                    uint16_t* hrow = a.h + (int64_t)tok * a.f + hbase;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<uint2*>(hrow + 8 * q) =
+                            pack4_bf16(silu_f(g[4 * q]) * u[4 * q], silu_f(g[4 * q + 1]) * u[4 * q + 1],
+                                       silu_f(g[4 * q + 2]) * u[4 * q + 2], silu_f(g[4 * q + 3]) * u[4 * q + 3]);
                 }
             }
         }
     } else {
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) {
-            const int hcol = s * a.F + (ftile * (BM / 16) + wm * C::TM + i) * 16 + (lane >> 4) * 4;
+            const int hbase = s * a.F + (ftile * (BM / 32) + wm * C::TM + i) * 32 + fsub;
 #pragma unroll
             for (int j = 0; j < C::TN; ++j) {
-                const int tok = t0 + (wn * C::TN + j) * 16 + (lane & 15);
+                const int tok = t0 + (wn * C::TN + j) * 32 + (lane & 31);
                 if (tok < a.T) {
-                    const f32x4 u = acc[i][j];
-                    *reinterpret_cast<uint2*>(a.h + (int64_t)tok * a.f + hcol) =
-                        pack4_bf16(gelu_tanh_f(u[0]), gelu_tanh_f(u[1]), gelu_tanh_f(u[2]),
-                                   gelu_tanh_f(u[3]));
+                    const f32x16 u = acc[i][j];
+                    uint16_t* hrow = a.h + (int64_t)tok * a.f + hbase;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<uint2*>(hrow + 8 * q) =
+                            pack4_bf16(gelu_tanh_f(u[4 * q]), gelu_tanh_f(u[4 * q + 1]),
+                                       gelu_tanh_f(u[4 * q + 2]), gelu_tanh_f(u[4 * q + 3]));
                 }
             }
         }
@@ -243,35 +519,234 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_tiled(Bf16Args a, int n_f
 }
 
 template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64) void down_tiled(Bf16Args a, int n_ft, int n_tt) {
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void down_tiled(Bf16Args a, int n_ft, int n_tt) {
     using C = TileCfg<BM, BN, WM, WN>;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
 
     int ttile, ftile;
     raster(xcd_remap(blockIdx.x, gridDim.x), n_ft, n_tt, ttile, ftile);
-    const int spp = a.F >> 5;                           // steps per shard
-    const int64_t a_rs = (int64_t)spp * 512;
-    const uint16_t* a_ft = a.packed + a.down_off + (int64_t)(ftile * (BM / 16)) * a_rs;
+    const int spp = a.F >> 5;                           // 32-wide steps per shard
+    const int64_t a_rs = (int64_t)(a.F >> 4) * 512;     // elements per 32-row block row
+    const uint16_t* a_ft = a.packed + a.down_off + (int64_t)(ftile * (BM / 32)) * a_rs;
     const int t0 = ttile * BN;
 
-    f32x4 acc[C::TM][C::TN];
+    f32x16 acc[C::TM][C::TN];
     // Reduction step t is local step t % spp of ring step t / spp; records
     // and H columns are both stored in ring order, so this is a linear walk.
-    mainloop<C>(lds, acc, a.P * spp, a_rs, a.h, a.f, t0, a.T,
+    run_mainloop<C>(lds, acc, a.P * spp, a_rs, a.h, a.f, t0, a.T,
                 [&](int t, const uint16_t*& ab, int64_t& bk) {
                     const int k = t / spp, ls = t - k * spp;
-                    ab = a_ft + (int64_t)k * a.shard_elems + (int64_t)ls * 512;
+                    ab = a_ft + (int64_t)k * a.shard_elems + (int64_t)ls * 1024;
                     bk = (int64_t)t * 32;
                 });
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w / WN, wn = w % WN;
+    const int fsub = 4 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {
-        const int n = ftile * BM + (wm * C::TM + i) * 16 + (lane >> 4) * 4;
+        const int n = ftile * BM + (wm * C::TM + i) * 32 + fsub;
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
-            const int tok = t0 + (wn * C::TN + j) * 16 + (lane & 15);
+            const int tok = t0 + (wn * C::TN + j) * 32 + (lane & 31);
+            if (tok < a.T) {
+                const f32x16 v = acc[i][j];
+                float* yrow = a.y + (int64_t)tok * a.d + n;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<float4*>(yrow + 8 * q) =
+                        make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+            }
+        }
+    }
+}
+
+// ---- 16x16x32 ping-pong over global-to-LDS loads --------------------------
+//
+// Same packed layout, tile 256 features x 256 tokens, 8 waves as 4 x 2 (wave
+// tile 64 x 128 as 4 x 8 MFMA blocks of 16 x 16). Global data goes straight
+// into a 4-deep LDS ring with global_load_lds_dwordx4 (no staging registers),
+// and the waves run the two-group ping-pong with 16x16x32 MFMAs. A 16x16x32
+// A fragment (16 rows x 32 indices) is gathered from two 32 x 16 blocks;
+// a 16x16x32 B fragment is exactly one 16-token LDS block.
+namespace pp16 {
+
+constexpr int BM = 256, BN = 256, NW = 8, WN = 2;
+constexpr int TM = 4, TN = 8;                           // 16-row / 16-token MFMA blocks per wave
+constexpr int A_BLK = BM / 16, B_BLK = BN / 16;         // 1 KiB blocks per 32-wide stage
+constexpr int LOADS = (A_BLK + B_BLK) / NW;
+constexpr int STAGE = (A_BLK + B_BLK) * 512;
+constexpr int NS = 4;
+
+__device__ __forceinline__ void issue(uint16_t* lds_stage, const uint16_t* __restrict__ a_base, int64_t a_rs,
+                                      const uint16_t* __restrict__ b_src, int ldb, int64_t b_koff, int t0,
+                                      int T, int w, int lane) {
+    const int r = lane >> 2;                            // token inside a B block
+    const int c = (lane & 3) ^ ((r >> 2) & 3);          // chunk this lane fetches (slot = lane)
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int b = i * NW + w;                       // wave-uniform block id
+        const uint16_t* g;
+        if (b < A_BLK) {
+            g = a_base + (b >> 1) * a_rs + (b & 1) * 512 + lane * 8;
+        } else {
+            const int tok = min(t0 + (b - A_BLK) * 16 + r, T - 1);
+            g = b_src + (int64_t)tok * ldb + b_koff + c * 8;
+        }
+        __builtin_amdgcn_global_load_lds(g, (TSP_LDS void*)(lds_stage + b * 512), 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void wait_stages(int newer) {
+#define TSP_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+    if (newer >= 2) TSP_VMCNT(2 * LOADS);
+    else if (newer == 1) TSP_VMCNT(LOADS);
+    else TSP_VMCNT(0);
+#undef TSP_VMCNT
+}
+
+__device__ __forceinline__ void read_frags(const uint16_t* lds_stage, bf16x8 (&af)[TM], bf16x8 (&bv)[TN],
+                                           int wm, int wn, int lane) {
+    const bf16x8* as = reinterpret_cast<const bf16x8*>(lds_stage);
+    const bf16x8* bs = reinterpret_cast<const bf16x8*>(lds_stage + A_BLK * 512);
+    const int r = lane & 15, c = lane >> 4;             // row / token, 8-index chunk (0..3)
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int ib = wm * TM + i;                     // 16-row block in the tile
+        // rows 16 (ib % 2) + r of 32-row block ib / 2, reduction block c / 2
+        af[i] = as[((ib >> 1) * 2 + (c >> 1)) * 64 + (c & 1) * 32 + (ib & 1) * 16 + r];
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bv[j] = bs[(wn * TN + j) * 64 + tok_slot(r, c)];
+}
+
+__device__ __forceinline__ void mainloop(uint16_t* lds, f32x4 (&acc)[TM][TN], int ksteps, int64_t a_rs,
+                                         const uint16_t* b_src, int ldb, int t0, int T,
+                                         const uint16_t* a_tile, int64_t a_rec, int spp) {
+    // a_rec / spp: when spp > 0 the reduction walks shard records (down
+    // product): step t is local step t % spp of record t / spp.
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = w / WN, wn = w % WN;
+    const bool g1 = w >= NW / 2;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto src = [&](int t) {
+        if (spp > 0) {
+            const int k = t / spp, ls = t - k * spp;
+            return a_tile + (int64_t)k * a_rec + (int64_t)ls * 1024;
+        }
+        return a_tile + (int64_t)t * 1024;
+    };
+    constexpr int AHEAD = NS - 1;
+    const int pro = min(AHEAD, ksteps);
+    for (int t = 0; t < pro; ++t)
+        issue(lds + (t % NS) * STAGE, src(t), a_rs, b_src, ldb, (int64_t)t * 32, t0, T, w, lane);
+    wait_stages(pro - 1);
+    if (g1) stage_barrier();
+    bf16x8 af[TM], bv[TN];
+    for (int t = 0; t < ksteps; ++t) {
+        stage_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + AHEAD < ksteps)
+            issue(lds + ((t + AHEAD) % NS) * STAGE, src(t + AHEAD), a_rs, b_src, ldb,
+                  (int64_t)(t + AHEAD) * 32, t0, T, w, lane);
+        read_frags(lds + (t % NS) * STAGE, af, bv, wm, wn, lane);
+        lgkm_zero();
+        const int newer = min(t + AHEAD, ksteps - 1) - (t + 1);
+        if (g1) wait_stages(newer);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bv[j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!g1) wait_stages(newer);
+    }
+    if (!g1) stage_barrier();
+}
+
+}  // namespace pp16
+
+// 16x16 result layout: lane l holds token l % 16 and features 4 (l / 16) + r.
+template <int ACT>
+__global__ __launch_bounds__(512) void gateup_pp16(Bf16Args a, int n_ft_shard, int n_tt) {
+    using namespace pp16;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
+    int ttile, flin;
+    raster(xcd_remap(blockIdx.x, gridDim.x), a.P * n_ft_shard, n_tt, ttile, flin);
+    const int s = flin / n_ft_shard;
+    const int ftile = flin - s * n_ft_shard;
+    const int64_t a_rs = (int64_t)(a.d >> 4) * 512;
+    const uint16_t* a_tile = a.packed + (int64_t)s * a.shard_elems + (int64_t)(ftile * (BM / 32)) * a_rs;
+    const int t0 = ttile * BN;
+    f32x4 acc[TM][TN];
+    pp16::mainloop(lds, acc, a.d >> 5, a_rs, a.x, a.d, t0, a.T, a_tile, 0, 0);
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w / WN, wn = w % WN;
+    const int fsub = 4 * (lane >> 4);
+    if constexpr (ACT == 1) {
+        // wave rows: 16-row blocks 0, 1 are gate rows of 32-row block 2 wm,
+        // blocks 2, 3 the matching up rows
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int hcol = s * a.F + (ftile * (BM / 64) + wm) * 32 + i * 16 + fsub;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int tok = t0 + (wn * TN + j) * 16 + (lane & 15);
+                if (tok < a.T) {
+                    const f32x4 g = acc[i][j], u = acc[i + 2][j];
+                    *reinterpret_cast<uint2*>(a.h + (int64_t)tok * a.f + hcol) =
+                        pack4_bf16(silu_f(g[0]) * u[0], silu_f(g[1]) * u[1], silu_f(g[2]) * u[2],
+                                   silu_f(g[3]) * u[3]);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int hcol = s * a.F + ftile * BM + (wm * TM + i) * 16 + fsub;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int tok = t0 + (wn * TN + j) * 16 + (lane & 15);
+                if (tok < a.T) {
+                    const f32x4 u = acc[i][j];
+                    *reinterpret_cast<uint2*>(a.h + (int64_t)tok * a.f + hcol) =
+                        pack4_bf16(gelu_tanh_f(u[0]), gelu_tanh_f(u[1]), gelu_tanh_f(u[2]), gelu_tanh_f(u[3]));
+                }
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(512) void down_pp16(Bf16Args a, int n_ft, int n_tt) {
+    using namespace pp16;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
+    int ttile, ftile;
+    raster(xcd_remap(blockIdx.x, gridDim.x), n_ft, n_tt, ttile, ftile);
+    const int spp = a.F >> 5;
+    const int64_t a_rs = (int64_t)(a.F >> 4) * 512;
+    const uint16_t* a_ft = a.packed + a.down_off + (int64_t)(ftile * (BM / 32)) * a_rs;
+    const int t0 = ttile * BN;
+    f32x4 acc[TM][TN];
+    pp16::mainloop(lds, acc, a.P * spp, a_rs, a.h, a.f, t0, a.T, a_ft, a.shard_elems, spp);
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w / WN, wn = w % WN;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int n = ftile * BM + (wm * TM + i) * 16 + 4 * (lane >> 4);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int tok = t0 + (wn * TN + j) * 16 + (lane & 15);
             if (tok < a.T) {
                 const f32x4 v = acc[i][j];
                 *reinterpret_cast<float4*>(a.y + (int64_t)tok * a.d + n) = make_float4(v[0], v[1], v[2], v[3]);
@@ -282,32 +757,39 @@ __global__ __launch_bounds__(WM * WN * 64) void down_tiled(Bf16Args a, int n_ft,
 
 // ------------------------------------------------------------------ configs
 // cfg: 0 = 256 x 256 (8 waves as 4 x 2), 1 = 256 x 128 (8 waves),
-//      2 = 128 x 128 (4 waves as 2 x 2), 3 = 64 x 128 (4 waves as 1 x 4)
+//      2 = 128 x 128 (4 waves as 2 x 2), 3 = 64 x 128 (4 waves as 1 x 4),
+//      4 = 256 x 256 with 4 waves (one per SIMD), 5 = 256 x 256 16x16x32
+//      ping-pong over global-to-LDS loads (the fastest measured at large T)
 struct CfgDesc { int bm, bn; const char* name; };
-static const CfgDesc kCfgs[4] = {
-    {256, 256, "256x256"}, {256, 128, "256x128"}, {128, 128, "128x128"}, {64, 128, "64x128"}};
+constexpr int kNumCfgs = 6;
+static const CfgDesc kCfgs[kNumCfgs] = {
+    {256, 256, "256x256"}, {256, 128, "256x128"}, {128, 128, "128x128"}, {64, 128, "64x128"},
+    {256, 256, "256x256 4-wave"}, {256, 256, "256x256 16x16 ping-pong"}};
 
-const char* tiled_cfg_name(int cfg) { return (cfg >= 0 && cfg < 4) ? kCfgs[cfg].name : "none"; }
+const char* tiled_cfg_name(int cfg) { return (cfg >= 0 && cfg < kNumCfgs) ? kCfgs[cfg].name : "none"; }
 
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool gateup_cfg_fits(int cfg, int d, int F, int swiglu) {
-    if (cfg < 0 || cfg >= 4) return false;
+    if (cfg < 0 || cfg >= kNumCfgs) return false;
     const int64_t ngu = swiglu ? 2LL * F : (int64_t)F;
     return ngu % kCfgs[cfg].bm == 0 && d % 64 == 0;
 }
 
 bool down_cfg_fits(int cfg, int d, int F) {
-    return cfg >= 0 && cfg < 4 && d % kCfgs[cfg].bm == 0 && F % 64 == 0;
+    return cfg >= 0 && cfg < kNumCfgs && d % kCfgs[cfg].bm == 0 && F % 64 == 0;
 }
 
+// Automatic choice: the first shape in kAuto that divides the shard's packed
+// width (gate/up) or d (down) and still gives at least one full wave of
+// workgroups on 256 CUs; otherwise the first one that divides. Shapes 0 and
+// 4 stay reachable through tsp_mlp_set_tiles.
+static const int kAuto[4] = {5, 1, 2, 3};
+
 int choose_gateup_cfg(int T, int d, int F, int P, int swiglu) {
-    // Largest tile that divides the shard's packed width and still gives at
-    // least one full wave of workgroups on 256 CUs; otherwise the largest
-    // that divides.
     const int64_t ngu = swiglu ? 2LL * F : (int64_t)F;
     int fallback = -1;
-    for (int c = 0; c < 4; ++c) {
+    for (int c : kAuto) {
         if (ngu % kCfgs[c].bm || d % 64) continue;
         const int64_t wgs = (int64_t)P * (ngu / kCfgs[c].bm) * cdiv(T, kCfgs[c].bn);
         if (fallback < 0) fallback = c;
@@ -318,7 +800,7 @@ int choose_gateup_cfg(int T, int d, int F, int P, int swiglu) {
 
 int choose_down_cfg(int T, int d, int F) {
     int fallback = -1;
-    for (int c = 0; c < 4; ++c) {
+    for (int c : kAuto) {
         if (d % kCfgs[c].bm || F % 64) continue;
         const int64_t wgs = (d / kCfgs[c].bm) * cdiv(T, kCfgs[c].bn);
         if (fallback < 0) fallback = c;
@@ -355,6 +837,17 @@ hipError_t launch_gateup_tiled(const Bf16Args& a, int cfg, hipStream_t st) {
         case 1: return gateup_go<256, 128, 4, 2>(a, st);
         case 2: return gateup_go<128, 128, 2, 2>(a, st);
         case 3: return gateup_go<64, 128, 1, 4>(a, st);
+        case 4: return gateup_go<256, 256, 2, 2>(a, st);
+        case 5: {
+            const int ngu = a.swiglu ? 2 * a.F : a.F;
+            const int n_ft_shard = ngu / 256, n_tt = (int)cdiv(a.T, 256);
+            const dim3 grid((unsigned)(a.P * n_ft_shard * n_tt));
+            if (a.swiglu)
+                hipLaunchKernelGGL(gateup_pp16<1>, grid, dim3(512), 0, st, a, n_ft_shard, n_tt);
+            else
+                hipLaunchKernelGGL(gateup_pp16<2>, grid, dim3(512), 0, st, a, n_ft_shard, n_tt);
+            return hipGetLastError();
+        }
         default: return hipErrorInvalidValue;
     }
 }
@@ -365,6 +858,12 @@ hipError_t launch_down_tiled(const Bf16Args& a, int cfg, hipStream_t st) {
         case 1: return down_go<256, 128, 4, 2>(a, st);
         case 2: return down_go<128, 128, 2, 2>(a, st);
         case 3: return down_go<64, 128, 1, 4>(a, st);
+        case 4: return down_go<256, 256, 2, 2>(a, st);
+        case 5: {
+            const int n_ft = a.d / 256, n_tt = (int)cdiv(a.T, 256);
+            hipLaunchKernelGGL(down_pp16, dim3((unsigned)(n_ft * n_tt)), dim3(512), 0, st, a, n_ft, n_tt);
+            return hipGetLastError();
+        }
         default: return hipErrorInvalidValue;
     }
 }

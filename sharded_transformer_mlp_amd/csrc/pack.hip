@@ -10,12 +10,12 @@
 // a rank holds at ring step k. The forward kernels then walk records 0..P-1
 // and never look the order up.
 //
-// bf16 record of shard s (all in 16 x 32 fragment blocks, see common.h):
+// bf16 record of shard s (all in 32 x 16 fragment blocks, see common.h):
 //   [gate/up part]  NGU x d, NGU = 2F (SwiGLU, gate and up interleaved in
-//                   groups of 16 features) or F (GeLU: columns of A);
-//                   reduction index = model dim, d / 32 blocks per feature row.
+//                   groups of 32 features) or F (GeLU: columns of A);
+//                   reduction index = model dim, d / 16 blocks per feature row.
 //   [down part]     d x F: feature = output column n of the down matrix,
-//                   reduction index = the shard's local hidden row, F / 32
+//                   reduction index = the shard's local hidden row, F / 16
 //                   blocks per feature row.
 #include "common.h"
 #include "launch.h"
@@ -29,20 +29,20 @@ __global__ void pack_gateup_bf16(const uint16_t* __restrict__ wg, const uint16_t
     const int64_t total = chunks_per_shard;
     const int rec = blockIdx.y;
     const int s = order[rec];
-    const int kblocks = d >> 5;
+    const int kblocks = d >> 4;
     for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
          c += (int64_t)gridDim.x * blockDim.x) {
         const int64_t block = c >> 6;
         const int lane = (int)(c & 63);
         const int64_t nb = block / kblocks;
         const int kb = (int)(block - nb * kblocks);
-        const int64_t j = nb * 16 + (lane & 15);          // packed feature within the shard
-        const int k0 = kb * 32 + (lane >> 4) * 8;
+        const int64_t j = nb * 32 + (lane & 31);          // packed feature within the shard
+        const int k0 = kb * 16 + (lane >> 5) * 8;
         const uint16_t* src;
         int64_t col;
         if (swiglu) {
-            src = ((j & 31) < 16) ? wg : wu;
-            col = (int64_t)s * F + (j >> 5) * 16 + (j & 15);
+            src = ((j & 63) < 32) ? wg : wu;
+            col = (int64_t)s * F + (j >> 6) * 32 + (j & 31);
         } else {
             src = wu;
             col = (int64_t)s * F + j;
@@ -64,15 +64,15 @@ __global__ void pack_down_bf16(const uint16_t* __restrict__ wd, uint16_t* __rest
                                int64_t down_off, int d, int F, int64_t chunks_per_shard) {
     const int rec = blockIdx.y;
     const int s = order[rec];
-    const int kblocks = F >> 5;
+    const int kblocks = F >> 4;
     for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks_per_shard;
          c += (int64_t)gridDim.x * blockDim.x) {
         const int64_t block = c >> 6;
         const int lane = (int)(c & 63);
         const int64_t nb = block / kblocks;
         const int kb = (int)(block - nb * kblocks);
-        const int64_t n = nb * 16 + (lane & 15);          // output feature (column of Wd)
-        const int64_t r0 = (int64_t)s * F + kb * 32 + (lane >> 4) * 8;   // row of Wd
+        const int64_t n = nb * 32 + (lane & 31);          // output feature (column of Wd)
+        const int64_t r0 = (int64_t)s * F + kb * 16 + (lane >> 5) * 8;   // row of Wd
         uint16_t v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = wd[(r0 + e) * d + n];

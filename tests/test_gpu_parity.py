@@ -105,7 +105,7 @@ def test_small_full_parity(name):
     check(w, y, ref(w, inp), name)
 
 
-@pytest.mark.parametrize("gcfg,dcfg", [(0, 0), (1, 1), (2, 2), (3, 3), (0, 3), (3, 0)])
+@pytest.mark.parametrize("gcfg,dcfg", [(0, 0), (1, 1), (2, 2), (3, 3), (4, 4), (5, 5), (0, 3), (3, 0), (4, 0), (5, 1)])
 def test_every_tile_shape(gcfg, dcfg):
     w = Workload("t", T=290, d=512, f=2048, P=2, act="swiglu", dtype="bf16", seed=21, r0=1)
     say(f"[gpu] tile shapes gateup={gcfg} down={dcfg}")
@@ -114,7 +114,7 @@ def test_every_tile_shape(gcfg, dcfg):
     check(w, y, ref(w, inp), f"tiles {gcfg}/{dcfg}")
 
 
-@pytest.mark.parametrize("gcfg", [0, 1, 2])
+@pytest.mark.parametrize("gcfg", [0, 1, 2, 4, 5])
 def test_every_tile_shape_gelu(gcfg):
     w = Workload("t", T=130, d=256, f=1024, P=2, act="gelu_tanh", dtype="bf16", seed=22)
     say(f"[gpu] gelu tile shape {gcfg}")
@@ -123,7 +123,7 @@ def test_every_tile_shape_gelu(gcfg):
     check(w, y, ref(w, inp), f"gelu tiles {gcfg}")
 
 
-@pytest.mark.parametrize("T", [1, 5, 16])
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 32])
 @pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
 def test_skinny_parity(T, act):
     w = Workload("k", T=T, d=1024, f=2048, P=4, act=act, dtype="bf16", seed=31, r0=2)
