@@ -110,6 +110,10 @@ def cpu_baseline(w, inp, budget_s: float):
     while dt < 0.25 * budget_s and n < w.T:
         n = min(w.T, max(n + 1, int(n * min(8.0, 0.6 * budget_s / max(dt, 1e-3)))))
         dt = run(n)
+    reps = 1
+    if n == w.T and dt < 0.5 * budget_s:       # whole workload is quick: repeat it, report the mean
+        reps = max(1, int(0.5 * budget_s / max(dt, 1e-3)))
+        dt = sum(run(n) for _ in range(reps)) / reps
     if w.T <= 64:                               # decode-like: report bytes streamed per second
         value = w.bytes(n) / dt / 1e9
         unit = "GB/s"
@@ -117,7 +121,8 @@ def cpu_baseline(w, inp, budget_s: float):
         value = w.flops(n) / dt / 1e12
         unit = "TFLOP/s"
     return {"value": value, "unit": unit, "cores": cores, "kind": "oracle",
-            "sample": f"first {n} of {w.T} token rows, full weights, fp64 numpy oracle, {dt:.2f} s"}
+            "sample": f"first {n} of {w.T} token rows, full weights, fp64 numpy oracle, "
+                      f"{dt:.2f} s per pass, mean of {reps} pass(es)"}
 
 
 def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):
