@@ -227,7 +227,10 @@ tsp_status_t tsp_mlp_create(tsp_mlp_t* out, int64_t T_max, int64_t d, int64_t f,
         es = 4;
     }
     h->packed_bytes = h->shard_elems * P * es;
+    // hidden activations: T_max x f (tiled and fp32 paths), or f / 16 fragment
+    // blocks of 1 KiB (skinny path); the larger of the two
     h->work_bytes = T_max * f * es;
+    if (dtype == TSP_DTYPE_BF16 && f * 64 > h->work_bytes) h->work_bytes = f * 64;
 
     if ((e = hipMalloc(&h->order_dev, sizeof(int32_t) * (size_t)P)) != hipSuccess ||
         (e = hipMalloc(&h->packed, (size_t)h->packed_bytes)) != hipSuccess ||

@@ -10,11 +10,20 @@
 //   and the hidden columns they produce are both stored in ring order). Its
 //   waves split the model dimension, each keeps fp32 gate and up
 //   accumulators, the partial sums are added in LDS in wave order, and wave
-//   0 applies the activation and writes T tokens x 32 hidden bf16 values.
+//   0 applies the activation and writes the 32 hidden bf16 values of every
+//   token straight into the MFMA token-fragment order the down product
+//   reads (see below).
 // skinny_down: one workgroup per 32 output features. The reduction runs over
 //   all shards in ring order, flattened to one index range that the waves
 //   split into consecutive pieces; the pieces are added in wave order, which
 //   is ring order, and the fp32 result goes straight to Y.
+//
+// Skinny hidden-activation layout (library workspace): for every 16 hidden
+// indices (ring-step order) one 1 KiB fragment block, lane l holding token
+// l % 32 and hidden indices 8 (l / 32) .. + 7; so the down product loads its
+// token operand with one contiguous 16-byte-per-lane access, like a weight
+// block. Slots of tokens >= T are never written; they only feed output
+// columns that are not stored.
 #include "common.h"
 #include "launch.h"
 
@@ -25,7 +34,14 @@ constexpr int SKD_NW = 16;     // waves per down workgroup
 constexpr int SK_U = 4;        // fragment blocks in flight per wave per operand
 
 __device__ __forceinline__ bf16x8 load_frag(const uint16_t* p) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// Weight fragments are read exactly once per forward: nontemporal loads keep
+// them from displacing the tokens / hidden activations in the caches (and
+// stream HBM measurably faster than plain loads on this part).
+__device__ __forceinline__ bf16x8 load_weight_frag(const uint16_t* p) {
+    return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
 }
 
 // Token operand: lane l supplies token l % 32, reduction indices 8 * (l / 32) .. + 7.
@@ -33,7 +49,7 @@ __device__ __forceinline__ bf16x8 token_frag(const uint16_t* __restrict__ src, i
                                              int lane, int T) {
     const int tok = lane & 31;
     if (tok < T) return load_frag(src + (int64_t)tok * ld + koff + (lane >> 5) * 8);
-    return __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
+    return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -67,8 +83,8 @@ __global__ __launch_bounds__(SKG_NW * 64) void skinny_gateup(Bf16Args a) {
         bf16x8 wv[NACC][SK_U], xv[SK_U];
 #pragma unroll
         for (int u = 0; u < SK_U; ++u) {
-            wv[0][u] = load_frag(pg + (int64_t)(kb + u) * 512);
-            if (NACC == 2) wv[NACC - 1][u] = load_frag(pu + (int64_t)(kb + u) * 512);
+            wv[0][u] = load_weight_frag(pg + (int64_t)(kb + u) * 512);
+            if (NACC == 2) wv[NACC - 1][u] = load_weight_frag(pu + (int64_t)(kb + u) * 512);
             xv[u] = token_frag(a.x, a.d, (int64_t)(kb + u) * 16, lane, a.T);
         }
 #pragma unroll
@@ -89,9 +105,12 @@ __global__ __launch_bounds__(SKG_NW * 64) void skinny_gateup(Bf16Args a) {
             for (int i = 1; i < SKG_NW; ++i) sum[c] += red[i][c][lane];
         }
         const f32x16 g = sum[0], u = sum[NACC - 1];
-        const int tok = lane & 31;
+        const int tok = lane & 31, h = lane >> 5;
         if (tok < a.T) {
-            uint16_t* hrow = a.h + (int64_t)tok * a.f + s * a.F + grp * 32 + 4 * (lane >> 5);
+            // this lane holds hidden 8 q + 4 h + r (q, r = 0..3) of the group:
+            // fragment block 2 q' + q / 2 of the group (q' = group), chunk q % 2,
+            // elements 4 h .. 4 h + 3 of that chunk for token tok
+            const int64_t kb_base = ((int64_t)s * a.F + grp * 32) >> 4;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 uint2 v;
@@ -101,7 +120,8 @@ __global__ __launch_bounds__(SKG_NW * 64) void skinny_gateup(Bf16Args a) {
                 else
                     v = pack4_bf16(gelu_tanh_f(g[4 * q]), gelu_tanh_f(g[4 * q + 1]),
                                    gelu_tanh_f(g[4 * q + 2]), gelu_tanh_f(g[4 * q + 3]));
-                *reinterpret_cast<uint2*>(hrow + 8 * q) = v;
+                uint16_t* blk = a.h + (kb_base + (q >> 1)) * 512;
+                *reinterpret_cast<uint2*>(blk + ((q & 1) * 32 + tok) * 8 + 4 * h) = v;
             }
         }
     }
@@ -125,8 +145,8 @@ __global__ __launch_bounds__(SKD_NW * 64) void skinny_down(Bf16Args a) {
         for (int u = 0; u < SK_U; ++u) {
             const int q = kb + u;                       // records and H are in ring order
             const int k = q / kbF, lk = q - k * kbF;
-            wv[u] = load_frag(base + (int64_t)k * a.shard_elems + (int64_t)lk * 512);
-            hv[u] = token_frag(a.h, a.f, (int64_t)q * 16, lane, a.T);
+            wv[u] = load_weight_frag(base + (int64_t)k * a.shard_elems + (int64_t)lk * 512);
+            hv[u] = load_frag(a.h + (int64_t)q * 512 + lane * 8);     // fragment-ordered H
         }
 #pragma unroll
         for (int u = 0; u < SK_U; ++u)
