@@ -135,6 +135,25 @@ def test_skinny_parity(T, act):
     check(w, y2, ref(w, inp), f"tiled T={T}")
 
 
+def test_skinny_smallest_shape_and_limits():
+    """The smallest shape the skinny kernels take (d = 256, P * F = 1024),
+    with several ring orders; a shape they cannot take is rejected, not run."""
+    from sharded_transformer_mlp_amd.binding import TspError
+    for P, r0 in ((2, 1), (4, 3), (8, 5)):
+        w = Workload("m", T=9, d=256, f=1024, P=P, act="swiglu", dtype="bf16", seed=33, r0=r0)
+        say(f"[gpu] skinny d=256 f=1024 P={P}")
+        inp = make_inputs(w)
+        y, _ = run_gpu(w, inp, path="skinny")
+        check(w, y, ref(w, inp), f"skinny P={P}")
+    w = Workload("m", T=9, d=192, f=1024, P=2, act="swiglu", dtype="bf16", seed=33)
+    say("[gpu] skinny unsupported d=192")
+    inp = make_inputs(w)
+    with pytest.raises(TspError):
+        run_gpu(w, inp, path="skinny")
+    y, _ = run_gpu(w, inp)                  # AUTO falls back to the tiled kernels
+    check(w, y, ref(w, inp), "auto d=192")
+
+
 def test_ring_orders():
     """Every rotation and the reversed ring give the oracle's result."""
     w = Workload("r", T=100, d=256, f=1024, P=4, act="swiglu", dtype="bf16", seed=41)
