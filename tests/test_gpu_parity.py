@@ -166,6 +166,32 @@ def test_ring_orders():
         check(w, y, yref, f"order {order}")
 
 
+@pytest.mark.parametrize("n,d,f", [(100, 256, 1024), (16, 1024, 2048)])
+def test_tsp_group_on_one_gpu(n, d, f):
+    """A whole TSP group run rank by rank: rank r holds sequence shard r and
+    starts its ring at weight shard r. The ranks' outputs, concatenated, match
+    the oracle's group simulation and the unsharded block. n = 16 takes the
+    skinny kernels, n = 100 the tiled ones."""
+    P = 4
+    w = Workload("g", T=P * n, d=d, f=f, P=P, act="swiglu", dtype="bf16", seed=46)
+    inp = make_inputs(w)
+    outs = []
+    for r in range(P):
+        say(f"[gpu] TSP group rank {r} of {P}, {n} tokens")
+        order = [(r + k) % P for k in range(P)]
+        shard = Workload("g", T=n, d=d, f=f, P=P, act="swiglu", dtype="bf16", seed=46)
+        from sharded_transformer_mlp_amd.inputs import MLPInputs
+        y, _ = run_gpu(shard, MLPInputs(inp.x[r * n:(r + 1) * n], inp.w_gate, inp.w_up, inp.w_down),
+                       order=order)
+        outs.append(y)
+    y = np.concatenate(outs, axis=0)
+    group = oracle.tsp_simulate(_np(inp.x), _np(inp.w_gate), _np(inp.w_up), _np(inp.w_down), P, "swiglu")
+    check(w, y, group, "TSP group")
+    unsharded = oracle.mlp_forward(_np(inp.x), _np(inp.w_gate), _np(inp.w_up), _np(inp.w_down), 1, [0],
+                                   "swiglu")
+    check(w, y, unsharded, "TSP group vs unsharded")
+
+
 def test_p_independence():
     """The same weights cut into P = 1, 2, 4, 8 shards give the same block."""
     base = Workload("p", T=64, d=256, f=2048, P=1, act="swiglu", dtype="bf16", seed=42)
