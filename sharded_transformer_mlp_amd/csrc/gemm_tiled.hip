@@ -23,11 +23,11 @@
 // fragment blocks, so every operand fragment read is one contiguous (or
 // XOR-swizzled) 16-byte-per-lane access without bank conflicts. The waves
 // run a two-group ping-pong (see mainloop): on every SIMD one wave issues
-// MFMAs while the other moves data. Measured on this part, plain vector
-// loads overlap with MFMA issue on the same SIMD, while global-to-LDS DMA
-// loads (global_load_lds) largely serialise with it; and one wave issuing
-// 32x32x16 MFMAs back to back keeps the matrix pipe busy, which the 16x16x32
-// form does not.
+// MFMAs while the other moves data. Shapes 0-4 use this register-staged
+// loop with 32x32x16 MFMAs; shape 5 (namespace pp16, the automatic choice at
+// large T) loads global memory straight into LDS and uses 16x16x32 MFMAs.
+// The choice between them is empirical: shape 5 measured fastest on every
+// large-T workload.
 #include "common.h"
 #include "launch.h"
 
