@@ -148,6 +148,7 @@ def main():
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the HBM-read and MFMA ceiling probes")
     ap.add_argument("--calibrate-copy", action="store_true", help="only run the copy kernel used to scale counters")
     args = ap.parse_args()
 
@@ -253,6 +254,24 @@ def main():
     mlp.close()
     del x, y
     torch.cuda.empty_cache()
+    if not args.no_ceilings:
+        # Measured ceilings of this GPU beside the datasheet peaks, after the
+        # timed regions so they do not heat the GPU before them.
+        from sharded_transformer_mlp_amd.binding import probe_hbm_read, probe_mfma_bf16
+        log("ceiling probes")
+        # The read rate depends on the buffer size (measured: ~7.0 TB/s at
+        # 1 GiB, 6.8 at 2 GiB, 6.3 at 4 GiB), so the probe reads as many bytes
+        # as the workload's weights, at least 1 GiB (4x the last-level cache).
+        chunk = 64 << 20
+        probe_bytes = max(1 << 30, -(-w.bytes() // chunk) * chunk)
+        ceil = {"hbm_read_GBs": probe_hbm_read(probe_bytes, 10),
+                "mfma_bf16_TFLOPs": probe_mfma_bf16(20000),
+                "how": f"library probes: a {probe_bytes >> 20} MiB buffer read 10x with 16-byte nontemporal "
+                       "loads; 16 independent 16x16x32 bf16 MFMAs per wave, 2 waves per SIMD, "
+                       "pseudo-random operands"}
+        out["ceilings"] = ceil
+        c = ceil["hbm_read_GBs"] if decode else (ceil["mfma_bf16_TFLOPs"] if w.dtype == "bf16" else None)
+        roof["frac_of_measured_ceiling"] = None if c is None else roof["achieved"] / c
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)

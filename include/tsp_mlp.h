@@ -154,6 +154,24 @@ tsp_status_t tsp_mlp_set_timing(tsp_mlp_t h, int32_t enable);
 tsp_status_t tsp_mlp_read_timing(tsp_mlp_t h, int32_t max_kernels, char (*names)[64],
                                  double* total_ms, int64_t* launches, int32_t* n_kernels);
 
+/*
+ * Ceiling probes, for reporting the block's kernels against what this GPU
+ * sustains beside its datasheet peaks. Not part of the forward path. Each
+ * allocates and frees its own device buffers, synchronises `stream` (NULL =
+ * the null stream) and times with HIP events recorded on it.
+ *
+ * tsp_probe_hbm_read: reads a zero-filled device buffer of `bytes` bytes
+ * (64 MiB .. 16 GiB, a multiple of 64 KiB) `reps` times (1 .. 1000) with
+ * 16-byte nontemporal loads; *gb_per_s = bytes * reps / elapsed / 1e9.
+ * tsp_probe_mfma_bf16: every wave issues `iters` (1 .. 1e6) rounds of 16
+ * independent v_mfma_f32_16x16x32_bf16 on pseudo-random unit-scale operands,
+ * enough waves to fill every SIMD twice over; *tflops = flops / elapsed / 1e12.
+ * Errors: TSP_ERR_INVALID_ARG for out-of-range arguments or NULL outputs,
+ * TSP_ERR_OOM if the buffer cannot be allocated, TSP_ERR_HIP otherwise.
+ */
+tsp_status_t tsp_probe_hbm_read(int64_t bytes, int32_t reps, hipStream_t stream, double* gb_per_s);
+tsp_status_t tsp_probe_mfma_bf16(int32_t iters, hipStream_t stream, double* tflops);
+
 /* Static text for a status code. */
 const char* tsp_status_string(tsp_status_t s);
 

@@ -72,6 +72,21 @@ def gelu_tanh(u: np.ndarray) -> np.ndarray:
     return 0.5 * u * (1.0 + np.tanh(SQRT_2_OVER_PI * (u + GELU_TANH_CUBIC * u * u * u)))
 
 
+def round_bf16(a) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps 8 significant bits (the fp32 exponent range). With
+    a = m * 2**e and 0.5 <= |m| < 1, m * 2**8 is rounded to an integer (numpy
+    rounds halves to even) and scaled back; every step but the rounding is an
+    exact power-of-two scaling. Covers the normal range only (no bfloat16
+    subnormals or overflow occur in this block). Diagnostic use: it lets a test
+    give the oracle the same rounding of the hidden activations that the bf16
+    kernels apply before the down product.
+    """
+    m, e = np.frexp(f64(a))
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
+
+
 def ring_order(P: int, r0: int = 0) -> list:
     """Rotated ring order: at step k the rank holds shard (r0 + k) mod P."""
     return [(r0 + k) % P for k in range(P)]
@@ -100,14 +115,21 @@ def shard_hidden(X, w_gate, w_up, s: int, F: int, act: str) -> np.ndarray:
     raise ValueError(f"unknown activation {act!r}")
 
 
-def shard_partial(X, w_gate, w_up, w_down, s: int, F: int, act: str) -> np.ndarray:
-    """Shard s's partial output H_s . W_down[rows of shard s, :] (walk-through steps 4-5)."""
+def shard_partial(X, w_gate, w_up, w_down, s: int, F: int, act: str,
+                  round_h_bf16: bool = False) -> np.ndarray:
+    """Shard s's partial output H_s . W_down[rows of shard s, :] (walk-through steps 4-5).
+
+    ``round_h_bf16`` (diagnostic, never the pass/fail reference) rounds H_s to
+    bfloat16 first, as the bf16 kernels store it.
+    """
     h = shard_hidden(X, w_gate, w_up, s, F, act)
+    if round_h_bf16:
+        h = round_bf16(h)
     return h @ f64(w_down[s * F:(s + 1) * F, :])
 
 
 def mlp_forward(X, w_gate, w_up, w_down, P: int, order: Optional[Sequence[int]] = None,
-                act: str = "swiglu", rows=None) -> np.ndarray:
+                act: str = "swiglu", rows=None, round_h_bf16: bool = False) -> np.ndarray:
     """One rank's TSP gated-MLP forward in float64.
 
     X: T x d; w_gate, w_up: d x f (w_gate None for gelu_tanh, where w_up is the
@@ -116,6 +138,7 @@ def mlp_forward(X, w_gate, w_up, w_down, P: int, order: Optional[Sequence[int]] 
     local fp64 accumulator Y (TSP abstract; walk-through step 6 with the
     all-reduce replaced by this local sum). ``rows`` restricts the token rows
     (rows are independent: the block is applied token by token).
+    ``round_h_bf16`` is the diagnostic form of ``shard_partial``.
     """
     X = f64(X)
     if rows is not None:
@@ -132,7 +155,7 @@ def mlp_forward(X, w_gate, w_up, w_down, P: int, order: Optional[Sequence[int]] 
     order = _check_order(ring_order(P) if order is None else order, P)
     Y = np.zeros((T, d), dtype=np.float64)
     for s in order:
-        Y += shard_partial(X, w_gate, w_up, w_down, s, F, act)
+        Y += shard_partial(X, w_gate, w_up, w_down, s, F, act, round_h_bf16)
     return Y
 
 

@@ -31,6 +31,8 @@ SIGNATURES = {
     "tsp_mlp_set_timing": (_i32, [_vp, _i32]),
     "tsp_mlp_read_timing": (_i32, [_vp, _i32, _vp, ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(_i64), ctypes.POINTER(_i32)]),
+    "tsp_probe_hbm_read": (_i32, [_i64, _i32, _vp, ctypes.POINTER(ctypes.c_double)]),
+    "tsp_probe_mfma_bf16": (_i32, [_i32, _vp, ctypes.POINTER(ctypes.c_double)]),
     "tsp_status_string": (ctypes.c_char_p, [_i32]),
     "tsp_last_error": (ctypes.c_char_p, []),
 }
@@ -86,6 +88,20 @@ def _stream_ptr(stream) -> Optional[int]:
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
+
+
+def probe_hbm_read(nbytes: int = 4 << 30, reps: int = 10, stream=None) -> float:
+    """Sustained HBM read rate in GB/s (nontemporal 16-byte loads)."""
+    out = ctypes.c_double()
+    check(lib().tsp_probe_hbm_read(int(nbytes), int(reps), _stream_ptr(stream), ctypes.byref(out)))
+    return out.value
+
+
+def probe_mfma_bf16(iters: int = 4000, stream=None) -> float:
+    """Sustained bf16 MFMA rate in TFLOP/s (16x16x32, pseudo-random operands)."""
+    out = ctypes.c_double()
+    check(lib().tsp_probe_mfma_bf16(int(iters), _stream_ptr(stream), ctypes.byref(out)))
+    return out.value
 
 
 class TspMLP:

@@ -392,4 +392,78 @@ tsp_status_t tsp_mlp_read_timing(tsp_mlp_t h, int32_t max_kernels, char (*names)
     return TSP_OK;
 }
 
+
+// ---- ceiling probes -------------------------------------------------------
+
+extern "C++" {
+namespace {
+
+// Times `reps` launches of `launch` on `st` with HIP events after one
+// untimed launch; returns milliseconds through *ms.
+template <class Fn>
+tsp_status_t time_probe(hipStream_t st, int reps, Fn&& launch, double* ms) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    hipError_t err = hipEventCreate(&e0);
+    if (err == hipSuccess) err = hipEventCreate(&e1);
+    if (err == hipSuccess) err = launch();
+    if (err == hipSuccess) err = hipEventRecord(e0, st);
+    for (int r = 0; r < reps && err == hipSuccess; ++r) err = launch();
+    if (err == hipSuccess) err = hipEventRecord(e1, st);
+    if (err == hipSuccess) err = hipEventSynchronize(e1);
+    float t = 0.f;
+    if (err == hipSuccess) err = hipEventElapsedTime(&t, e0, e1);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (err != hipSuccess) return hip_fail(err, "probe");
+    *ms = t;
+    return TSP_OK;
+}
+
+}  // namespace
+}  // extern "C++"
+
+tsp_status_t tsp_probe_hbm_read(int64_t bytes, int32_t reps, hipStream_t stream, double* gb_per_s) {
+    if (!gb_per_s) return fail(TSP_ERR_INVALID_ARG, "gb_per_s is NULL");
+    if (bytes < (64LL << 20) || bytes > (16LL << 30) || bytes % (64 << 10))
+        return fail(TSP_ERR_INVALID_ARG, "bytes=%lld: need 64 MiB .. 16 GiB, a multiple of 64 KiB", (long long)bytes);
+    if (reps < 1 || reps > 1000) return fail(TSP_ERR_INVALID_ARG, "reps=%d out of [1, 1000]", reps);
+    void* buf = nullptr;
+    void* sink = nullptr;
+    if (hipMalloc(&buf, (size_t)bytes) != hipSuccess || hipMalloc(&sink, 64) != hipSuccess) {
+        (void)hipGetLastError();
+        if (buf) (void)hipFree(buf);
+        return fail(TSP_ERR_OOM, "probe buffer of %lld bytes", (long long)bytes);
+    }
+    tsp_status_t s = TSP_OK;
+    hipError_t err = hipMemsetAsync(buf, 0, (size_t)bytes, stream);
+    double ms = 0.0;
+    if (err != hipSuccess) s = hip_fail(err, "hipMemsetAsync");
+    else s = time_probe(stream, reps, [&] { return tsp::launch_probe_hbm_read(buf, bytes, sink, stream); }, &ms);
+    (void)hipStreamSynchronize(stream);
+    (void)hipFree(buf);
+    (void)hipFree(sink);
+    if (s != TSP_OK) return s;
+    *gb_per_s = (double)bytes * reps / (ms * 1e-3) / 1e9;
+    return TSP_OK;
+}
+
+tsp_status_t tsp_probe_mfma_bf16(int32_t iters, hipStream_t stream, double* tflops) {
+    if (!tflops) return fail(TSP_ERR_INVALID_ARG, "tflops is NULL");
+    if (iters < 1 || iters > 1000000) return fail(TSP_ERR_INVALID_ARG, "iters=%d out of [1, 1e6]", iters);
+    float* sink = nullptr;
+    const size_t n = (size_t)tsp::probe_mfma_blocks() * tsp::probe_mfma_threads();
+    if (hipMalloc(&sink, n * sizeof(float)) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(TSP_ERR_OOM, "probe sink");
+    }
+    double ms = 0.0;
+    const int reps = 5;
+    tsp_status_t s = time_probe(stream, reps, [&] { return tsp::launch_probe_mfma_bf16(iters, sink, stream); }, &ms);
+    (void)hipStreamSynchronize(stream);
+    (void)hipFree(sink);
+    if (s != TSP_OK) return s;
+    *tflops = tsp::probe_mfma_flops(iters) * reps / (ms * 1e-3) / 1e12;
+    return TSP_OK;
+}
+
 }  // extern "C"

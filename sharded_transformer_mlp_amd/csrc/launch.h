@@ -48,7 +48,7 @@ const char* tiled_cfg_name(int cfg);
 bool gateup_cfg_fits(int cfg, int d, int F, int swiglu);
 bool down_cfg_fits(int cfg, int d, int F);
 
-// Skinny (T <= 16) weight-streaming path.
+// Skinny (T <= 32) weight-streaming path.
 hipError_t launch_gateup_skinny(const Bf16Args& a, hipStream_t st);
 hipError_t launch_down_skinny(const Bf16Args& a, hipStream_t st);
 bool skinny_supported(int d, int F, int P);
@@ -56,5 +56,12 @@ bool skinny_supported(int d, int F, int P);
 // fp32 path.
 hipError_t launch_gateup_f32(const F32Args& a, hipStream_t st);
 hipError_t launch_down_f32(const F32Args& a, hipStream_t st);
+
+// Ceiling probes (measurement only).
+hipError_t launch_probe_hbm_read(const void* buf, int64_t bytes, void* sink, hipStream_t st);
+hipError_t launch_probe_mfma_bf16(int iters, float* sink, hipStream_t st);
+int probe_mfma_blocks();
+int probe_mfma_threads();
+double probe_mfma_flops(int iters);
 
 }  // namespace tsp

@@ -17,7 +17,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "ts
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tsp_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(tsp_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -98,3 +98,15 @@ def test_null_handle_calls():
     assert lib.tsp_mlp_set_timing(None, 1) == INV
     n = ctypes.c_int32()
     assert lib.tsp_mlp_read_timing(None, 0, None, None, None, ctypes.byref(n)) == INV
+
+
+def test_probes_reject_bad_arguments_before_any_hip_call():
+    lib = B.lib()
+    out = ctypes.c_double()
+    assert lib.tsp_probe_hbm_read(1 << 30, 5, None, None) == INV
+    assert lib.tsp_probe_hbm_read(1 << 20, 5, None, ctypes.byref(out)) == INV       # below 64 MiB
+    assert lib.tsp_probe_hbm_read((1 << 30) + 4, 5, None, ctypes.byref(out)) == INV  # not 64 KiB aligned
+    assert lib.tsp_probe_hbm_read(1 << 30, 0, None, ctypes.byref(out)) == INV
+    assert b"reps" in lib.tsp_last_error()
+    assert lib.tsp_probe_mfma_bf16(0, None, ctypes.byref(out)) == INV
+    assert lib.tsp_probe_mfma_bf16(100, None, None) == INV

@@ -217,8 +217,36 @@ def pin_linearity(o):
         assert np.array_equal(Y5, Y[rows])
 
 
+def pin_round_bf16(o):
+    """bfloat16 round-to-nearest-even: representable values stay, halfway
+    cases go to the even neighbour, and fp32 inputs match torch's own
+    fp32 -> bfloat16 conversion (a single rounding there too)."""
+    exact = np.array([0.0, 1.0, -1.5, 3.25, 2.0 ** -100, -(2.0 ** 90), 255.0, 1.0 + 2.0 ** -7])
+    assert np.array_equal(o.round_bf16(exact), exact)
+    # near 1 the bfloat16 spacing is 2^-7
+    ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 2 + 2.0 ** -7, 2 + 3 * 2.0 ** -7])
+    want = np.array([1.0, 1 + 2.0 ** -6, -1.0, 2.0, 2 + 2.0 ** -5])
+    assert np.array_equal(o.round_bf16(ties), want)
+    assert np.array_equal(o.round_bf16(np.array([1 + 2.0 ** -8 + 2.0 ** -30])), np.array([1 + 2.0 ** -7]))
+    import torch
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(20000, generator=g) * torch.exp(torch.randn(20000, generator=g) * 8)
+    ref = x.to(torch.bfloat16).double().numpy()
+    assert np.array_equal(o.round_bf16(x.double().numpy()), ref)
+    # rounding H moves each hidden value by at most 2^-9 of itself
+    T, d, f, P = 5, 16, 32, 4
+    for act in ("swiglu", "gelu_tanh"):
+        X, wg, wu, wd = _rng_inputs(T, d, f, act, 13)
+        Y = o.mlp_forward(X, wg, wu, wd, P, None, act)
+        Yr = o.mlp_forward(X, wg, wu, wd, P, None, act, round_h_bf16=True)
+        H = np.concatenate([o.shard_hidden(X, wg, wu, s, f // P, act) for s in range(P)], axis=1)
+        bound = 2.0 ** -9 * (np.abs(H) @ np.abs(wd)) * (1 + 1e-12)
+        assert np.all(np.abs(Yr - Y) <= bound + 1e-15)
+        assert not np.array_equal(Yr, Y)
+
+
 ALL_PINS = [pin_golden, pin_brute_force, pin_silu, pin_gelu, pin_identity_weights,
-            pin_selection_weights, pin_column_then_row_identity, pin_linearity]
+            pin_selection_weights, pin_column_then_row_identity, pin_linearity, pin_round_bf16]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -295,14 +323,14 @@ def _mut_swap_gate_up(X, w_gate, w_up, s, F, act):
     return _orig_shard_hidden(X, w_up, w_gate, s, F, act)
 
 
-def _mut_wrong_down_rows(X, w_gate, w_up, w_down, s, F, act):
+def _mut_wrong_down_rows(X, w_gate, w_up, w_down, s, F, act, round_h_bf16=False):
     P = w_down.shape[0] // F
     h = O.shard_hidden(X, w_gate, w_up, s, F, act)
     s2 = (s + 1) % P
     return h @ O.f64(w_down[s2 * F:(s2 + 1) * F, :])
 
 
-def _mut_drop_last_shard(X, w_gate, w_up, w_down, P, order=None, act="swiglu", rows=None):
+def _mut_drop_last_shard(X, w_gate, w_up, w_down, P, order=None, act="swiglu", rows=None, round_h_bf16=False):
     X = O.f64(X) if rows is None else O.f64(X)[np.asarray(rows)]
     F = w_up.shape[1] // P
     order = O.ring_order(P) if order is None else list(order)
@@ -312,7 +340,7 @@ def _mut_drop_last_shard(X, w_gate, w_up, w_down, P, order=None, act="swiglu", r
     return Y
 
 
-def _mut_down_transposed(X, w_gate, w_up, w_down, s, F, act):
+def _mut_down_transposed(X, w_gate, w_up, w_down, s, F, act, round_h_bf16=False):
     h = O.shard_hidden(X, w_gate, w_up, s, F, act)
     wt = O.f64(w_down).T if w_down.shape[0] == w_down.shape[1] else O.f64(w_down)
     return h @ wt[s * F:(s + 1) * F, :]
