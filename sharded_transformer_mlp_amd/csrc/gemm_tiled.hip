@@ -578,11 +578,19 @@ constexpr int LOADS = (A_BLK + B_BLK) / NW;
 constexpr int STAGE = (A_BLK + B_BLK) * 512;
 constexpr int NS = 4;
 
+// LDS slot of token r's 8-index chunk c in a B block. The 16x16x32 B
+// fragment read has lane l take token l % 16, chunk l / 16; with this XOR
+// (on r / 2) that read runs without LDS bank conflicts (measured with
+// SQ_LDS_BANK_CONFLICT; the tok_slot swizzle on r / 4 that suits the
+// 32x32x16 read costs this one a 2-way conflict). Each group of 4 lanes
+// still loads the 64 contiguous bytes of one token row.
+__device__ __forceinline__ int b_slot(int r, int c) { return 4 * r + (c ^ ((r >> 1) & 3)); }
+
 __device__ __forceinline__ void issue(uint16_t* lds_stage, const uint16_t* __restrict__ a_base, int64_t a_rs,
                                       const uint16_t* __restrict__ b_src, int ldb, int64_t b_koff, int t0,
                                       int T, int w, int lane) {
     const int r = lane >> 2;                            // token inside a B block
-    const int c = (lane & 3) ^ ((r >> 2) & 3);          // chunk this lane fetches (slot = lane)
+    const int c = (lane & 3) ^ ((r >> 1) & 3);          // chunk this lane fetches (slot = lane = b_slot(r, c))
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
         const int b = i * NW + w;                       // wave-uniform block id
@@ -617,7 +625,7 @@ __device__ __forceinline__ void read_frags(const uint16_t* lds_stage, bf16x8 (&a
         af[i] = as[((ib >> 1) * 2 + (c >> 1)) * 64 + (c & 1) * 32 + (ib & 1) * 16 + r];
     }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bv[j] = bs[(wn * TN + j) * 64 + tok_slot(r, c)];
+    for (int j = 0; j < TN; ++j) bv[j] = bs[(wn * TN + j) * 64 + b_slot(r, c)];
 }
 
 __device__ __forceinline__ void mainloop(uint16_t* lds, f32x4 (&acc)[TM][TN], int ksteps, int64_t a_rs,
