@@ -41,6 +41,7 @@ KERNEL_SOURCES = {
     "skinny_down": ["gemm_skinny.hip", "common.h"],
     "gateup_f32": ["gemm_f32.hip", "common.h"],
     "down_f32": ["gemm_f32.hip", "common.h"],
+    "reduce_partials": ["gemm_tiled.hip", "common.h"],
 }
 
 
@@ -63,6 +64,10 @@ def kernel_work(w, kernel: str, T: int):
     if kernel in ("gateup_tiled", "skinny_gateup", "gateup_f32"):
         flops = 2 * T * w.d * w.f * n_gu
         byts = n_gu * w.d * w.f * es + T * w.d * es + T * w.f * es      # W_gu, X, H out
+    elif kernel == "reduce_partials":
+        # adds the ring-group partials of a split down product into Y; its only
+        # algorithmic traffic is the Y write (the partials are implementation)
+        flops, byts = 0, T * w.d * 4
     else:
         flops = 2 * T * w.f * w.d
         byts = w.f * w.d * es + T * w.f * es + T * w.d * 4                 # W_d, H in, Y out

@@ -59,6 +59,7 @@ struct tsp_mlp {
     int64_t packed_bytes = 0, shard_elems = 0, down_off = 0;
     void* work = nullptr;
     int64_t work_bytes = 0;
+    int64_t part_off = 0;                      // byte offset of the down-split partials in work
     int32_t path = TSP_PATH_AUTO;
     int32_t cfg_gateup = -1, cfg_down = -1;   // tiled shapes; -1 = chosen per forward
     // kernel timing
@@ -229,8 +230,15 @@ tsp_status_t tsp_mlp_create(tsp_mlp_t* out, int64_t T_max, int64_t d, int64_t f,
     h->packed_bytes = h->shard_elems * P * es;
     // hidden activations: T_max x f (tiled and fp32 paths), or f / 16 fragment
     // blocks of 1 KiB (skinny path); the larger of the two
+    // workspace: hidden activations (tiled: T_max x f; skinny: 32-token
+    // fragment blocks, f * 32 elements), then for bf16 the fp32 partials of a
+    // ring-group split of the down product (at most 64 MiB, see
+    // down_split_bytes)
     h->work_bytes = T_max * f * es;
     if (dtype == TSP_DTYPE_BF16 && f * 64 > h->work_bytes) h->work_bytes = f * 64;
+    h->work_bytes = (h->work_bytes + 255) / 256 * 256;
+    h->part_off = h->work_bytes;
+    if (dtype == TSP_DTYPE_BF16) h->work_bytes += tsp::down_split_bytes(T_max, (int)d, P);
 
     if ((e = hipMalloc(&h->order_dev, sizeof(int32_t) * (size_t)P)) != hipSuccess ||
         (e = hipMalloc(&h->packed, (size_t)h->packed_bytes)) != hipSuccess ||
@@ -279,6 +287,7 @@ tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y, hi
         a.x = static_cast<const uint16_t*>(X);
         a.h = static_cast<uint16_t*>(h->work);
         a.y = Y;
+        a.part = reinterpret_cast<float*>(static_cast<char*>(h->work) + h->part_off);
         a.shard_elems = h->shard_elems;
         a.down_off = h->down_off;
         a.T = (int)T; a.d = (int)h->d; a.f = (int)h->f; a.F = (int)h->F; a.P = h->P;
@@ -286,7 +295,7 @@ tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y, hi
         const bool sk_ok = T <= 32 && tsp::skinny_supported(a.d, a.F, a.P);
         bool skinny = false;
         if (h->path == TSP_PATH_SKINNY) {
-            if (!sk_ok) return fail(TSP_ERR_UNSUPPORTED, "skinny path needs T <= 32, d %% 512 == 0 and P*F %% 1024 == 0");
+            if (!sk_ok) return fail(TSP_ERR_UNSUPPORTED, "skinny path needs T <= 32, d %% 256 == 0 and P*F %% 1024 == 0");
             skinny = true;
         } else if (h->path == TSP_PATH_AUTO) {
             skinny = sk_ok;
@@ -297,14 +306,20 @@ tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y, hi
             return timed_launch(h, "skinny_down", st, [&] { return tsp::launch_down_skinny(a, st); });
         }
         const int cg = h->cfg_gateup >= 0 ? h->cfg_gateup : tsp::choose_gateup_cfg(a.T, a.d, a.F, a.P, a.swiglu);
-        const int cd = h->cfg_down >= 0 ? h->cfg_down : tsp::choose_down_cfg(a.T, a.d, a.F);
+        const int cd = h->cfg_down >= 0 ? h->cfg_down : tsp::choose_down_cfg(a.T, a.d, a.F, a.P);
+        const int split = tsp::choose_down_split(a.T, a.d, a.P, cd);
+        if (split > 1 && (int64_t)split * T * a.d * 4 > h->work_bytes - h->part_off)
+            return fail(TSP_ERR_HIP, "internal: split partials exceed the workspace");
         const int64_t n_tok_tiles = (T + 63) / 64;
         if (n_tok_tiles * (int64_t)(2 * a.f / 64 + a.d / 64) > INT32_MAX / 2)
             return fail(TSP_ERR_UNSUPPORTED, "grid too large");
         if (cg < 0 || cd < 0) return fail(TSP_ERR_UNSUPPORTED, "no tile shape fits d=%d F=%d", a.d, a.F);
         s = timed_launch(h, "gateup_tiled", st, [&] { return tsp::launch_gateup_tiled(a, cg, st); });
         if (s != TSP_OK) return s;
-        return timed_launch(h, "down_tiled", st, [&] { return tsp::launch_down_tiled(a, cd, st); });
+        s = timed_launch(h, "down_tiled", st, [&] { return tsp::launch_down_tiled(a, cd, split, st); });
+        if (s != TSP_OK || split == 1) return s;
+        return timed_launch(h, "reduce_partials", st,
+                            [&] { return tsp::launch_reduce_partials(a.part, split, T * a.d, Y, st); });
     }
     if (h->path == TSP_PATH_SKINNY) return fail(TSP_ERR_UNSUPPORTED, "skinny path is bf16 only");
     tsp::F32Args a;

@@ -735,17 +735,27 @@ __global__ __launch_bounds__(512) void gateup_pp16(Bf16Args a, int n_ft_shard, i
     }
 }
 
-__global__ __launch_bounds__(512) void down_pp16(Bf16Args a, int n_ft, int n_tt) {
+// split > 1: workgroup group g (of `split`) sums ring steps
+// [g * P / split, (g + 1) * P / split) into its own fp32 partial; records and
+// H columns are in ring order, so a group is a contiguous range of both.
+__global__ __launch_bounds__(512) void down_pp16(Bf16Args a, int n_ft, int n_tt, int split) {
     using namespace pp16;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
+    const int n_tiles = n_ft * n_tt;
+    const int lin = xcd_remap(blockIdx.x, gridDim.x);
+    const int g = lin / n_tiles;                        // ring-step group
     int ttile, ftile;
-    raster(xcd_remap(blockIdx.x, gridDim.x), n_ft, n_tt, ttile, ftile);
+    raster(lin - g * n_tiles, n_ft, n_tt, ttile, ftile);
     const int spp = a.F >> 5;
+    const int steps_per_group = a.P / split;
     const int64_t a_rs = (int64_t)(a.F >> 4) * 512;
-    const uint16_t* a_ft = a.packed + a.down_off + (int64_t)(ftile * (BM / 32)) * a_rs;
+    const uint16_t* a_ft = a.packed + a.down_off + (int64_t)(g * steps_per_group) * a.shard_elems +
+                           (int64_t)(ftile * (BM / 32)) * a_rs;
+    const uint16_t* h_g = a.h + (int64_t)(g * steps_per_group) * a.F;
+    float* y = split > 1 ? a.part + (int64_t)g * a.T * a.d : a.y;
     const int t0 = ttile * BN;
     f32x4 acc[TM][TN];
-    pp16::mainloop(lds, acc, a.P * spp, a_rs, a.h, a.f, t0, a.T, a_ft, a.shard_elems, spp);
+    pp16::mainloop(lds, acc, steps_per_group * spp, a_rs, h_g, a.f, t0, a.T, a_ft, a.shard_elems, spp);
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w / WN, wn = w % WN;
@@ -757,9 +767,22 @@ __global__ __launch_bounds__(512) void down_pp16(Bf16Args a, int n_ft, int n_tt)
             const int tok = t0 + (wn * TN + j) * 16 + (lane & 15);
             if (tok < a.T) {
                 const f32x4 v = acc[i][j];
-                *reinterpret_cast<float4*>(a.y + (int64_t)tok * a.d + n) = make_float4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<float4*>(y + (int64_t)tok * a.d + n) = make_float4(v[0], v[1], v[2], v[3]);
             }
         }
+    }
+}
+
+// Y = sum of the `split` partials, added in ring order (group 0 first).
+__global__ __launch_bounds__(256) void reduce_partials(const float4* __restrict__ part, int split, int64_t n4,
+                                                       float4* __restrict__ y) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+        float4 s = part[i];
+        for (int g = 1; g < split; ++g) {
+            const float4 v = part[(int64_t)g * n4 + i];
+            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+        }
+        y[i] = s;
     }
 }
 
@@ -806,11 +829,30 @@ int choose_gateup_cfg(int T, int d, int F, int P, int swiglu) {
     return fallback;
 }
 
-int choose_down_cfg(int T, int d, int F) {
+int choose_down_split(int T, int d, int P, int cfg) {
+    if (cfg != 5 || d % 256) return 1;
+    const int64_t tiles = (int64_t)(d / 256) * cdiv(T, 256);
+    int best = 1;
+    for (int s = 2; s <= P; ++s)                        // the largest divisor of P that keeps one round
+        if (P % s == 0 && tiles * s <= 256) best = s;
+    return best;
+}
+
+int64_t down_split_bytes(int64_t T_max, int d, int P) {
+    int64_t most = 0;
+    for (int64_t t = 256; t < T_max + 256; t += 256) {
+        const int64_t T = t < T_max ? t : T_max;
+        const int s = choose_down_split((int)T, d, P, 5);
+        if (s > 1 && s * T * d * 4 > most) most = s * T * d * 4;
+    }
+    return most;
+}
+
+int choose_down_cfg(int T, int d, int F, int P) {
     int fallback = -1;
     for (int c : kAuto) {
         if (d % kCfgs[c].bm || F % 64) continue;
-        const int64_t wgs = (d / kCfgs[c].bm) * cdiv(T, kCfgs[c].bn);
+        const int64_t wgs = (d / kCfgs[c].bm) * cdiv(T, kCfgs[c].bn) * choose_down_split(T, d, P, c);
         if (fallback < 0) fallback = c;
         if (wgs >= 256) return c;
     }
@@ -860,7 +902,8 @@ hipError_t launch_gateup_tiled(const Bf16Args& a, int cfg, hipStream_t st) {
     }
 }
 
-hipError_t launch_down_tiled(const Bf16Args& a, int cfg, hipStream_t st) {
+hipError_t launch_down_tiled(const Bf16Args& a, int cfg, int split, hipStream_t st) {
+    if (split > 1 && (cfg != 5 || a.P % split || !a.part)) return hipErrorInvalidValue;
     switch (cfg) {
         case 0: return down_go<256, 256, 4, 2>(a, st);
         case 1: return down_go<256, 128, 4, 2>(a, st);
@@ -869,11 +912,20 @@ hipError_t launch_down_tiled(const Bf16Args& a, int cfg, hipStream_t st) {
         case 4: return down_go<256, 256, 2, 2>(a, st);
         case 5: {
             const int n_ft = a.d / 256, n_tt = (int)cdiv(a.T, 256);
-            hipLaunchKernelGGL(down_pp16, dim3((unsigned)(n_ft * n_tt)), dim3(512), 0, st, a, n_ft, n_tt);
+            hipLaunchKernelGGL(down_pp16, dim3((unsigned)(n_ft * n_tt * split)), dim3(512), 0, st, a, n_ft, n_tt,
+                               split);
             return hipGetLastError();
         }
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_reduce_partials(const float* part, int split, int64_t n, float* y, hipStream_t st) {
+    const int64_t n4 = n / 4;                           // n = T * d, d a multiple of 64
+    const int64_t blocks = std::min<int64_t>(cdiv(n4, 256), 4096);
+    hipLaunchKernelGGL(reduce_partials, dim3((unsigned)blocks), dim3(256), 0, st,
+                       reinterpret_cast<const float4*>(part), split, n4, reinterpret_cast<float4*>(y));
+    return hipGetLastError();
 }
 
 }  // namespace tsp

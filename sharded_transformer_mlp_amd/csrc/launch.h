@@ -14,6 +14,7 @@ struct Bf16Args {
     const uint16_t* x;        // T x d tokens
     uint16_t* h;              // T x f hidden activations (workspace), columns in ring-step order
     float* y;                 // T x d output
+    float* part;              // split-reduction partials, split x T x d fp32 (workspace; may be null)
     int64_t shard_elems;      // elements per shard record (records in ring order)
     int64_t down_off;         // offset of the down part inside a record
     int T, d, f, F, P;
@@ -40,10 +41,18 @@ hipError_t launch_pack_f32(const void* wg, const void* wu, const void* wd, void*
 
 // Tiled MFMA path. Each returns the launch status; `cfg` picks a tile shape.
 hipError_t launch_gateup_tiled(const Bf16Args& a, int cfg, hipStream_t st);
-hipError_t launch_down_tiled(const Bf16Args& a, int cfg, hipStream_t st);
+// split > 1 (shape 5 only): the ring is cut into `split` groups of
+// consecutive ring steps, each group's sum goes to its own fp32 partial in
+// a.part, and launch_reduce_partials adds the partials in ring order into Y.
+hipError_t launch_down_tiled(const Bf16Args& a, int cfg, int split, hipStream_t st);
+hipError_t launch_reduce_partials(const float* part, int split, int64_t n, float* y, hipStream_t st);
+// Number of ring-step groups for the down product at this shape (1 = none).
+int choose_down_split(int T, int d, int P, int cfg);
+// Bytes of partials the largest split needs for any T <= T_max.
+int64_t down_split_bytes(int64_t T_max, int d, int P);
 // Tile-shape choice for a shape (host logic; -1 = none fits).
 int choose_gateup_cfg(int T, int d, int F, int P, int swiglu);
-int choose_down_cfg(int T, int d, int F);
+int choose_down_cfg(int T, int d, int F, int P);
 const char* tiled_cfg_name(int cfg);
 bool gateup_cfg_fits(int cfg, int d, int F, int swiglu);
 bool down_cfg_fits(int cfg, int d, int F);

@@ -193,6 +193,23 @@ def test_skinny_smallest_shape_and_limits():
     check(w, y, ref(w, inp), "auto d=192")
 
 
+@pytest.mark.parametrize("T,d,f,P,r0", [(100, 1024, 4096, 4, 1), (300, 512, 4096, 8, 5), (513, 2048, 2048, 2, 1)])
+def test_down_ring_group_split(T, d, f, P, r0):
+    """Few output tiles: the down product is cut into groups of consecutive
+    ring steps, each summed into its own fp32 partial, and the partials are
+    added in ring order. Checked against the oracle, for bitwise
+    reproducibility, and against the unsplit 256 x 128 tile shape."""
+    w = Workload("q", T=T, d=d, f=f, P=P, act="swiglu", dtype="bf16", seed=48, r0=r0)
+    say(f"[gpu] down split T={T} d={d} f={f} P={P}")
+    inp = make_inputs(w)
+    y, mlp = run_gpu(w, inp)
+    check(w, y, ref(w, inp), "split")
+    y2, _ = run_gpu(w, inp, reuse=mlp)
+    assert np.array_equal(y, y2)
+    y3, _ = run_gpu(w, inp, path="tiled", tiles=(5, 1))
+    check(w, y3, ref(w, inp), "unsplit")
+
+
 def test_ring_orders():
     """Every rotation and the reversed ring give the oracle's result."""
     w = Workload("r", T=100, d=256, f=1024, P=4, act="swiglu", dtype="bf16", seed=41)
