@@ -251,6 +251,9 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "P": w.P, "act": w.act,
                    "ring_order": w.order(), "parallelism": "one TSP rank (shard loop on one GPU)"},
         "pct_of_peak": (value / (PEAK_HBM_GBS if decode else roof["peak"])) * 100.0,
+        "env": {"gpu": torch.cuda.get_device_name(0),
+                "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
+                "torch": torch.__version__, "hip": torch.version.hip},
         "kernels_ms": kernels,
         "pack_ms": pack_ms,
         "roofline": roof,

@@ -18,6 +18,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtsp_mlp.so")
+# Same sources with TSP_LDS_POISON: every kernel fills its LDS with NaN
+# before first use (tests run parity cases on it to catch missing waits).
+DEBUG_LIB = os.path.join(PKG, "libtsp_mlp_lds_poison.so")
 ARCH = "gfx950"
 
 # Packed-fp32 VALU ops are disabled for every device pass.
@@ -39,9 +42,9 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPFLAGS, "-c", src, "-o", obj]
+def _compile(src: str, tag: str = "", defs=()) -> str:
+    obj = os.path.join(OBJ, os.path.basename(src) + tag + ".o")
+    cmd = [hipcc(), *HIPFLAGS, *defs, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
@@ -52,20 +55,28 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(OBJ, exist_ok=True)
-    srcs = sources()
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every source and link the shared library (and its LDS-poison
+    debug twin); returns the library's path."""
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = sources()
+    with ThreadPoolExecutor(max_workers=min(8, 2 * len(srcs))) as ex:
+        objs = ex.map(_compile, srcs)
+        dbg = ex.map(lambda s: _compile(s, ".poison", ("-DTSP_LDS_POISON=1",)), srcs)
+        objs, dbg = list(objs), list(dbg)
+    _link(objs, LIB)
+    _link(dbg, DEBUG_LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+        print(f"built {LIB} and {os.path.basename(DEBUG_LIB)} from {len(srcs)} sources")
     return LIB
 
 

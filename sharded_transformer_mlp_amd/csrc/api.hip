@@ -228,12 +228,10 @@ tsp_status_t tsp_mlp_create(tsp_mlp_t* out, int64_t T_max, int64_t d, int64_t f,
         es = 4;
     }
     h->packed_bytes = h->shard_elems * P * es;
-    // hidden activations: T_max x f (tiled and fp32 paths), or f / 16 fragment
-    // blocks of 1 KiB (skinny path); the larger of the two
-    // workspace: hidden activations (tiled: T_max x f; skinny: 32-token
-    // fragment blocks, f * 32 elements), then for bf16 the fp32 partials of a
-    // ring-group split of the down product (at most 64 MiB, see
-    // down_split_bytes)
+    // workspace: hidden activations (tiled and fp32 paths: T_max x f; skinny:
+    // f / 16 fragment blocks of 1 KiB; the larger of the two), then for bf16
+    // the fp32 partials of a ring-group split of the down product (at most
+    // 64 MiB, see down_split_bytes)
     h->work_bytes = T_max * f * es;
     if (dtype == TSP_DTYPE_BF16 && f * 64 > h->work_bytes) h->work_bytes = f * 64;
     h->work_bytes = (h->work_bytes + 255) / 256 * 256;

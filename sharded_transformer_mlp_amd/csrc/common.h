@@ -68,4 +68,22 @@ __device__ inline uint2 pack4_bf16(float a, float b, float c, float d) {
     return r;
 }
 
+// Debug builds (TSP_LDS_POISON) fill a kernel's LDS with NaN bit patterns
+// (0x7FC0 in every 16-bit half: a bf16 NaN, and an fp32 NaN per word)
+// before first use, so a fragment read that runs ahead of the data it waits
+// for turns the output into NaN instead of reusing stale values.
+__device__ inline void poison_lds(void* p, int bytes) {
+#if TSP_LDS_POISON
+    u32x4* q = static_cast<u32x4*>(p);
+    const u32x4 nan4 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+    const int n = bytes / 16;
+    const int nt = blockDim.x * blockDim.y * blockDim.z;
+    for (int i = threadIdx.x; i < n; i += nt) q[i] = nan4;
+    __syncthreads();
+#else
+    (void)p;
+    (void)bytes;
+#endif
+}
+
 }  // namespace tsp

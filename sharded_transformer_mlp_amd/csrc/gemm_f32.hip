@@ -19,6 +19,9 @@ __global__ __launch_bounds__(256) void gateup_f32(F32Args a) {
     __shared__ float xs[FT][FT + 1];
     __shared__ float gs[FT][FT + 1];
     __shared__ float us[FT][FT + 1];
+    poison_lds(xs, sizeof(xs));
+    poison_lds(gs, sizeof(gs));
+    poison_lds(us, sizeof(us));
     const int s = blockIdx.z;                            // ring step = packed record
     const int c0 = blockIdx.x * FT;                      // local hidden column
     const int t0 = blockIdx.y * FT;
@@ -69,6 +72,8 @@ __global__ __launch_bounds__(256) void gateup_f32(F32Args a) {
 __global__ __launch_bounds__(256) void down_f32(F32Args a) {
     __shared__ float hs[FT][FT + 1];
     __shared__ float ds[FT][FT + 1];
+    poison_lds(hs, sizeof(hs));
+    poison_lds(ds, sizeof(ds));
     const int n0 = blockIdx.x * FT;
     const int t0 = blockIdx.y * FT;
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;

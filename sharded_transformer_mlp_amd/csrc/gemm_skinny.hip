@@ -69,6 +69,7 @@ __global__ __launch_bounds__(SKG_NW * 64) void skinny_gateup(Bf16Args a) {
     constexpr int NACC = ACT == 1 ? 2 : 1;              // gate and up, or A only
     constexpr int NR = SK_G * NACC;                     // 32-feature block rows per workgroup
     __shared__ f32x16 red[SKG_NW][NR][64];
+    poison_lds(red, sizeof(red));
     const int wg_per_shard = (a.F >> 5) / SK_G;
     const int s = blockIdx.x / wg_per_shard;            // ring step = packed record
     const int grp0 = (blockIdx.x - s * wg_per_shard) * SK_G;
@@ -132,6 +133,7 @@ __global__ __launch_bounds__(SKG_NW * 64) void skinny_gateup(Bf16Args a) {
 
 __global__ __launch_bounds__(SKD_NW * 64) void skinny_down(Bf16Args a) {
     __shared__ f32x16 red[SKD_NW][64];
+    poison_lds(red, sizeof(red));
     const int nb = blockIdx.x;                          // 32 output features
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int kbF = a.F >> 4;                           // fragment blocks per shard

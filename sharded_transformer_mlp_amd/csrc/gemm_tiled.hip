@@ -459,6 +459,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
     using C = TileCfg<BM, BN, WM, WN>;
     static_assert(ACT != 1 || C::TM % 2 == 0, "SwiGLU pairs gate and up blocks inside a wave");
     __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
+    poison_lds(lds, sizeof(lds));
 
     int ttile, flin;
     raster(xcd_remap(blockIdx.x, gridDim.x), a.P * n_ft_shard, n_tt, ttile, flin);
@@ -522,6 +523,7 @@ template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void down_tiled(Bf16Args a, int n_ft, int n_tt) {
     using C = TileCfg<BM, BN, WM, WN>;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[C::NS * C::STAGE];
+    poison_lds(lds, sizeof(lds));
 
     int ttile, ftile;
     raster(xcd_remap(blockIdx.x, gridDim.x), n_ft, n_tt, ttile, ftile);
@@ -688,6 +690,7 @@ template <int ACT>
 __global__ __launch_bounds__(512) void gateup_pp16(Bf16Args a, int n_ft_shard, int n_tt) {
     using namespace pp16;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
+    poison_lds(lds, sizeof(lds));
     int ttile, flin;
     raster(xcd_remap(blockIdx.x, gridDim.x), a.P * n_ft_shard, n_tt, ttile, flin);
     const int s = flin / n_ft_shard;
@@ -741,6 +744,7 @@ __global__ __launch_bounds__(512) void gateup_pp16(Bf16Args a, int n_ft_shard, i
 __global__ __launch_bounds__(512) void down_pp16(Bf16Args a, int n_ft, int n_tt, int split) {
     using namespace pp16;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
+    poison_lds(lds, sizeof(lds));
     const int n_tiles = n_ft * n_tt;
     const int lin = xcd_remap(blockIdx.x, gridDim.x);
     const int g = lin / n_tiles;                        // ring-step group

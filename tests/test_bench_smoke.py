@@ -1,0 +1,40 @@
+"""bench.py on every workload with a few steps: one JSON line with the
+contract's fields and a roofline object for the dominant kernel."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0 and "one GPU" in r.stderr
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("wl", ["tiny", "gelu", "llama8b", "decode70b", "long70b"])
+def test_bench_emits_the_contract_line(wl):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print(f"[gpu] bench {wl}", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", wl, "--steps", "2",
+                        "--warmup", "1", "--no-cpu-baseline", "--no-ceilings"],
+                       capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+              "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert k in d, k
+    assert d["n_gpus"] == 1 and d["steps"] == 2 and d["warmup"] == 1 and d["value"] > 0
+    roof = d["roofline"]
+    for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert k in roof, k
+    assert 0 < roof["frac"] < 1

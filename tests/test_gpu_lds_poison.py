@@ -1,0 +1,75 @@
+"""Parity on the LDS-poison debug build (libtsp_mlp_lds_poison.so): every
+kernel fills its LDS with NaN before first use, so a fragment read that ran
+ahead of its data (a missing wait or barrier in a staging ring) shows up as
+NaN in Y. Same cases and bars as the main parity tests, fewer of them."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sharded_transformer_mlp_amd import binding
+from sharded_transformer_mlp_amd.inputs import Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEBUG_LIB = os.path.join(os.path.dirname(binding.LIB_PATH), "libtsp_mlp_lds_poison.so")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def poison_library():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if not os.path.exists(DEBUG_LIB):
+        raise RuntimeError(f"{DEBUG_LIB} is missing: build with `python -m sharded_transformer_mlp_amd.build`")
+    saved = (binding._lib, binding.LIB_PATH)
+    binding._lib, binding.LIB_PATH = None, DEBUG_LIB
+    yield
+    binding._lib, binding.LIB_PATH = saved
+
+
+CASES = [
+    ("tiled shape 5 + split", Workload("a", T=300, d=512, f=2048, P=4, act="swiglu", dtype="bf16", seed=11, r0=1),
+     "tiled", None),
+    ("tiled shape 5, 4 tiles", Workload("b", T=513, d=1024, f=4096, P=2, act="swiglu", dtype="bf16", seed=12),
+     "tiled", (5, 5)),
+    ("tiled shape 0", Workload("c", T=290, d=512, f=2048, P=2, act="swiglu", dtype="bf16", seed=21), "tiled", (0, 0)),
+    ("tiled shape 4", Workload("c", T=290, d=512, f=2048, P=2, act="swiglu", dtype="bf16", seed=21), "tiled", (4, 4)),
+    ("tiled gelu shape 1/3", Workload("g", T=200, d=256, f=1024, P=2, act="gelu_tanh", dtype="bf16", seed=12),
+     "tiled", (1, 3)),
+    ("skinny", Workload("k", T=17, d=1024, f=2048, P=4, act="swiglu", dtype="bf16", seed=31, r0=2), "skinny", None),
+    ("fp32", Workload("f", T=70, d=96, f=200, P=4, act="swiglu", dtype="f32", seed=14, r0=3), "auto", None),
+]
+
+
+@pytest.mark.parametrize("name,w,path,tiles", CASES, ids=[c[0] for c in CASES])
+def test_parity_with_poisoned_lds(name, w, path, tiles):
+    assert binding.LIB_PATH == DEBUG_LIB
+    say(f"[gpu] LDS poison: {name}")
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    mlp = binding.TspMLP(None if inp.w_gate is None else inp.w_gate.to(dev), inp.w_up.to(dev),
+                         inp.w_down.to(dev), w.P, order=w.order(), act=w.act, T_max=w.T)
+    mlp.set_path(path)
+    if tiles is not None:
+        mlp.set_tiles(*tiles)
+    y = mlp.forward(inp.x.to(dev))
+    torch.cuda.synchronize()
+    mlp.close()
+    y = y.cpu().double().numpy()
+    assert np.isfinite(y).all(), f"{name}: NaN in Y (a read ran ahead of its data)"
+    f = lambda t: None if t is None else t.float().numpy()
+    ref = oracle.mlp_forward(f(inp.x), f(inp.w_gate), f(inp.w_up), f(inp.w_down), w.P, w.order(), w.act)
+    dy = y - ref
+    if w.dtype == "f32":
+        assert np.max(np.abs(dy)) / np.max(np.abs(ref)) <= 1e-4
+    else:
+        assert np.linalg.norm(dy) / np.linalg.norm(ref) <= 3e-3
+        assert np.max(np.abs(dy)) <= 2e-2 * np.max(np.abs(ref))
