@@ -38,3 +38,4 @@ def test_c_program_runs(tmp_path):
         r = subprocess.run([exe, str(T)], capture_output=True, text=True, timeout=120)
         print(r.stdout.strip(), r.stderr.strip(), flush=True)
         assert r.returncode == 0, r.stdout + r.stderr
+
