@@ -86,7 +86,8 @@ tsp_status_t tsp_mlp_validate(int64_t T_max, int64_t d, int64_t f, int32_t P,
  *
  * out      : receives the handle; set to NULL on any failure.
  * T_max    : largest T any forward on this handle will pass (sizes the
- *            workspace that holds the hidden activations, T_max x f).
+ *            workspace: the hidden activations, T_max x f, plus for bf16
+ *            up to 64 MiB of fp32 partials for a split down product).
  * d, f, P  : hidden size, FFN width, number of weight shards.
  * act      : tsp_act_t.   dtype: tsp_dtype_t.
  * order    : host array of P int32, the ring order (order[k] = shard used at
@@ -134,6 +135,8 @@ tsp_status_t tsp_mlp_set_path(tsp_mlp_t h, int32_t path);
  * Shapes (features x tokens): 0 = 256 x 256, 1 = 256 x 128, 2 = 128 x 128,
  * 3 = 64 x 128, 4 = 256 x 256 with one wave per SIMD, 5 = 256 x 256 with
  * 16x16x32 MFMAs over global-to-LDS loads (the automatic choice at large T).
+ * With down shape 5 and fewer than 256 output tiles, the ring is split into
+ * groups of consecutive shards whose fp32 partials are added in ring order.
  * TSP_ERR_UNSUPPORTED if the shape does not divide the shard's
  * packed width (gate/up) or d (down), or for an fp32 handle. */
 tsp_status_t tsp_mlp_set_tiles(tsp_mlp_t h, int32_t gateup_tile, int32_t down_tile);
