@@ -579,6 +579,9 @@ constexpr int A_BLK = BM / 16, B_BLK = BN / 16;         // 1 KiB blocks per 32-w
 constexpr int LOADS = (A_BLK + B_BLK) / NW;
 constexpr int STAGE = (A_BLK + B_BLK) * 512;
 constexpr int NS = 4;
+// Fourth word of a raw (untyped, unswizzled) buffer resource on this GPU
+// family: 32-bit data format, no index stride.
+constexpr int kRawBufferWord3 = 0x00020000;
 
 // LDS slot of token r's 8-index chunk c in a B block. The 16x16x32 B
 // fragment read has lane l take token l % 16, chunk l / 16; with this XOR
@@ -588,6 +591,11 @@ constexpr int NS = 4;
 // still loads the 64 contiguous bytes of one token row.
 __device__ __forceinline__ int b_slot(int r, int c) { return 4 * r + (c ^ ((r >> 1) & 3)); }
 
+// One stage's global-to-LDS loads for this wave. BUF selects buffer loads
+// (buffer_load_dwordx4 ... lds: 128-bit resource + 32-bit per-lane offset)
+// instead of global_load_lds with 64-bit per-lane addresses; the caller
+// guarantees every offset stays below 2^31 bytes from the slab's start.
+template <bool BUF>
 __device__ __forceinline__ void issue(uint16_t* lds_stage, const uint16_t* __restrict__ a_base, int64_t a_rs,
                                       const uint16_t* __restrict__ b_src, int ldb, int64_t b_koff, int t0,
                                       int T, int w, int lane) {
@@ -596,14 +604,27 @@ __device__ __forceinline__ void issue(uint16_t* lds_stage, const uint16_t* __res
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
         const int b = i * NW + w;                       // wave-uniform block id
-        const uint16_t* g;
+        TSP_LDS void* dst = (TSP_LDS void*)(lds_stage + b * 512);
         if (b < A_BLK) {
-            g = a_base + (b >> 1) * a_rs + (b & 1) * 512 + lane * 8;
+            const int64_t off = (b >> 1) * a_rs + (b & 1) * 512 + lane * 8;
+            if constexpr (BUF) {
+                const __amdgpu_buffer_rsrc_t rs =
+                    __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, 0x7fffffff, kRawBufferWord3);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (int)(off * 2), 0, 0, 0);
+            } else {
+                __builtin_amdgcn_global_load_lds(a_base + off, dst, 16, 0, 0);
+            }
         } else {
             const int tok = min(t0 + (b - A_BLK) * 16 + r, T - 1);
-            g = b_src + (int64_t)tok * ldb + b_koff + c * 8;
+            const int64_t off = (int64_t)tok * ldb + c * 8;
+            if constexpr (BUF) {
+                const __amdgpu_buffer_rsrc_t rs =
+                    __builtin_amdgcn_make_buffer_rsrc((void*)(b_src + b_koff), (short)0, 0x7fffffff, kRawBufferWord3);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (int)(off * 2), 0, 0, 0);
+            } else {
+                __builtin_amdgcn_global_load_lds(b_src + b_koff + off, dst, 16, 0, 0);
+            }
         }
-        __builtin_amdgcn_global_load_lds(g, (TSP_LDS void*)(lds_stage + b * 512), 16, 0, 0);
     }
 }
 
@@ -630,6 +651,7 @@ __device__ __forceinline__ void read_frags(const uint16_t* lds_stage, bf16x8 (&a
     for (int j = 0; j < TN; ++j) bv[j] = bs[(wn * TN + j) * 64 + b_slot(r, c)];
 }
 
+template <bool BUF>
 __device__ __forceinline__ void mainloop(uint16_t* lds, f32x4 (&acc)[TM][TN], int ksteps, int64_t a_rs,
                                          const uint16_t* b_src, int ldb, int t0, int T,
                                          const uint16_t* a_tile, int64_t a_rec, int spp) {
@@ -653,7 +675,7 @@ __device__ __forceinline__ void mainloop(uint16_t* lds, f32x4 (&acc)[TM][TN], in
     constexpr int AHEAD = NS - 1;
     const int pro = min(AHEAD, ksteps);
     for (int t = 0; t < pro; ++t)
-        issue(lds + (t % NS) * STAGE, src(t), a_rs, b_src, ldb, (int64_t)t * 32, t0, T, w, lane);
+        issue<BUF>(lds + (t % NS) * STAGE, src(t), a_rs, b_src, ldb, (int64_t)t * 32, t0, T, w, lane);
     wait_stages(pro - 1);
     if (g1) stage_barrier();
     bf16x8 af[TM], bv[TN];
@@ -661,7 +683,7 @@ __device__ __forceinline__ void mainloop(uint16_t* lds, f32x4 (&acc)[TM][TN], in
         stage_barrier();
         __builtin_amdgcn_sched_barrier(0);
         if (t + AHEAD < ksteps)
-            issue(lds + ((t + AHEAD) % NS) * STAGE, src(t + AHEAD), a_rs, b_src, ldb,
+            issue<BUF>(lds + ((t + AHEAD) % NS) * STAGE, src(t + AHEAD), a_rs, b_src, ldb,
                   (int64_t)(t + AHEAD) * 32, t0, T, w, lane);
         read_frags(lds + (t % NS) * STAGE, af, bv, wm, wn, lane);
         lgkm_zero();
@@ -686,7 +708,9 @@ __device__ __forceinline__ void mainloop(uint16_t* lds, f32x4 (&acc)[TM][TN], in
 }  // namespace pp16
 
 // 16x16 result layout: lane l holds token l % 16 and features 4 (l / 16) + r.
-template <int ACT>
+// BUF: buffer loads (measured faster for the gate/up kernel; the down kernel
+// keeps global_load_lds, which measured faster there)
+template <int ACT, bool BUF>
 __global__ __launch_bounds__(512) void gateup_pp16(Bf16Args a, int n_ft_shard, int n_tt) {
     using namespace pp16;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
@@ -699,7 +723,7 @@ __global__ __launch_bounds__(512) void gateup_pp16(Bf16Args a, int n_ft_shard, i
     const uint16_t* a_tile = a.packed + (int64_t)s * a.shard_elems + (int64_t)(ftile * (BM / 32)) * a_rs;
     const int t0 = ttile * BN;
     f32x4 acc[TM][TN];
-    pp16::mainloop(lds, acc, a.d >> 5, a_rs, a.x, a.d, t0, a.T, a_tile, 0, 0);
+    pp16::mainloop<BUF>(lds, acc, a.d >> 5, a_rs, a.x, a.d, t0, a.T, a_tile, 0, 0);
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w / WN, wn = w % WN;
@@ -759,7 +783,7 @@ __global__ __launch_bounds__(512) void down_pp16(Bf16Args a, int n_ft, int n_tt,
     float* y = split > 1 ? a.part + (int64_t)g * a.T * a.d : a.y;
     const int t0 = ttile * BN;
     f32x4 acc[TM][TN];
-    pp16::mainloop(lds, acc, steps_per_group * spp, a_rs, h_g, a.f, t0, a.T, a_ft, a.shard_elems, spp);
+    pp16::mainloop<false>(lds, acc, steps_per_group * spp, a_rs, h_g, a.f, t0, a.T, a_ft, a.shard_elems, spp);
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w / WN, wn = w % WN;
@@ -896,10 +920,16 @@ hipError_t launch_gateup_tiled(const Bf16Args& a, int cfg, hipStream_t st) {
             const int ngu = a.swiglu ? 2 * a.F : a.F;
             const int n_ft_shard = ngu / 256, n_tt = (int)cdiv(a.T, 256);
             const dim3 grid((unsigned)(a.P * n_ft_shard * n_tt));
-            if (a.swiglu)
-                hipLaunchKernelGGL(gateup_pp16<1>, grid, dim3(512), 0, st, a, n_ft_shard, n_tt);
-            else
-                hipLaunchKernelGGL(gateup_pp16<2>, grid, dim3(512), 0, st, a, n_ft_shard, n_tt);
+            // buffer offsets are 32-bit: X (T x d bf16) and one stage's weight
+            // slab (8 rows of 32 x d-element blocks) must each span < 2^31 bytes
+            const bool buf = (int64_t)a.T * a.d * 2 < (int64_t(1) << 31) && (int64_t)a.d * 512 < (int64_t(1) << 31);
+            if (a.swiglu) {
+                if (buf) hipLaunchKernelGGL((gateup_pp16<1, true>), grid, dim3(512), 0, st, a, n_ft_shard, n_tt);
+                else hipLaunchKernelGGL((gateup_pp16<1, false>), grid, dim3(512), 0, st, a, n_ft_shard, n_tt);
+            } else {
+                if (buf) hipLaunchKernelGGL((gateup_pp16<2, true>), grid, dim3(512), 0, st, a, n_ft_shard, n_tt);
+                else hipLaunchKernelGGL((gateup_pp16<2, false>), grid, dim3(512), 0, st, a, n_ft_shard, n_tt);
+            }
             return hipGetLastError();
         }
         default: return hipErrorInvalidValue;
