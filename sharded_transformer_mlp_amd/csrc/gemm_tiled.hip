@@ -567,8 +567,9 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
 //
 // Same packed layout, tile 256 features x 256 tokens, 8 waves as 4 x 2 (wave
 // tile 64 x 128 as 4 x 8 MFMA blocks of 16 x 16). Global data goes straight
-// into a 4-deep LDS ring with global_load_lds_dwordx4 (no staging registers),
-// and the waves run the two-group ping-pong with 16x16x32 MFMAs. A 16x16x32
+// into a 5-deep LDS ring (4 stages in flight) with buffer_load ... lds or
+// global_load_lds (no staging registers), and the waves run the two-group
+// ping-pong with 16x16x32 MFMAs. A 16x16x32
 // A fragment (16 rows x 32 indices) is gathered from two 32 x 16 blocks;
 // a 16x16x32 B fragment is exactly one 16-token LDS block.
 namespace pp16 {
@@ -578,7 +579,7 @@ constexpr int TM = 4, TN = 8;                           // 16-row / 16-token MFM
 constexpr int A_BLK = BM / 16, B_BLK = BN / 16;         // 1 KiB blocks per 32-wide stage
 constexpr int LOADS = (A_BLK + B_BLK) / NW;
 constexpr int STAGE = (A_BLK + B_BLK) * 512;
-constexpr int NS = 4;
+constexpr int NS = 5;                                   // LDS ring depth: 5 x 32 KiB = all 160 KiB
 // Fourth word of a raw (untyped, unswizzled) buffer resource on this GPU
 // family: 32-bit data format, no index stride.
 constexpr int kRawBufferWord3 = 0x00020000;
@@ -630,7 +631,8 @@ __device__ __forceinline__ void issue(uint16_t* lds_stage, const uint16_t* __res
 
 __device__ __forceinline__ void wait_stages(int newer) {
 #define TSP_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-    if (newer >= 2) TSP_VMCNT(2 * LOADS);
+    if (newer >= 3) TSP_VMCNT(3 * LOADS);
+    else if (newer == 2) TSP_VMCNT(2 * LOADS);
     else if (newer == 1) TSP_VMCNT(LOADS);
     else TSP_VMCNT(0);
 #undef TSP_VMCNT
