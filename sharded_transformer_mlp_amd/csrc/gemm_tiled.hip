@@ -569,9 +569,9 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
 // tile 64 x 128 as 4 x 8 MFMA blocks of 16 x 16). Global data goes straight
 // into a 5-deep LDS ring (4 stages in flight) with buffer_load ... lds or
 // global_load_lds (no staging registers), and the waves run the two-group
-// ping-pong with 16x16x32 MFMAs. A 16x16x32
-// A fragment (16 rows x 32 indices) is gathered from two 32 x 16 blocks;
-// a 16x16x32 B fragment is exactly one 16-token LDS block.
+// ping-pong with 16x16x32 MFMAs. A 16x16x32 A fragment (16 rows x 32
+// indices) is gathered from two 32 x 16 blocks; a 16x16x32 B fragment is
+// exactly one 16-token LDS block.
 namespace pp16 {
 
 constexpr int BM = 256, BN = 256, NW = 8, WN = 2;
@@ -653,6 +653,16 @@ __device__ __forceinline__ void read_frags(const uint16_t* lds_stage, bf16x8 (&a
     for (int j = 0; j < TN; ++j) bv[j] = bs[(wn * TN + j) * 64 + b_slot(r, c)];
 }
 
+// Ping-pong over stages t = 0 .. ksteps-1. Waves 0-3 (group 0) and 4-7
+// (group 1), one of each per SIMD, alternate a memory phase M(t) (issue the
+// loads of stage t + 4 into the buffer stage t - 1 used, read stage t's
+// fragments, wait for them) and a compute phase C(t) (the 32 MFMAs). Group 1
+// runs one phase behind, and every phase boundary is a workgroup barrier, so
+// on each SIMD one wave computes while the other moves data. Each wave waits
+// for its own loads of stage t + 1 before the barrier that precedes M(t + 1)
+// (group 1 at the end of M(t), group 0 after C(t)); the barrier then makes
+// every wave's share visible. Stage t - 1's buffer was last read in M(t - 1)
+// of both groups, which ended before M(t) of group 0 starts.
 template <bool BUF>
 __device__ __forceinline__ void mainloop(uint16_t* lds, f32x4 (&acc)[TM][TN], int ksteps, int64_t a_rs,
                                          const uint16_t* b_src, int ldb, int t0, int T,
