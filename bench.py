@@ -22,6 +22,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -50,10 +51,15 @@ def log(*a):
 
 
 def kernel_source_hash(kernel: str) -> str:
+    """Hash of the code (comments and blank lines removed) of the sources a
+    kernel is built from: counter summaries stay valid across comment edits."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "sharded_transformer_mlp_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "sharded_transformer_mlp_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
+        h.update("\n".join(line for line in lines if line.strip()).encode())
     return h.hexdigest()[:16]
 
 
