@@ -125,8 +125,8 @@ tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y,
 tsp_status_t tsp_mlp_destroy(tsp_mlp_t h);
 
 /* Choose the forward path: AUTO (the weight-streaming skinny kernels when
- * T <= 32 and the shape suits them, bf16 only), TILED or SKINNY. SKINNY needs
- * bf16, T <= 32, d % 256 == 0 and P * F % 1024 == 0 at forward time
+ * T <= 48 and the shape suits them, bf16 only), TILED or SKINNY. SKINNY needs
+ * bf16, T <= 48, d % 256 == 0 and P * F % 1024 == 0 at forward time
  * (TSP_ERR_UNSUPPORTED otherwise). */
 tsp_status_t tsp_mlp_set_path(tsp_mlp_t h, int32_t path);
 

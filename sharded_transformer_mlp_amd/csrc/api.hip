@@ -229,11 +229,14 @@ tsp_status_t tsp_mlp_create(tsp_mlp_t* out, int64_t T_max, int64_t d, int64_t f,
     }
     h->packed_bytes = h->shard_elems * P * es;
     // workspace: hidden activations (tiled and fp32 paths: T_max x f; skinny:
-    // f / 16 fragment blocks of 1 KiB; the larger of the two), then for bf16
-    // the fp32 partials of a ring-group split of the down product (at most
-    // 64 MiB, see down_split_bytes)
+    // f / 16 fragment blocks of 1 KiB per 32-token block; the larger of the
+    // two), then for bf16 the fp32 partials of a ring-group split of the down
+    // product (at most 64 MiB, see down_split_bytes)
     h->work_bytes = T_max * f * es;
-    if (dtype == TSP_DTYPE_BF16 && f * 64 > h->work_bytes) h->work_bytes = f * 64;
+    if (dtype == TSP_DTYPE_BF16) {
+        const int64_t ntb = ((T_max < tsp::SKINNY_T_MAX ? T_max : tsp::SKINNY_T_MAX) + 31) / 32;
+        if (ntb * 32 * f * 2 > h->work_bytes) h->work_bytes = ntb * 32 * f * 2;
+    }
     h->work_bytes = (h->work_bytes + 255) / 256 * 256;
     h->part_off = h->work_bytes;
     if (dtype == TSP_DTYPE_BF16) h->work_bytes += tsp::down_split_bytes(T_max, (int)d, P);
@@ -290,10 +293,10 @@ tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y, hi
         a.down_off = h->down_off;
         a.T = (int)T; a.d = (int)h->d; a.f = (int)h->f; a.F = (int)h->F; a.P = h->P;
         a.swiglu = swiglu ? 1 : 0;
-        const bool sk_ok = T <= 32 && tsp::skinny_supported(a.d, a.F, a.P);
+        const bool sk_ok = T <= tsp::SKINNY_T_MAX && tsp::skinny_supported(a.d, a.F, a.P);
         bool skinny = false;
         if (h->path == TSP_PATH_SKINNY) {
-            if (!sk_ok) return fail(TSP_ERR_UNSUPPORTED, "skinny path needs T <= 32, d %% 256 == 0 and P*F %% 1024 == 0");
+            if (!sk_ok) return fail(TSP_ERR_UNSUPPORTED, "skinny path needs T <= %d, d %% 256 == 0 and P*F %% 1024 == 0", tsp::SKINNY_T_MAX);
             skinny = true;
         } else if (h->path == TSP_PATH_AUTO) {
             skinny = sk_ok;

@@ -57,7 +57,8 @@ const char* tiled_cfg_name(int cfg);
 bool gateup_cfg_fits(int cfg, int d, int F, int swiglu);
 bool down_cfg_fits(int cfg, int d, int F);
 
-// Skinny (T <= 32) weight-streaming path.
+// Skinny weight-streaming path (T <= SKINNY_T_MAX).
+constexpr int SKINNY_T_MAX = 48;
 hipError_t launch_gateup_skinny(const Bf16Args& a, hipStream_t st);
 hipError_t launch_down_skinny(const Bf16Args& a, hipStream_t st);
 bool skinny_supported(int d, int F, int P);

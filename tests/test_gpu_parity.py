@@ -162,7 +162,7 @@ def test_every_tile_shape_gelu(gcfg):
     check(w, y, ref(w, inp), f"gelu tiles {gcfg}")
 
 
-@pytest.mark.parametrize("T", [1, 5, 16, 17, 32])
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 32, 33, 40, 48])
 @pytest.mark.parametrize("act", ["swiglu", "gelu_tanh"])
 def test_skinny_parity(T, act):
     w = Workload("k", T=T, d=1024, f=2048, P=4, act=act, dtype="bf16", seed=31, r0=2)
@@ -184,6 +184,13 @@ def test_skinny_smallest_shape_and_limits():
         inp = make_inputs(w)
         y, _ = run_gpu(w, inp, path="skinny")
         check(w, y, ref(w, inp), f"skinny P={P}")
+    w = Workload("m", T=49, d=256, f=1024, P=2, act="swiglu", dtype="bf16", seed=33)
+    say("[gpu] skinny unsupported T=49")
+    inp = make_inputs(w)
+    with pytest.raises(TspError):
+        run_gpu(w, inp, path="skinny")
+    y, _ = run_gpu(w, inp)                  # AUTO takes the tiled kernels at T = 49
+    check(w, y, ref(w, inp), "auto T=49")
     w = Workload("m", T=9, d=192, f=1024, P=2, act="swiglu", dtype="bf16", seed=33)
     say("[gpu] skinny unsupported d=192")
     inp = make_inputs(w)
