@@ -812,6 +812,308 @@ __global__ __launch_bounds__(512) void down_pp16(Bf16Args a, int n_ft, int n_tt,
     }
 }
 
+// ------------------------------------------------------------------ shape 6
+// 256 x 256 tile, 4 waves (one per SIMD) as 2 x 2, each wave a 128 x 128
+// piece held in 64 16x16 fp32 accumulators (all 256 accumulation registers),
+// 16x16x32 MFMAs, global-to-LDS loads into the same 5-stage ring as shape 5.
+// A wave reads 16 fragments per 64 MFMAs (shape 5's 64 x 128 wave pieces:
+// 12 per 32), so LDS read traffic per flop is two thirds of shape 5's.
+//
+// The first reduction step starts every accumulator from the constant 0
+// (MFMA source C = 0) instead of adding to zero-initialised registers: with
+// that form the compiler keeps each accumulator in one register across the
+// loop (with zero-initialised registers it copies accumulators between
+// registers on every trip).
+//
+// Measured (Llama-3-8B shape): the down kernel runs ~5 % faster than shape
+// 5's (the automatic down choice); the gate/up kernel ~1 % slower, as its
+// seven tiles per CU each end in an epilogue that no other wave overlaps
+// (shape 5's second wave group still computes while the first one stores).
+// Taking the global-to-LDS loads out (a timing copy, not kept) makes either
+// kernel ~25 % faster: issuing them, not LDS reads or barriers, is what keeps
+// the matrix pipe below full rate here. Staging one or both operands through
+// registers instead measured slower.
+namespace w16 {
+
+constexpr int BM = 256, BN = 256, NW = 4, WN = 2;
+constexpr int TM = 8, TN = 8;                           // 16-row / 16-token MFMA blocks per wave
+constexpr int A_BLK = BM / 16, B_BLK = BN / 16;         // 1 KiB blocks per 32-wide stage
+constexpr int LA = A_BLK / NW, LB = B_BLK / NW;         // blocks each wave loads per stage
+constexpr int LOADS = LA + LB;
+constexpr int STAGE = (A_BLK + B_BLK) * 512;
+constexpr int NS = 5;                                   // 5 x 32 KiB = all 160 KiB of LDS
+static_assert(NS * STAGE * 2 <= 160 * 1024, "LDS");
+static_assert((NS - 1) * LOADS <= 63, "vmcnt range");
+
+#define TSP_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// Load r of this wave's LOADS global-to-LDS loads of one stage: A blocks
+// w, w + 4, .. first, then B blocks likewise (same LDS layout and B swizzle
+// as shape 5). BUF: buffer loads with 32-bit offsets (see shape 5).
+template <bool BUF>
+__device__ __forceinline__ void issue_one(int r, uint16_t* lds_stage, const uint16_t* __restrict__ a_base,
+                                          int64_t a_rs, const uint16_t* __restrict__ b_src, int ldb,
+                                          int64_t b_koff, int t0, int T, int w, int lane) {
+    if (r < LA) {
+        const int b = r * NW + w;
+        TSP_LDS void* dst = (TSP_LDS void*)(lds_stage + b * 512);
+        const int64_t off = (b >> 1) * a_rs + (b & 1) * 512 + lane * 8;
+        if constexpr (BUF) {
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, 0x7fffffff, pp16::kRawBufferWord3);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (int)(off * 2), 0, 0, 0);
+        } else {
+            __builtin_amdgcn_global_load_lds(a_base + off, dst, 16, 0, 0);
+        }
+    } else {
+        const int bb = (r - LA) * NW + w;
+        const int rr = lane >> 2;
+        const int c = (lane & 3) ^ ((rr >> 1) & 3);     // slot = lane = pp16::b_slot(rr, c)
+        TSP_LDS void* dst = (TSP_LDS void*)(lds_stage + (A_BLK + bb) * 512);
+        const int tok = min(t0 + bb * 16 + rr, T - 1);
+        const int64_t off = (int64_t)tok * ldb + c * 8;
+        if constexpr (BUF) {
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(b_src + b_koff), (short)0, 0x7fffffff, pp16::kRawBufferWord3);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (int)(off * 2), 0, 0, 0);
+        } else {
+            __builtin_amdgcn_global_load_lds(b_src + b_koff + off, dst, 16, 0, 0);
+        }
+    }
+}
+
+// Fragment q of a stage for this wave: A fragments 0 .. TM-1 (16 rows x 32
+// reduction indices: lane l takes row l % 16, chunk l / 16), then the B
+// fragments (16 tokens x 32 indices).
+__device__ __forceinline__ void read_one(int q, const uint16_t* lds_stage, bf16x8 (&af)[TM], bf16x8 (&bv)[TN],
+                                         int wm, int wn, int lane) {
+    const int r = lane & 15, c = lane >> 4;
+    if (q < TM) {
+        const bf16x8* as = reinterpret_cast<const bf16x8*>(lds_stage);
+        const int ib = wm * TM + q;                     // 16-row block: rows 16 (ib % 2) + r of 32-row block ib / 2
+        af[q] = as[((ib >> 1) * 2 + (c >> 1)) * 64 + (c & 1) * 32 + (ib & 1) * 16 + r];
+    } else {
+        const bf16x8* bs = reinterpret_cast<const bf16x8*>(lds_stage + A_BLK * 512);
+        bv[q - TM] = bs[(wn * TN + q - TM) * 64 + pp16::b_slot(r, c)];
+    }
+}
+
+// Load cursor: the next stage to load (clamped to the last one), advanced
+// without divisions. spp > 0 (down product): the reduction walks shard
+// records, spp steps each, a_rec elements apart.
+struct Cursor {
+    const uint16_t* a;                                  // A slab of the stage
+    int tl, ls;                                         // stage index, step inside the record
+    int ksteps, spp;
+    int64_t a_rec;
+    __device__ int64_t bk() const { return (int64_t)tl * 32; }
+    __device__ void advance() {
+        const bool adv = tl + 1 < ksteps;
+        const bool wrap = spp > 0 && ls + 1 == spp;
+        a += adv ? (wrap ? a_rec - (int64_t)(spp - 1) * 1024 : (int64_t)1024) : (int64_t)0;
+        ls = adv ? (wrap ? 0 : ls + 1) : ls;
+        tl += adv ? 1 : 0;
+    }
+};
+
+__device__ __forceinline__ int next_buf(int off) { return off == (NS - 1) * STAGE ? 0 : off + STAGE; }
+
+// Step t. The barrier makes every wave's share of stage t + 1 visible and
+// ends every wave's fragment reads of stage t (issued in step t - 1), so
+// stage t's buffer takes the loads of stage t + NS. The wave then reads stage
+// t + 1's fragments into the other register set while its MFMAs run on stage
+// t's, and before the next barrier waits for those reads and for its own
+// loads of stage t + 2. Every step issues one stage (past the end, the last
+// stage again, into a buffer nobody reads), so that wait is always "at most 3
+// stages newer". FIRST: the accumulators start from 0. LAST: MFMAs only.
+//
+// With one wave per SIMD nothing else feeds the matrix pipe while this wave
+// issues other work, so scheduling fences fix the order: three MFMAs right
+// after the barrier, then one load per MFMA, one fragment read per two
+// MFMAs, and the scalar bookkeeping for the next step spread over the
+// remaining MFMAs.
+template <bool BUF, bool FIRST, bool LAST>
+__device__ __forceinline__ void step(int& ld_ref, int& rd_ref, Cursor& cur, uint16_t* lds, f32x4 (&acc)[TM][TN],
+                                     const bf16x8 (&ca)[TM], const bf16x8 (&cb)[TN], bf16x8 (&na)[TM],
+                                     bf16x8 (&nb)[TN], int64_t a_rs, const uint16_t* b_src, int ldb, int t0, int T,
+                                     int w, int wm, int wn, int lane) {
+    constexpr int LEAD = 3;
+    constexpr int REST = TM * TN - LEAD - LOADS - 2 * (TM + TN);
+    static_assert(REST >= 8, "schedule");
+    auto mf = [&](int m) {
+        const int i = m / TN, j = m % TN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], FIRST ? f32x4{0.f, 0.f, 0.f, 0.f}
+                                                                                : acc[i][j], 0, 0, 0);
+    };
+    if constexpr (LAST) {
+#pragma unroll
+        for (int m = 0; m < TM * TN; ++m) mf(m);
+        return;
+    }
+    const int ld_off = ld_ref, rd_off = rd_ref;
+    const uint16_t* ap = cur.a;
+    const int64_t bk = cur.bk();
+    stage_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < LEAD; ++m) mf(m);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+        issue_one<BUF>(r, lds + ld_off, ap, a_rs, b_src, ldb, bk, t0, T, w, lane);
+        mf(LEAD + r);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = 0; q < TM + TN; ++q) {
+        read_one(q, lds + rd_off, na, nb, wm, wn, lane);
+        mf(LEAD + LOADS + 2 * q);
+        mf(LEAD + LOADS + 2 * q + 1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    cur.advance();
+    ld_ref = rd_off;
+    rd_ref = next_buf(rd_off);
+#pragma unroll
+    for (int m = TM * TN - REST; m < TM * TN; ++m) mf(m);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x006, 3, 0);   // VALU / SALU
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, REST - 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    TSP_VMCNT(3 * LOADS);                               // own loads of stage t + 2 landed
+    lgkm_zero();                                        // stage t + 1's fragments in registers
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The reduction over ksteps stages (even, >= 2: d and F are multiples of 64).
+template <bool BUF>
+__device__ __forceinline__ void mainloop(uint16_t* lds, f32x4 (&acc)[TM][TN], int ksteps, int64_t a_rs,
+                                         const uint16_t* b_src, int ldb, int t0, int T,
+                                         const uint16_t* a_tile, int64_t a_rec, int spp) {
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = w / WN, wn = w % WN;
+    Cursor cur{a_tile, 0, 0, ksteps, spp, a_rec};
+    for (int t = 0; t < NS; ++t) {
+#pragma unroll
+        for (int r = 0; r < LOADS; ++r)
+            issue_one<BUF>(r, lds + t * STAGE, cur.a, a_rs, b_src, ldb, cur.bk(), t0, T, w, lane);
+        cur.advance();
+    }
+    bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
+    TSP_VMCNT((NS - 1) * LOADS);                        // own loads of stage 0 landed
+    stage_barrier();
+#pragma unroll
+    for (int q = 0; q < TM + TN; ++q) read_one(q, lds, a0, b0, wm, wn, lane);
+    TSP_VMCNT((NS - 2) * LOADS);                        // own loads of stage 1 landed
+    lgkm_zero();
+    __builtin_amdgcn_sched_barrier(0);
+    int ld = 0, rd = STAGE;                             // buffers of stages t and t + 1
+    step<BUF, true, false>(ld, rd, cur, lds, acc, a0, b0, a1, b1, a_rs, b_src, ldb, t0, T, w, wm, wn, lane);
+    for (int t = 1; t + 2 < ksteps; t += 2) {
+        step<BUF, false, false>(ld, rd, cur, lds, acc, a1, b1, a0, b0, a_rs, b_src, ldb, t0, T, w, wm, wn, lane);
+        step<BUF, false, false>(ld, rd, cur, lds, acc, a0, b0, a1, b1, a_rs, b_src, ldb, t0, T, w, wm, wn, lane);
+    }
+    step<BUF, false, true>(ld, rd, cur, lds, acc, a1, b1, a0, b0, a_rs, b_src, ldb, t0, T, w, wm, wn, lane);
+    TSP_VMCNT(0);                                       // no load into LDS outlives the workgroup
+}
+#undef TSP_VMCNT
+
+}  // namespace w16
+
+template <int ACT, bool BUF>
+__global__ __launch_bounds__(256) void gateup_w16(Bf16Args a, int n_ft_shard, int n_tt) {
+    using namespace w16;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
+    poison_lds(lds, sizeof(lds));
+    int ttile, flin;
+    raster(xcd_remap(blockIdx.x, gridDim.x), a.P * n_ft_shard, n_tt, ttile, flin);
+    const int s = flin / n_ft_shard;
+    const int ftile = flin - s * n_ft_shard;
+    const int64_t a_rs = (int64_t)(a.d >> 4) * 512;
+    const uint16_t* a_tile = a.packed + (int64_t)s * a.shard_elems + (int64_t)(ftile * (BM / 32)) * a_rs;
+    const int t0 = ttile * BN;
+    f32x4 acc[TM][TN];
+    w16::mainloop<BUF>(lds, acc, a.d >> 5, a_rs, a.x, a.d, t0, a.T, a_tile, 0, 0);
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w / WN, wn = w % WN;
+    const int fsub = 4 * (lane >> 4);
+    if constexpr (ACT == 1) {
+        // the wave's 128 rows are two (32 gate, 32 up) row pairs: 16-row
+        // blocks 4 q, 4 q + 1 gate and 4 q + 2, 4 q + 3 up of hidden group q
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int hcol = s * a.F + (ftile * (BM / 64) + wm * 2 + q) * 32 + i * 16 + fsub;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int tok = t0 + (wn * TN + j) * 16 + (lane & 15);
+                    if (tok < a.T) {
+                        const f32x4 g = acc[4 * q + i][j], u = acc[4 * q + 2 + i][j];
+                        *reinterpret_cast<uint2*>(a.h + (int64_t)tok * a.f + hcol) =
+                            pack4_bf16(silu_f(g[0]) * u[0], silu_f(g[1]) * u[1], silu_f(g[2]) * u[2],
+                                       silu_f(g[3]) * u[3]);
+                    }
+                }
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int hcol = s * a.F + ftile * BM + (wm * TM + i) * 16 + fsub;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int tok = t0 + (wn * TN + j) * 16 + (lane & 15);
+                if (tok < a.T) {
+                    const f32x4 u = acc[i][j];
+                    *reinterpret_cast<uint2*>(a.h + (int64_t)tok * a.f + hcol) =
+                        pack4_bf16(gelu_tanh_f(u[0]), gelu_tanh_f(u[1]), gelu_tanh_f(u[2]), gelu_tanh_f(u[3]));
+                }
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void down_w16(Bf16Args a, int n_ft, int n_tt, int split) {
+    using namespace w16;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
+    poison_lds(lds, sizeof(lds));
+    const int n_tiles = n_ft * n_tt;
+    const int lin = xcd_remap(blockIdx.x, gridDim.x);
+    const int g = lin / n_tiles;
+    int ttile, ftile;
+    raster(lin - g * n_tiles, n_ft, n_tt, ttile, ftile);
+    const int spp = a.F >> 5;
+    const int steps_per_group = a.P / split;
+    const int64_t a_rs = (int64_t)(a.F >> 4) * 512;
+    const uint16_t* a_ft = a.packed + a.down_off + (int64_t)(g * steps_per_group) * a.shard_elems +
+                           (int64_t)(ftile * (BM / 32)) * a_rs;
+    const uint16_t* h_g = a.h + (int64_t)(g * steps_per_group) * a.F;
+    float* y = split > 1 ? a.part + (int64_t)g * a.T * a.d : a.y;
+    const int t0 = ttile * BN;
+    f32x4 acc[TM][TN];
+    w16::mainloop<false>(lds, acc, steps_per_group * spp, a_rs, h_g, a.f, t0, a.T, a_ft, a.shard_elems, spp);
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w / WN, wn = w % WN;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int n = ftile * BM + (wm * TM + i) * 16 + 4 * (lane >> 4);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int tok = t0 + (wn * TN + j) * 16 + (lane & 15);
+            if (tok < a.T) {
+                const f32x4 v = acc[i][j];
+                *reinterpret_cast<float4*>(y + (int64_t)tok * a.d + n) = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+    }
+}
+
 // Y = sum of the `split` partials, added in ring order (group 0 first).
 __global__ __launch_bounds__(256) void reduce_partials(const float4* __restrict__ part, int split, int64_t n4,
                                                        float4* __restrict__ y) {
@@ -829,12 +1131,13 @@ __global__ __launch_bounds__(256) void reduce_partials(const float4* __restrict_
 // cfg: 0 = 256 x 256 (8 waves as 4 x 2), 1 = 256 x 128 (8 waves),
 //      2 = 128 x 128 (4 waves as 2 x 2), 3 = 64 x 128 (4 waves as 1 x 4),
 //      4 = 256 x 256 with 4 waves (one per SIMD), 5 = 256 x 256 16x16x32
-//      ping-pong over global-to-LDS loads (the fastest measured at large T)
+//      ping-pong over global-to-LDS loads, 6 = 256 x 256 16x16x32 with 4
+//      waves of 128 x 128 over global-to-LDS loads
 struct CfgDesc { int bm, bn; const char* name; };
-constexpr int kNumCfgs = 6;
+constexpr int kNumCfgs = 7;
 static const CfgDesc kCfgs[kNumCfgs] = {
     {256, 256, "256x256"}, {256, 128, "256x128"}, {128, 128, "128x128"}, {64, 128, "64x128"},
-    {256, 256, "256x256 4-wave"}, {256, 256, "256x256 16x16 ping-pong"}};
+    {256, 256, "256x256 4-wave"}, {256, 256, "256x256 16x16 ping-pong"}, {256, 256, "256x256 16x16 4-wave"}};
 
 const char* tiled_cfg_name(int cfg) { return (cfg >= 0 && cfg < kNumCfgs) ? kCfgs[cfg].name : "none"; }
 
@@ -850,11 +1153,13 @@ bool down_cfg_fits(int cfg, int d, int F) {
     return cfg >= 0 && cfg < kNumCfgs && d % kCfgs[cfg].bm == 0 && F % 64 == 0;
 }
 
-// Automatic choice: the first shape in kAuto that divides the shard's packed
-// width (gate/up) or d (down) and still gives at least one full wave of
-// workgroups on 256 CUs; otherwise the first one that divides. Shapes 0 and
-// 4 stay reachable through tsp_mlp_set_tiles.
+// Automatic choice: the first shape in the list that divides the shard's
+// packed width (gate/up) or d (down) and still gives at least one full wave
+// of workgroups on 256 CUs; otherwise the first one that divides. Shapes 0
+// and 4 stay reachable through tsp_mlp_set_tiles (and 6 for gate/up, 5 for
+// down).
 static const int kAuto[4] = {5, 1, 2, 3};
+static const int kAutoDown[4] = {6, 1, 2, 3};
 
 int choose_gateup_cfg(int T, int d, int F, int P, int swiglu) {
     const int64_t ngu = swiglu ? 2LL * F : (int64_t)F;
@@ -869,7 +1174,7 @@ int choose_gateup_cfg(int T, int d, int F, int P, int swiglu) {
 }
 
 int choose_down_split(int T, int d, int P, int cfg) {
-    if (cfg != 5 || d % 256) return 1;
+    if ((cfg != 5 && cfg != 6) || d % 256) return 1;
     const int64_t tiles = (int64_t)(d / 256) * cdiv(T, 256);
     int best = 1;
     for (int s = 2; s <= P; ++s)                        // the largest divisor of P that keeps one round
@@ -881,7 +1186,7 @@ int64_t down_split_bytes(int64_t T_max, int d, int P) {
     int64_t most = 0;
     for (int64_t t = 256; t < T_max + 256; t += 256) {
         const int64_t T = t < T_max ? t : T_max;
-        const int s = choose_down_split((int)T, d, P, 5);
+        const int s = choose_down_split((int)T, d, P, 6);     // shapes 5 and 6 split alike
         if (s > 1 && s * T * d * 4 > most) most = s * T * d * 4;
     }
     return most;
@@ -889,7 +1194,7 @@ int64_t down_split_bytes(int64_t T_max, int d, int P) {
 
 int choose_down_cfg(int T, int d, int F, int P) {
     int fallback = -1;
-    for (int c : kAuto) {
+    for (int c : kAutoDown) {
         if (d % kCfgs[c].bm || F % 64) continue;
         const int64_t wgs = (d / kCfgs[c].bm) * cdiv(T, kCfgs[c].bn) * choose_down_split(T, d, P, c);
         if (fallback < 0) fallback = c;
@@ -943,12 +1248,26 @@ hipError_t launch_gateup_tiled(const Bf16Args& a, int cfg, hipStream_t st) {
             }
             return hipGetLastError();
         }
+        case 6: {
+            const int ngu = a.swiglu ? 2 * a.F : a.F;
+            const int n_ft_shard = ngu / 256, n_tt = (int)cdiv(a.T, 256);
+            const dim3 grid((unsigned)(a.P * n_ft_shard * n_tt));
+            const bool buf = (int64_t)a.T * a.d * 2 < (int64_t(1) << 31) && (int64_t)a.d * 512 < (int64_t(1) << 31);
+            if (a.swiglu) {
+                if (buf) hipLaunchKernelGGL((gateup_w16<1, true>), grid, dim3(256), 0, st, a, n_ft_shard, n_tt);
+                else hipLaunchKernelGGL((gateup_w16<1, false>), grid, dim3(256), 0, st, a, n_ft_shard, n_tt);
+            } else {
+                if (buf) hipLaunchKernelGGL((gateup_w16<2, true>), grid, dim3(256), 0, st, a, n_ft_shard, n_tt);
+                else hipLaunchKernelGGL((gateup_w16<2, false>), grid, dim3(256), 0, st, a, n_ft_shard, n_tt);
+            }
+            return hipGetLastError();
+        }
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_down_tiled(const Bf16Args& a, int cfg, int split, hipStream_t st) {
-    if (split > 1 && (cfg != 5 || a.P % split || !a.part)) return hipErrorInvalidValue;
+    if (split > 1 && ((cfg != 5 && cfg != 6) || a.P % split || !a.part)) return hipErrorInvalidValue;
     switch (cfg) {
         case 0: return down_go<256, 256, 4, 2>(a, st);
         case 1: return down_go<256, 128, 4, 2>(a, st);
@@ -958,6 +1277,12 @@ hipError_t launch_down_tiled(const Bf16Args& a, int cfg, int split, hipStream_t 
         case 5: {
             const int n_ft = a.d / 256, n_tt = (int)cdiv(a.T, 256);
             hipLaunchKernelGGL(down_pp16, dim3((unsigned)(n_ft * n_tt * split)), dim3(512), 0, st, a, n_ft, n_tt,
+                               split);
+            return hipGetLastError();
+        }
+        case 6: {
+            const int n_ft = a.d / 256, n_tt = (int)cdiv(a.T, 256);
+            hipLaunchKernelGGL(down_w16, dim3((unsigned)(n_ft * n_tt * split)), dim3(256), 0, st, a, n_ft, n_tt,
                                split);
             return hipGetLastError();
         }

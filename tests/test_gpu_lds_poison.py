@@ -37,9 +37,15 @@ def poison_library():
 
 CASES = [
     ("tiled shape 5 + split", Workload("a", T=300, d=512, f=2048, P=4, act="swiglu", dtype="bf16", seed=11, r0=1),
-     "tiled", None),
+     "tiled", (5, 5)),
+    ("tiled auto shapes + split", Workload("a", T=300, d=512, f=2048, P=4, act="swiglu", dtype="bf16", seed=11,
+                                           r0=1), "tiled", None),
     ("tiled shape 5, 4 tiles", Workload("b", T=513, d=1024, f=4096, P=2, act="swiglu", dtype="bf16", seed=12),
      "tiled", (5, 5)),
+    ("tiled shape 6 + split", Workload("a", T=300, d=512, f=2048, P=4, act="swiglu", dtype="bf16", seed=11, r0=1),
+     "tiled", (6, 6)),
+    ("tiled shape 6, 4 tiles", Workload("b", T=513, d=1024, f=4096, P=2, act="swiglu", dtype="bf16", seed=12),
+     "tiled", (6, 6)),
     ("tiled shape 0", Workload("c", T=290, d=512, f=2048, P=2, act="swiglu", dtype="bf16", seed=21), "tiled", (0, 0)),
     ("tiled shape 4", Workload("c", T=290, d=512, f=2048, P=2, act="swiglu", dtype="bf16", seed=21), "tiled", (4, 4)),
     ("tiled gelu shape 1/3", Workload("g", T=200, d=256, f=1024, P=2, act="gelu_tanh", dtype="bf16", seed=12),
