@@ -134,10 +134,9 @@ tsp_status_t tsp_mlp_set_path(tsp_mlp_t h, int32_t path);
  * gate/up and down kernels (-1 = choose per forward from T and the shape).
  * Shapes (features x tokens): 0 = 256 x 256, 1 = 256 x 128, 2 = 128 x 128,
  * 3 = 64 x 128, 4 = 256 x 256 with one wave per SIMD, 5 = 256 x 256 with
- * 16x16x32 MFMAs over global-to-LDS loads, two wave groups in ping-pong (the
- * automatic gate/up choice at large T), 6 = the same tile with four waves of
- * 128 x 128 (the automatic down choice at large T). Shapes 5 and 6 compute
- * bitwise identical results. With down shape 5 or 6 and fewer than 256
+ * 16x16x32 MFMAs over global-to-LDS loads, two wave groups in ping-pong,
+ * 6 = the same tile with four waves of 128 x 128 (the automatic choice at
+ * large T). Shapes 5 and 6 compute bitwise identical results. With down shape 5 or 6 and fewer than 256
  * output tiles, the ring is split into groups of consecutive shards whose
  * fp32 partials are added in ring order.
  * TSP_ERR_UNSUPPORTED if the shape does not divide the shard's

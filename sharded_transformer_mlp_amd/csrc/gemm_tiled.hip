@@ -24,10 +24,12 @@
 // XOR-swizzled) 16-byte-per-lane access without bank conflicts. The waves
 // run a two-group ping-pong (see mainloop): on every SIMD one wave issues
 // MFMAs while the other moves data. Shapes 0-4 use this register-staged
-// loop with 32x32x16 MFMAs; shape 5 (namespace pp16, the automatic choice at
-// large T) loads global memory straight into LDS and uses 16x16x32 MFMAs.
-// The choice between them is empirical: shape 5 measured fastest on every
-// large-T workload.
+// loop with 32x32x16 MFMAs; shape 5 (namespace pp16) keeps the ping-pong but
+// loads global memory straight into LDS and uses 16x16x32 MFMAs; shape 6
+// (namespace w16, the automatic choice at large T) loads like shape 5 but
+// runs one wave per SIMD holding a 128 x 128 piece in all 256 accumulation
+// registers. The choice between them is empirical: shape 6 measured fastest
+// on every large-T workload, shape 5 next.
 #include "common.h"
 #include "launch.h"
 
@@ -825,14 +827,14 @@ __global__ __launch_bounds__(512) void down_pp16(Bf16Args a, int n_ft, int n_tt,
 // loop (with zero-initialised registers it copies accumulators between
 // registers on every trip).
 //
-// Measured (Llama-3-8B shape): the down kernel runs ~5 % faster than shape
-// 5's (the automatic down choice); the gate/up kernel ~1 % slower, as its
-// seven tiles per CU each end in an epilogue that no other wave overlaps
-// (shape 5's second wave group still computes while the first one stores).
-// Taking the global-to-LDS loads out (a timing copy, not kept) makes either
-// kernel ~25 % faster: issuing them, not LDS reads or barriers, is what keeps
-// the matrix pipe below full rate here. Staging one or both operands through
-// registers instead measured slower.
+// Measured (Llama-3-8B shape, same box): gate/up ~4 % and down ~8 % faster
+// than shape 5, so shape 6 is the automatic choice for both. Taking the
+// global-to-LDS loads out (a timing copy, not kept) makes either kernel ~25 %
+// faster: issuing them, not LDS reads or barriers, is what keeps the matrix
+// pipe below full rate, and how far apart they are issued matters (see
+// step). Staging one or both operands through registers, and a persistent
+// grid that streams the next tile's first stages during the epilogue, each
+// measured slower.
 namespace w16 {
 
 constexpr int BM = 256, BN = 256, NW = 4, WN = 2;
@@ -929,17 +931,18 @@ __device__ __forceinline__ int next_buf(int off) { return off == (NS - 1) * STAG
 //
 // With one wave per SIMD nothing else feeds the matrix pipe while this wave
 // issues other work, so scheduling fences fix the order: three MFMAs right
-// after the barrier, then one load per MFMA, one fragment read per two
-// MFMAs, and the scalar bookkeeping for the next step spread over the
-// remaining MFMAs.
+// after the barrier, then eight groups of one load, two fragment reads and
+// seven MFMAs (a load right after another costs the matrix pipe far more
+// than one that follows a few MFMAs: 3-5 % of the kernel time here), and the
+// scalar bookkeeping for the next step spread over the last five MFMAs.
 template <bool BUF, bool FIRST, bool LAST>
 __device__ __forceinline__ void step(int& ld_ref, int& rd_ref, Cursor& cur, uint16_t* lds, f32x4 (&acc)[TM][TN],
                                      const bf16x8 (&ca)[TM], const bf16x8 (&cb)[TN], bf16x8 (&na)[TM],
                                      bf16x8 (&nb)[TN], int64_t a_rs, const uint16_t* b_src, int ldb, int t0, int T,
                                      int w, int wm, int wn, int lane) {
-    constexpr int LEAD = 3;
-    constexpr int REST = TM * TN - LEAD - LOADS - 2 * (TM + TN);
-    static_assert(REST >= 8, "schedule");
+    constexpr int LEAD = 3, GROUP = 7;
+    constexpr int TAIL = TM * TN - LEAD - LOADS * GROUP;
+    static_assert(LOADS == 8 && TM + TN == 2 * LOADS && TAIL == 5, "schedule");
     auto mf = [&](int m) {
         const int i = m / TN, j = m % TN;
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], FIRST ? f32x4{0.f, 0.f, 0.f, 0.f}
@@ -959,29 +962,32 @@ __device__ __forceinline__ void step(int& ld_ref, int& rd_ref, Cursor& cur, uint
     for (int m = 0; m < LEAD; ++m) mf(m);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int r = 0; r < LOADS; ++r) {
-        issue_one<BUF>(r, lds + ld_off, ap, a_rs, b_src, ldb, bk, t0, T, w, lane);
-        mf(LEAD + r);
+    for (int g = 0; g < LOADS; ++g) {
+        const int m0 = LEAD + GROUP * g;
+        issue_one<BUF>(g, lds + ld_off, ap, a_rs, b_src, ldb, bk, t0, T, w, lane);
+        mf(m0);
+        mf(m0 + 1);
         __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int q = 0; q < TM + TN; ++q) {
-        read_one(q, lds + rd_off, na, nb, wm, wn, lane);
-        mf(LEAD + LOADS + 2 * q);
-        mf(LEAD + LOADS + 2 * q + 1);
+        read_one(2 * g, lds + rd_off, na, nb, wm, wn, lane);
+        mf(m0 + 2);
+        mf(m0 + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        read_one(2 * g + 1, lds + rd_off, na, nb, wm, wn, lane);
+        mf(m0 + 4);
+        mf(m0 + 5);
+        mf(m0 + 6);
         __builtin_amdgcn_sched_barrier(0);
     }
     cur.advance();
     ld_ref = rd_off;
     rd_ref = next_buf(rd_off);
 #pragma unroll
-    for (int m = TM * TN - REST; m < TM * TN; ++m) mf(m);
+    for (int m = TM * TN - TAIL; m < TM * TN; ++m) mf(m);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < TAIL; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x006, 3, 0);   // VALU / SALU
+        __builtin_amdgcn_sched_group_barrier(0x006, 4, 0);   // VALU / SALU
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, REST - 8, 0);
     __builtin_amdgcn_sched_barrier(0);
     TSP_VMCNT(3 * LOADS);                               // own loads of stage t + 2 landed
     lgkm_zero();                                        // stage t + 1's fragments in registers
@@ -1155,11 +1161,9 @@ bool down_cfg_fits(int cfg, int d, int F) {
 
 // Automatic choice: the first shape in the list that divides the shard's
 // packed width (gate/up) or d (down) and still gives at least one full wave
-// of workgroups on 256 CUs; otherwise the first one that divides. Shapes 0
-// and 4 stay reachable through tsp_mlp_set_tiles (and 6 for gate/up, 5 for
-// down).
-static const int kAuto[4] = {5, 1, 2, 3};
-static const int kAutoDown[4] = {6, 1, 2, 3};
+// of workgroups on 256 CUs; otherwise the first one that divides. Shapes 0,
+// 4 and 5 stay reachable through tsp_mlp_set_tiles.
+static const int kAuto[4] = {6, 1, 2, 3};
 
 int choose_gateup_cfg(int T, int d, int F, int P, int swiglu) {
     const int64_t ngu = swiglu ? 2LL * F : (int64_t)F;
@@ -1194,7 +1198,7 @@ int64_t down_split_bytes(int64_t T_max, int d, int P) {
 
 int choose_down_cfg(int T, int d, int F, int P) {
     int fallback = -1;
-    for (int c : kAutoDown) {
+    for (int c : kAuto) {
         if (d % kCfgs[c].bm || F % 64) continue;
         const int64_t wgs = (d / kCfgs[c].bm) * cdiv(T, kCfgs[c].bn) * choose_down_split(T, d, P, c);
         if (fallback < 0) fallback = c;
