@@ -87,6 +87,9 @@ def round_bf16(a) -> np.ndarray:
     return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
 
 
+round_bf16_fn = round_bf16
+
+
 def ring_order(P: int, r0: int = 0) -> list:
     """Rotated ring order: at step k the rank holds shard (r0 + k) mod P."""
     return [(r0 + k) % P for k in range(P)]
@@ -178,6 +181,147 @@ def tsp_simulate(X_full, w_gate, w_up, w_down, P: int, act: str = "swiglu",
         outs.append(mlp_forward(X_full[r * n:(r + 1) * n], w_gate, w_up, w_down, P,
                                 ring_order(P, (r + r0) % P), act))
     return np.concatenate(outs, axis=0)
+
+
+# ---------------------------------------------------------------- backward
+#
+# The pages name the backward pass only as the other half of a training step
+# ("Tensor Parallelism: Splitting the Math", the paragraph after the
+# walk-through: the split synchronises in the forward and in the backward
+# pass; "Folding Tensor and Sequence Parallelism ...", Abstract: the method is
+# for training). Reading taken (listed in the design doc): the backward of one
+# rank's block is the exact gradient of the forward above for a loss whose
+# gradient with respect to Y is dY. The rank visits the shards in the same ring
+# order; for shard s it forms that shard's part of dX (added into a local
+# accumulator, as Y is in the forward) and the full gradient of shard s's
+# weight blocks (columns [s*F, (s+1)*F) of the gate and up matrices, the same
+# rows of the down matrix), which go back to the shard's owner. Everything is
+# the chain rule applied to shard_hidden / shard_partial; numpy's matmul is the
+# only library step.
+
+
+def silu_grad(g: np.ndarray) -> np.ndarray:
+    """d SiLU / dg = sigma(g) (1 + g (1 - sigma(g))), sigma(g) = 1 / (1 + e^-g).
+
+    For very negative g, e^-g overflows, sigma is 0 and so is the derivative.
+    """
+    g = f64(g)
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-g))
+    return sig * (1.0 + g * (1.0 - sig))
+
+
+def gelu_tanh_grad(u: np.ndarray) -> np.ndarray:
+    """d/du of 0.5 u (1 + tanh(z)), z = sqrt(2/pi) (u + 0.044715 u^3):
+    0.5 (1 + tanh z) + 0.5 u (1 - tanh^2 z) sqrt(2/pi) (1 + 3 * 0.044715 u^2)."""
+    u = f64(u)
+    th = np.tanh(SQRT_2_OVER_PI * (u + GELU_TANH_CUBIC * u * u * u))
+    return 0.5 * (1.0 + th) + 0.5 * u * (1.0 - th * th) * SQRT_2_OVER_PI * (1.0 + 3.0 * GELU_TANH_CUBIC * u * u)
+
+
+def shard_backward(X, w_gate, w_up, w_down, dY, s: int, F: int, act: str,
+                   round_bf16: bool = False):
+    """Gradients from shard s: (part of dX, dWg block, dWu block, dWd block).
+
+    With G = X.Wg_s, U = X.Wu_s (or U = X.A_s), H = act(G, U), Y_s = H.Wd_s:
+    dH = dY.Wd_s^T; SwiGLU: dG = dH * U * SiLU'(G), dU = dH * SiLU(G); GeLU:
+    dU = dH * GeLU'(U); dX_s = dG.Wg_s^T + dU.Wu_s^T; dWg_s = X^T.dG,
+    dWu_s = X^T.dU, dWd_s = H^T.dY. ``round_bf16`` (diagnostic only) rounds
+    dG, dU and H to bfloat16 before the products that consume them, as the
+    bf16 kernels store them.
+    """
+    X, dY = f64(X), f64(dY)
+    cols = slice(s * F, (s + 1) * F)
+    wu = f64(w_up[:, cols])
+    wd = f64(w_down[cols, :])
+    u = X @ wu
+    dH = dY @ wd.T
+    rb = round_bf16_fn if round_bf16 else (lambda a: a)
+    if act == "swiglu":
+        wg = f64(w_gate[:, cols])
+        g = X @ wg
+        sg = silu(g)
+        h = rb(sg * u)
+        dG = rb(dH * u * silu_grad(g))
+        dU = rb(dH * sg)
+        dX = dG @ wg.T + dU @ wu.T
+        dWg = X.T @ dG
+    elif act == "gelu_tanh":
+        h = rb(gelu_tanh(u))
+        dU = rb(dH * gelu_tanh_grad(u))
+        dX = dU @ wu.T
+        dWg = None
+    else:
+        raise ValueError(f"unknown activation {act!r}")
+    return dX, dWg, X.T @ dU, h.T @ dY
+
+
+def mlp_backward(X, w_gate, w_up, w_down, dY, P: int, order: Optional[Sequence[int]] = None,
+                 act: str = "swiglu", round_bf16: bool = False) -> dict:
+    """One rank's TSP gated-MLP backward in float64.
+
+    Returns {"dX": T x d, "dW_gate": d x f (None for gelu_tanh), "dW_up": d x f,
+    "dW_down": f x d}. Ring step k visits shard order[k]; its dX part is added
+    into the local accumulator and its weight-gradient blocks are stored at the
+    shard's own columns / rows.
+    """
+    X, dY = f64(X), f64(dY)
+    T, d = X.shape
+    f = w_up.shape[1]
+    if dY.shape != (T, d) or w_up.shape[0] != d or w_down.shape != (f, d):
+        raise ValueError("shape mismatch")
+    if act == "swiglu" and (w_gate is None or w_gate.shape != (d, f)):
+        raise ValueError("swiglu needs a d x f gate matrix")
+    if P < 1 or f % P:
+        raise ValueError(f"P={P} must divide f={f}")
+    F = f // P
+    order = _check_order(ring_order(P) if order is None else order, P)
+    dX = np.zeros((T, d))
+    dWg = np.zeros((d, f)) if act == "swiglu" else None
+    dWu = np.zeros((d, f))
+    dWd = np.zeros((f, d))
+    for s in order:
+        cols = slice(s * F, (s + 1) * F)
+        px, pg, pu, pd = shard_backward(X, w_gate, w_up, w_down, dY, s, F, act, round_bf16)
+        dX += px
+        if pg is not None:
+            dWg[:, cols] = pg
+        dWu[:, cols] = pu
+        dWd[cols, :] = pd
+    return {"dX": dX, "dW_gate": dWg, "dW_up": dWu, "dW_down": dWd}
+
+
+def mlp_backward_columns(X, w_gate, w_up, w_down, dY, cols, act: str = "swiglu") -> dict:
+    """Weight gradients restricted to hidden columns ``cols`` (any subset of
+    0..f-1): dW_gate[:, cols], dW_up[:, cols], dW_down[cols, :]. Each hidden
+    column's gradients depend only on that column (every token row is
+    needed), so large shapes can be checked on sampled columns. Same formulas
+    as shard_backward, evaluated column by column block."""
+    X, dY = f64(X), f64(dY)
+    cols = np.asarray(cols)
+    wu = f64(w_up[:, cols])
+    wd = f64(w_down[cols, :])
+    u = X @ wu
+    dH = dY @ wd.T
+    if act == "swiglu":
+        g = X @ f64(w_gate[:, cols])
+        sg = silu(g)
+        h = sg * u
+        dG = dH * u * silu_grad(g)
+        dU = dH * sg
+        dWg = X.T @ dG
+    else:
+        h = gelu_tanh(u)
+        dU = dH * gelu_tanh_grad(u)
+        dWg = None
+    return {"dW_gate": dWg, "dW_up": X.T @ dU, "dW_down": h.T @ dY}
+
+
+def backward_flops(T: int, d: int, f: int, act: str) -> int:
+    """GEMM flops of one backward's gradients (2 per multiply-add): dH, then
+    dX, dW of the first matrices (two each for SwiGLU), dW of the down matrix.
+    A recomputation of the forward's hidden activations is not counted."""
+    return 2 * (6 if act == "swiglu" else 4) * T * d * f
 
 
 def flops(T: int, d: int, f: int, act: str) -> int:
