@@ -6,6 +6,21 @@
 
 namespace tsp {
 
+#define TSP_LDS __attribute__((address_space(3)))
+
+// s_waitcnt lgkmcnt(0): every LDS access of this wave has completed.
+__device__ __forceinline__ void lgkm_zero() {
+    __builtin_amdgcn_s_waitcnt((15 & 15) | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+// Workgroup barrier that orders LDS traffic without draining the global
+// loads still in flight for later stages (__syncthreads would wait for them).
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 

@@ -32,10 +32,10 @@
 // on every large-T workload, shape 5 next.
 #include "common.h"
 #include "launch.h"
+#include "w16.h"
 
 namespace tsp {
 
-#define TSP_LDS __attribute__((address_space(3)))
 
 template <int BM_, int BN_, int WM_, int WN_>
 struct TileCfg {
@@ -128,17 +128,6 @@ __device__ __forceinline__ void vmcnt_le(int n) {
     else __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
 }
 
-__device__ __forceinline__ void lgkm_zero() {
-    __builtin_amdgcn_s_waitcnt((15 & 15) | (7 << 4) | (0 << 8) | (3 << 14));
-}
-
-// Workgroup barrier that orders LDS traffic without draining the global
-// loads still in flight for later stages (__syncthreads would wait for them).
-__device__ __forceinline__ void stage_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
 template <class C>
 __device__ __forceinline__ void read_frags(const uint16_t* lds_stage, bf16x8 (&af)[2][C::TM],
@@ -582,17 +571,7 @@ constexpr int A_BLK = BM / 16, B_BLK = BN / 16;         // 1 KiB blocks per 32-w
 constexpr int LOADS = (A_BLK + B_BLK) / NW;
 constexpr int STAGE = (A_BLK + B_BLK) * 512;
 constexpr int NS = 5;                                   // LDS ring depth: 5 x 32 KiB = all 160 KiB
-// Fourth word of a raw (untyped, unswizzled) buffer resource on this GPU
-// family: 32-bit data format, no index stride.
-constexpr int kRawBufferWord3 = 0x00020000;
-
-// LDS slot of token r's 8-index chunk c in a B block. The 16x16x32 B
-// fragment read has lane l take token l % 16, chunk l / 16; with this XOR
-// (on r / 2) that read runs without LDS bank conflicts (measured with
-// SQ_LDS_BANK_CONFLICT; the tok_slot swizzle on r / 4 that suits the
-// 32x32x16 read costs this one a 2-way conflict). Each group of 4 lanes
-// still loads the 64 contiguous bytes of one token row.
-__device__ __forceinline__ int b_slot(int r, int c) { return 4 * r + (c ^ ((r >> 1) & 3)); }
+// B blocks use the conflict-free slot swizzle b_slot (w16.h).
 
 // One stage's global-to-LDS loads for this wave. BUF selects buffer loads
 // (buffer_load_dwordx4 ... lds: 128-bit resource + 32-bit per-lane offset)
@@ -815,220 +794,16 @@ __global__ __launch_bounds__(512) void down_pp16(Bf16Args a, int n_ft, int n_tt,
 }
 
 // ------------------------------------------------------------------ shape 6
-// 256 x 256 tile, 4 waves (one per SIMD) as 2 x 2, each wave a 128 x 128
-// piece held in 64 16x16 fp32 accumulators (all 256 accumulation registers),
-// 16x16x32 MFMAs, global-to-LDS loads into the same 5-stage ring as shape 5.
-// A wave reads 16 fragments per 64 MFMAs (shape 5's 64 x 128 wave pieces:
-// 12 per 32), so LDS read traffic per flop is two thirds of shape 5's.
-//
-// The first reduction step starts every accumulator from the constant 0
-// (MFMA source C = 0) instead of adding to zero-initialised registers: with
-// that form the compiler keeps each accumulator in one register across the
-// loop (with zero-initialised registers it copies accumulators between
-// registers on every trip).
+// The pipeline of w16.h with the forward's operands (PackedSrc).
 //
 // Measured (Llama-3-8B shape, same box): gate/up ~4 % and down ~8 % faster
 // than shape 5, so shape 6 is the automatic choice for both. Taking the
 // global-to-LDS loads out (a timing copy, not kept) makes either kernel ~25 %
 // faster: issuing them, not LDS reads or barriers, is what keeps the matrix
 // pipe below full rate, and how far apart they are issued matters (see
-// step). Staging one or both operands through registers, and a persistent
-// grid that streams the next tile's first stages during the epilogue, each
-// measured slower.
-namespace w16 {
-
-constexpr int BM = 256, BN = 256, NW = 4, WN = 2;
-constexpr int TM = 8, TN = 8;                           // 16-row / 16-token MFMA blocks per wave
-constexpr int A_BLK = BM / 16, B_BLK = BN / 16;         // 1 KiB blocks per 32-wide stage
-constexpr int LA = A_BLK / NW, LB = B_BLK / NW;         // blocks each wave loads per stage
-constexpr int LOADS = LA + LB;
-constexpr int STAGE = (A_BLK + B_BLK) * 512;
-constexpr int NS = 5;                                   // 5 x 32 KiB = all 160 KiB of LDS
-static_assert(NS * STAGE * 2 <= 160 * 1024, "LDS");
-static_assert((NS - 1) * LOADS <= 63, "vmcnt range");
-
-#define TSP_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-
-// Load r of this wave's LOADS global-to-LDS loads of one stage: A blocks
-// w, w + 4, .. first, then B blocks likewise (same LDS layout and B swizzle
-// as shape 5). BUF: buffer loads with 32-bit offsets (see shape 5).
-template <bool BUF>
-__device__ __forceinline__ void issue_one(int r, uint16_t* lds_stage, const uint16_t* __restrict__ a_base,
-                                          int64_t a_rs, const uint16_t* __restrict__ b_src, int ldb,
-                                          int64_t b_koff, int t0, int T, int w, int lane) {
-    if (r < LA) {
-        const int b = r * NW + w;
-        TSP_LDS void* dst = (TSP_LDS void*)(lds_stage + b * 512);
-        const int64_t off = (b >> 1) * a_rs + (b & 1) * 512 + lane * 8;
-        if constexpr (BUF) {
-            const __amdgpu_buffer_rsrc_t rs =
-                __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, 0x7fffffff, pp16::kRawBufferWord3);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (int)(off * 2), 0, 0, 0);
-        } else {
-            __builtin_amdgcn_global_load_lds(a_base + off, dst, 16, 0, 0);
-        }
-    } else {
-        const int bb = (r - LA) * NW + w;
-        const int rr = lane >> 2;
-        const int c = (lane & 3) ^ ((rr >> 1) & 3);     // slot = lane = pp16::b_slot(rr, c)
-        TSP_LDS void* dst = (TSP_LDS void*)(lds_stage + (A_BLK + bb) * 512);
-        const int tok = min(t0 + bb * 16 + rr, T - 1);
-        const int64_t off = (int64_t)tok * ldb + c * 8;
-        if constexpr (BUF) {
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                (void*)(b_src + b_koff), (short)0, 0x7fffffff, pp16::kRawBufferWord3);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (int)(off * 2), 0, 0, 0);
-        } else {
-            __builtin_amdgcn_global_load_lds(b_src + b_koff + off, dst, 16, 0, 0);
-        }
-    }
-}
-
-// Fragment q of a stage for this wave: A fragments 0 .. TM-1 (16 rows x 32
-// reduction indices: lane l takes row l % 16, chunk l / 16), then the B
-// fragments (16 tokens x 32 indices).
-__device__ __forceinline__ void read_one(int q, const uint16_t* lds_stage, bf16x8 (&af)[TM], bf16x8 (&bv)[TN],
-                                         int wm, int wn, int lane) {
-    const int r = lane & 15, c = lane >> 4;
-    if (q < TM) {
-        const bf16x8* as = reinterpret_cast<const bf16x8*>(lds_stage);
-        const int ib = wm * TM + q;                     // 16-row block: rows 16 (ib % 2) + r of 32-row block ib / 2
-        af[q] = as[((ib >> 1) * 2 + (c >> 1)) * 64 + (c & 1) * 32 + (ib & 1) * 16 + r];
-    } else {
-        const bf16x8* bs = reinterpret_cast<const bf16x8*>(lds_stage + A_BLK * 512);
-        bv[q - TM] = bs[(wn * TN + q - TM) * 64 + pp16::b_slot(r, c)];
-    }
-}
-
-// Load cursor: the next stage to load (clamped to the last one), advanced
-// without divisions. spp > 0 (down product): the reduction walks shard
-// records, spp steps each, a_rec elements apart.
-struct Cursor {
-    const uint16_t* a;                                  // A slab of the stage
-    int tl, ls;                                         // stage index, step inside the record
-    int ksteps, spp;
-    int64_t a_rec;
-    __device__ int64_t bk() const { return (int64_t)tl * 32; }
-    __device__ void advance() {
-        const bool adv = tl + 1 < ksteps;
-        const bool wrap = spp > 0 && ls + 1 == spp;
-        a += adv ? (wrap ? a_rec - (int64_t)(spp - 1) * 1024 : (int64_t)1024) : (int64_t)0;
-        ls = adv ? (wrap ? 0 : ls + 1) : ls;
-        tl += adv ? 1 : 0;
-    }
-};
-
-__device__ __forceinline__ int next_buf(int off) { return off == (NS - 1) * STAGE ? 0 : off + STAGE; }
-
-// Step t. The barrier makes every wave's share of stage t + 1 visible and
-// ends every wave's fragment reads of stage t (issued in step t - 1), so
-// stage t's buffer takes the loads of stage t + NS. The wave then reads stage
-// t + 1's fragments into the other register set while its MFMAs run on stage
-// t's, and before the next barrier waits for those reads and for its own
-// loads of stage t + 2. Every step issues one stage (past the end, the last
-// stage again, into a buffer nobody reads), so that wait is always "at most 3
-// stages newer". FIRST: the accumulators start from 0. LAST: MFMAs only.
-//
-// With one wave per SIMD nothing else feeds the matrix pipe while this wave
-// issues other work, so scheduling fences fix the order: three MFMAs right
-// after the barrier, then eight groups of one load, two fragment reads and
-// seven MFMAs (a load right after another costs the matrix pipe far more
-// than one that follows a few MFMAs: 3-5 % of the kernel time here), and the
-// scalar bookkeeping for the next step spread over the last five MFMAs.
-template <bool BUF, bool FIRST, bool LAST>
-__device__ __forceinline__ void step(int& ld_ref, int& rd_ref, Cursor& cur, uint16_t* lds, f32x4 (&acc)[TM][TN],
-                                     const bf16x8 (&ca)[TM], const bf16x8 (&cb)[TN], bf16x8 (&na)[TM],
-                                     bf16x8 (&nb)[TN], int64_t a_rs, const uint16_t* b_src, int ldb, int t0, int T,
-                                     int w, int wm, int wn, int lane) {
-    constexpr int LEAD = 3, GROUP = 7;
-    constexpr int TAIL = TM * TN - LEAD - LOADS * GROUP;
-    static_assert(LOADS == 8 && TM + TN == 2 * LOADS && TAIL == 5, "schedule");
-    auto mf = [&](int m) {
-        const int i = m / TN, j = m % TN;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], FIRST ? f32x4{0.f, 0.f, 0.f, 0.f}
-                                                                                : acc[i][j], 0, 0, 0);
-    };
-    if constexpr (LAST) {
-#pragma unroll
-        for (int m = 0; m < TM * TN; ++m) mf(m);
-        return;
-    }
-    const int ld_off = ld_ref, rd_off = rd_ref;
-    const uint16_t* ap = cur.a;
-    const int64_t bk = cur.bk();
-    stage_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0; m < LEAD; ++m) mf(m);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int g = 0; g < LOADS; ++g) {
-        const int m0 = LEAD + GROUP * g;
-        issue_one<BUF>(g, lds + ld_off, ap, a_rs, b_src, ldb, bk, t0, T, w, lane);
-        mf(m0);
-        mf(m0 + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        read_one(2 * g, lds + rd_off, na, nb, wm, wn, lane);
-        mf(m0 + 2);
-        mf(m0 + 3);
-        __builtin_amdgcn_sched_barrier(0);
-        read_one(2 * g + 1, lds + rd_off, na, nb, wm, wn, lane);
-        mf(m0 + 4);
-        mf(m0 + 5);
-        mf(m0 + 6);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    cur.advance();
-    ld_ref = rd_off;
-    rd_ref = next_buf(rd_off);
-#pragma unroll
-    for (int m = TM * TN - TAIL; m < TM * TN; ++m) mf(m);
-#pragma unroll
-    for (int k = 0; k < TAIL; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x006, 4, 0);   // VALU / SALU
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    TSP_VMCNT(3 * LOADS);                               // own loads of stage t + 2 landed
-    lgkm_zero();                                        // stage t + 1's fragments in registers
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// The reduction over ksteps stages (even, >= 2: d and F are multiples of 64).
-template <bool BUF>
-__device__ __forceinline__ void mainloop(uint16_t* lds, f32x4 (&acc)[TM][TN], int ksteps, int64_t a_rs,
-                                         const uint16_t* b_src, int ldb, int t0, int T,
-                                         const uint16_t* a_tile, int64_t a_rec, int spp) {
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = w / WN, wn = w % WN;
-    Cursor cur{a_tile, 0, 0, ksteps, spp, a_rec};
-    for (int t = 0; t < NS; ++t) {
-#pragma unroll
-        for (int r = 0; r < LOADS; ++r)
-            issue_one<BUF>(r, lds + t * STAGE, cur.a, a_rs, b_src, ldb, cur.bk(), t0, T, w, lane);
-        cur.advance();
-    }
-    bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
-    TSP_VMCNT((NS - 1) * LOADS);                        // own loads of stage 0 landed
-    stage_barrier();
-#pragma unroll
-    for (int q = 0; q < TM + TN; ++q) read_one(q, lds, a0, b0, wm, wn, lane);
-    TSP_VMCNT((NS - 2) * LOADS);                        // own loads of stage 1 landed
-    lgkm_zero();
-    __builtin_amdgcn_sched_barrier(0);
-    int ld = 0, rd = STAGE;                             // buffers of stages t and t + 1
-    step<BUF, true, false>(ld, rd, cur, lds, acc, a0, b0, a1, b1, a_rs, b_src, ldb, t0, T, w, wm, wn, lane);
-    for (int t = 1; t + 2 < ksteps; t += 2) {
-        step<BUF, false, false>(ld, rd, cur, lds, acc, a1, b1, a0, b0, a_rs, b_src, ldb, t0, T, w, wm, wn, lane);
-        step<BUF, false, false>(ld, rd, cur, lds, acc, a0, b0, a1, b1, a_rs, b_src, ldb, t0, T, w, wm, wn, lane);
-    }
-    step<BUF, false, true>(ld, rd, cur, lds, acc, a1, b1, a0, b0, a_rs, b_src, ldb, t0, T, w, wm, wn, lane);
-    TSP_VMCNT(0);                                       // no load into LDS outlives the workgroup
-}
-#undef TSP_VMCNT
-
-}  // namespace w16
+// w16::step). Staging one or both operands through registers, and a
+// persistent grid that streams the next tile's first stages during the
+// epilogue, each measured slower.
 
 template <int ACT, bool BUF>
 __global__ __launch_bounds__(256) void gateup_w16(Bf16Args a, int n_ft_shard, int n_tt) {
@@ -1042,11 +817,13 @@ __global__ __launch_bounds__(256) void gateup_w16(Bf16Args a, int n_ft_shard, in
     const int64_t a_rs = (int64_t)(a.d >> 4) * 512;
     const uint16_t* a_tile = a.packed + (int64_t)s * a.shard_elems + (int64_t)(ftile * (BM / 32)) * a_rs;
     const int t0 = ttile * BN;
-    f32x4 acc[TM][TN];
-    w16::mainloop<BUF>(lds, acc, a.d >> 5, a_rs, a.x, a.d, t0, a.T, a_tile, 0, 0);
-
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w / WN, wn = w % WN;
+    PackedSrc<BUF> src{a_tile, 0, 0, a.d >> 5, 0, 0, a_rs, a.x, a.d, t0, a.T,
+                       __builtin_amdgcn_readfirstlane(w), wm, wn, lane};
+    f32x4 acc[TM][TN];
+    w16::mainloop(lds, acc, a.d >> 5, src);
+
     const int fsub = 4 * (lane >> 4);
     if constexpr (ACT == 1) {
         // the wave's 128 rows are two (32 gate, 32 up) row pairs: 16-row
@@ -1101,11 +878,13 @@ __global__ __launch_bounds__(256) void down_w16(Bf16Args a, int n_ft, int n_tt, 
     const uint16_t* h_g = a.h + (int64_t)(g * steps_per_group) * a.F;
     float* y = split > 1 ? a.part + (int64_t)g * a.T * a.d : a.y;
     const int t0 = ttile * BN;
-    f32x4 acc[TM][TN];
-    w16::mainloop<false>(lds, acc, steps_per_group * spp, a_rs, h_g, a.f, t0, a.T, a_ft, a.shard_elems, spp);
-
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w / WN, wn = w % WN;
+    PackedSrc<false> src{a_ft, 0, 0, steps_per_group * spp, spp, a.shard_elems, a_rs, h_g, a.f, t0, a.T,
+                         __builtin_amdgcn_readfirstlane(w), wm, wn, lane};
+    f32x4 acc[TM][TN];
+    w16::mainloop(lds, acc, steps_per_group * spp, src);
+
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int n = ftile * BM + (wm * TM + i) * 16 + 4 * (lane >> 4);
