@@ -121,6 +121,37 @@ tsp_status_t tsp_mlp_create(tsp_mlp_t* out, int64_t T_max, int64_t d, int64_t f,
 tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y,
                              hipStream_t stream);
 
+/*
+ * Backward of the block for an output gradient dY: the gradients of the
+ * forward ("Folding Tensor and Sequence Parallelism ...", Abstract: the method
+ * is for training; "Tensor Parallelism: Splitting the Math", the paragraph
+ * after the walk-through: the split's synchronisation recurs in the backward
+ * pass). For each shard s, in the handle's ring order:
+ *   dH_s = dY . Wd_s^T; SwiGLU: dG_s = dH_s * U_s * SiLU'(G_s),
+ *   dU_s = dH_s * SiLU(G_s); GeLU: dU_s = dH_s * GeLU'(U_s);
+ *   dX += dG_s . Wg_s^T + dU_s . Wu_s^T  (accumulated locally, fp32);
+ *   dW_gate[:, s] = X^T . dG_s, dW_up[:, s] = X^T . dU_s,
+ *   dW_down[s, :] = H_s^T . dY           (each shard's own blocks),
+ * with G_s, U_s, H_s recomputed from X and the handle's packed weights.
+ * bf16 handles only (TSP_ERR_UNSUPPORTED for fp32), and d % 256 == 0 and
+ * F % 256 == 0 (TSP_ERR_UNSUPPORTED otherwise).
+ * X, dY: device, T x d row-major bf16. w_gate, w_up (d x f) and w_down
+ * (f x d): device, row-major bf16, the same values the handle was created
+ * with (w_gate NULL for GeLU); they are read for dH and dX. Outputs, device,
+ * fp32, overwritten: dX T x d; dW_gate, dW_up d x f (dW_gate NULL for GeLU);
+ * dW_down f x d, the weights' own layouts. All pointers 16-byte aligned;
+ * outputs must not overlap each other or the inputs. 1 <= T <= T_max
+ * (T == 0 is a no-op). The first call allocates a backward workspace sized
+ * for T_max (TSP_ERR_OOM if that fails); it is freed by tsp_mlp_destroy.
+ * Asynchronous like forward, on `stream` (NULL: the handle's stream); it
+ * shares nothing with a forward's workspace, but one backward at a time per
+ * handle.
+ */
+tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void* dY,
+                              const void* w_gate, const void* w_up, const void* w_down,
+                              float* dX, float* dW_gate, float* dW_up, float* dW_down,
+                              hipStream_t stream);
+
 /* Synchronise the handle's stream and free everything it owns. NULL is a no-op. */
 tsp_status_t tsp_mlp_destroy(tsp_mlp_t h);
 
@@ -136,9 +167,9 @@ tsp_status_t tsp_mlp_set_path(tsp_mlp_t h, int32_t path);
  * 3 = 64 x 128, 4 = 256 x 256 with one wave per SIMD, 5 = 256 x 256 with
  * 16x16x32 MFMAs over global-to-LDS loads, two wave groups in ping-pong,
  * 6 = the same tile with four waves of 128 x 128 (the automatic choice at
- * large T). Shapes 5 and 6 compute bitwise identical results. With down shape 5 or 6 and fewer than 256
- * output tiles, the ring is split into groups of consecutive shards whose
- * fp32 partials are added in ring order.
+ * large T). Shapes 5 and 6 compute bitwise identical results. With down
+ * shape 5 or 6 and fewer than 256 output tiles, the ring is split into
+ * groups of consecutive shards whose fp32 partials are added in ring order.
  * TSP_ERR_UNSUPPORTED if the shape does not divide the shard's
  * packed width (gate/up) or d (down), or for an fp32 handle. */
 tsp_status_t tsp_mlp_set_tiles(tsp_mlp_t h, int32_t gateup_tile, int32_t down_tile);

@@ -24,6 +24,7 @@ SIGNATURES = {
     "tsp_mlp_create": (_i32, [ctypes.POINTER(_vp), _i64, _i64, _i64, _i32, _i32, _i32,
                               ctypes.POINTER(_i32), _vp, _vp, _vp, _vp]),
     "tsp_mlp_forward": (_i32, [_vp, _i64, _vp, _vp, _vp]),
+    "tsp_mlp_backward": (_i32, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "tsp_mlp_destroy": (_i32, [_vp]),
     "tsp_mlp_set_path": (_i32, [_vp, _i32]),
     "tsp_mlp_set_tiles": (_i32, [_vp, _i32, _i32]),
@@ -153,6 +154,26 @@ class TspMLP:
         return y
 
     __call__ = forward
+
+    def backward(self, x, dy, w_gate, w_up, w_down, stream=None):
+        """Gradients for output gradient dy: {"dX", "dW_gate", "dW_up",
+        "dW_down"} (fp32 CUDA tensors; dW_gate is None for GeLU). w_* are the
+        weights the handle was created with (bf16, as passed to create)."""
+        import torch
+        T = x.shape[0]
+        for t in (x, dy):
+            if t.dtype != self.tdtype or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != (T, self.d):
+                raise ValueError("x and dy must be contiguous CUDA tensors T x d of the handle's dtype")
+        dev = x.device
+        dX = torch.empty(T, self.d, dtype=torch.float32, device=dev)
+        dWg = None if w_gate is None else torch.empty(self.d, self.f, dtype=torch.float32, device=dev)
+        dWu = torch.empty(self.d, self.f, dtype=torch.float32, device=dev)
+        dWd = torch.empty(self.f, self.d, dtype=torch.float32, device=dev)
+        ptr = lambda t: None if t is None else t.data_ptr()
+        check(lib().tsp_mlp_backward(self.handle, T, x.data_ptr(), dy.data_ptr(), ptr(w_gate), w_up.data_ptr(),
+                                     w_down.data_ptr(), dX.data_ptr(), ptr(dWg), dWu.data_ptr(), dWd.data_ptr(),
+                                     _stream_ptr(stream)))
+        return {"dX": dX, "dW_gate": dWg, "dW_up": dWu, "dW_down": dWd}
 
     def sizes(self):
         p, w = _i64(), _i64()

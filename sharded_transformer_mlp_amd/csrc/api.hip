@@ -59,6 +59,8 @@ struct tsp_mlp {
     int64_t packed_bytes = 0, shard_elems = 0, down_off = 0;
     void* work = nullptr;
     int64_t work_bytes = 0;
+    void* bwd = nullptr;                       // backward workspace (first backward call)
+    int64_t bwd_bytes = 0;
     int64_t part_off = 0;                      // byte offset of the down-split partials in work
     int32_t path = TSP_PATH_AUTO;
     int32_t cfg_gateup = -1, cfg_down = -1;   // tiled shapes; -1 = chosen per forward
@@ -133,6 +135,7 @@ void release(tsp_mlp* h) {
     if (h->order_dev) (void)hipFree(h->order_dev);
     if (h->packed) (void)hipFree(h->packed);
     if (h->work) (void)hipFree(h->work);
+    if (h->bwd) (void)hipFree(h->bwd);
     delete h;
 }
 
@@ -334,6 +337,158 @@ tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y, hi
     s = timed_launch(h, "gateup_f32", st, [&] { return tsp::launch_gateup_f32(a, st); });
     if (s != TSP_OK) return s;
     return timed_launch(h, "down_f32", st, [&] { return tsp::launch_down_f32(a, st); });
+}
+
+namespace {
+
+// Backward workspace, regions in bytes for T_max tokens (each 256-aligned):
+// transposed X and dY (d x Tp), dH (T x f fp32), dG, dU, H (T x f bf16) and
+// their transposes (f x Tp), Tp = T_max rounded up to 64.
+struct BwdLayout {
+    int64_t xt, dyt, dh, dg, du, hb, dgt, dut, ht, total;
+};
+
+BwdLayout bwd_layout(int64_t T_max, int64_t d, int64_t f) {
+    auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+    const int64_t Tp = (T_max + 63) / 64 * 64;
+    BwdLayout L;
+    int64_t o = 0;
+    L.xt = o; o += up(d * Tp * 2);
+    L.dyt = o; o += up(d * Tp * 2);
+    L.dh = o; o += up(T_max * f * 4);
+    L.dg = o; o += up(T_max * f * 2);
+    L.du = o; o += up(T_max * f * 2);
+    L.hb = o; o += up(T_max * f * 2);
+    L.dgt = o; o += up(f * Tp * 2);
+    L.dut = o; o += up(f * Tp * 2);
+    L.ht = o; o += up(f * Tp * 2);
+    L.total = o;
+    return L;
+}
+
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+}  // namespace
+
+tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void* dY, const void* w_gate,
+                              const void* w_up, const void* w_down, float* dX, float* dW_gate, float* dW_up,
+                              float* dW_down, hipStream_t stream) {
+    if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
+    if (T < 0 || T > h->T_max) return fail(TSP_ERR_INVALID_ARG, "T=%lld out of [0, T_max=%lld]", (long long)T, (long long)h->T_max);
+    if (h->dtype != TSP_DTYPE_BF16) return fail(TSP_ERR_UNSUPPORTED, "the backward is bf16 only");
+    if (h->d % 256 || h->F % 256) return fail(TSP_ERR_UNSUPPORTED, "the backward needs d %% 256 == 0 and F %% 256 == 0");
+    if (T == 0) return TSP_OK;
+    const bool swiglu = h->act == TSP_ACT_SWIGLU;
+    if (!X || !dY || !w_up || !w_down || !dX || !dW_up || !dW_down)
+        return fail(TSP_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (swiglu != (w_gate != nullptr) || swiglu != (dW_gate != nullptr))
+        return fail(TSP_ERR_INVALID_ARG, "w_gate and dW_gate are required for SwiGLU and must be NULL for GeLU");
+    const void* ptrs[] = {X, dY, w_gate, w_up, w_down, dX, dW_gate, dW_up, dW_down};
+    for (const void* q : ptrs)
+        if (q && !aligned16(q)) return fail(TSP_ERR_INVALID_ARG, "every pointer must be 16-byte aligned");
+    const int64_t d = h->d, f = h->f;
+    struct Span { const void* p; int64_t n; };
+    const Span outs[] = {{dX, T * d * 4}, {dW_gate, d * f * 4}, {dW_up, d * f * 4}, {dW_down, f * d * 4}};
+    const Span ins[] = {{X, T * d * 2}, {dY, T * d * 2}, {w_gate, d * f * 2}, {w_up, d * f * 2}, {w_down, f * d * 2}};
+    for (int i = 0; i < 4; ++i) {
+        if (!outs[i].p) continue;
+        for (int j = i + 1; j < 4; ++j)
+            if (outs[j].p && overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
+                return fail(TSP_ERR_INVALID_ARG, "gradient outputs overlap each other");
+        for (const Span& in : ins)
+            if (in.p && overlaps(outs[i].p, outs[i].n, in.p, in.n))
+                return fail(TSP_ERR_INVALID_ARG, "a gradient output overlaps an input");
+    }
+    hipStream_t st = stream ? stream : h->stream;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return fail(TSP_ERR_HIP, "cannot select the handle's device");
+    const BwdLayout L = bwd_layout(h->T_max, d, f);
+    if (!h->bwd) {
+        hipError_t e = hipMalloc(&h->bwd, (size_t)L.total);
+        if (e != hipSuccess) {
+            h->bwd = nullptr;
+            (void)hipGetLastError();
+            return fail(TSP_ERR_OOM, "backward workspace of %lld bytes: %s", (long long)L.total, hipGetErrorString(e));
+        }
+        h->bwd_bytes = L.total;
+    }
+    char* wsp = static_cast<char*>(h->bwd);
+    auto bf = [&](int64_t off) { return reinterpret_cast<uint16_t*>(wsp + off); };
+    uint16_t *xt = bf(L.xt), *dyt = bf(L.dyt), *dg = bf(L.dg), *du = bf(L.du), *hb = bf(L.hb);
+    uint16_t *dgt = bf(L.dgt), *dut = bf(L.dut), *ht = bf(L.ht);
+    float* dh = reinterpret_cast<float*>(wsp + L.dh);
+    const int Tp = (int)((T + 63) / 64 * 64);
+    const int F = (int)h->F, P = h->P;
+    const auto* x16 = static_cast<const uint16_t*>(X);
+    const auto* dy16 = static_cast<const uint16_t*>(dY);
+    const auto* wg16 = static_cast<const uint16_t*>(w_gate);
+    const auto* wu16 = static_cast<const uint16_t*>(w_up);
+    const auto* wd16 = static_cast<const uint16_t*>(w_down);
+
+    tsp_status_t s = timed_launch(h, "bwd_transpose", st, [&] {
+        hipError_t e = tsp::launch_transpose_bf16(x16, (int)T, (int)d, (int)d, xt, Tp, st);
+        return e != hipSuccess ? e : tsp::launch_transpose_bf16(dy16, (int)T, (int)d, (int)d, dyt, Tp, st);
+    });
+    if (s != TSP_OK) return s;
+    // dH[t][c] = sum_n dY[t][n] Wd[c][n], natural hidden columns
+    tsp::NtArgs p{};
+    p.a_base[0] = p.a_base[1] = wd16;
+    p.b_base[0] = p.b_base[1] = dy16;
+    p.lda = (int)d; p.ldb = (int)d; p.M = (int)f; p.N = (int)T;
+    p.spp = (int)(d / 32); p.nseg = 1; p.kinds = 1;
+    p.out = dh; p.ldc = f;
+    s = timed_launch(h, "bwd_dh", st, [&] { return tsp::launch_nt(p, st); });
+    if (s != TSP_OK) return s;
+    // recompute G, U (H) and form dG, dU, H in ring-ordered hidden columns
+    tsp::Bf16Args a{};
+    a.packed = static_cast<const uint16_t*>(h->packed);
+    a.x = x16;
+    a.shard_elems = h->shard_elems;
+    a.down_off = h->down_off;
+    a.T = (int)T; a.d = (int)d; a.f = (int)f; a.F = F; a.P = P;
+    a.swiglu = swiglu ? 1 : 0;
+    tsp::BwdArgs b{dh, dg, du, hb, h->order_dev};
+    s = timed_launch(h, "bwd_gateup", st, [&] { return tsp::launch_gateup_bwd(a, b, st); });
+    if (s != TSP_OK) return s;
+    s = timed_launch(h, "bwd_transpose", st, [&] {
+        hipError_t e = hipSuccess;
+        if (swiglu) e = tsp::launch_transpose_bf16(dg, (int)T, (int)f, (int)f, dgt, Tp, st);
+        if (e == hipSuccess) e = tsp::launch_transpose_bf16(du, (int)T, (int)f, (int)f, dut, Tp, st);
+        return e != hipSuccess ? e : tsp::launch_transpose_bf16(hb, (int)T, (int)f, (int)f, ht, Tp, st);
+    });
+    if (s != TSP_OK) return s;
+    // dX[t][i] = sum over ring steps k of dG_k[t] . Wg[i][order[k] F ..] + dU_k[t] . Wu[i][..]
+    tsp::NtArgs q{};
+    q.a_base[0] = swiglu ? wg16 : wu16;
+    q.a_base[1] = wu16;
+    q.b_base[0] = swiglu ? dg : du;
+    q.b_base[1] = du;
+    q.a_seg = F; q.b_seg = F; q.order = h->order_dev;
+    q.lda = (int)f; q.ldb = (int)f; q.M = (int)d; q.N = (int)T;
+    q.spp = F / 32; q.kinds = swiglu ? 2 : 1; q.nseg = P * q.kinds;
+    q.out = dX; q.ldc = d;
+    s = timed_launch(h, "bwd_dx", st, [&] { return tsp::launch_nt(q, st); });
+    if (s != TSP_OK) return s;
+    // weight gradients: reductions over the (zero-padded) token dimension
+    auto dw = [&](const uint16_t* at, const uint16_t* bt, int M, int N, float* out, int64_t ldc, int remap) {
+        tsp::NtArgs r{};
+        r.a_base[0] = r.a_base[1] = at;
+        r.b_base[0] = r.b_base[1] = bt;
+        r.lda = Tp; r.ldb = Tp; r.M = M; r.N = N;
+        r.spp = Tp / 32; r.nseg = 1; r.kinds = 1;
+        r.out = out; r.ldc = ldc; r.remap = remap; r.F = F; r.remap_order = h->order_dev;
+        return tsp::launch_nt(r, st);
+    };
+    s = timed_launch(h, "bwd_dw", st, [&] {
+        hipError_t e = hipSuccess;
+        if (swiglu) e = dw(dgt, xt, (int)f, (int)d, dW_gate, f, 1);       // dW_gate[i][c]
+        if (e == hipSuccess) e = dw(dut, xt, (int)f, (int)d, dW_up, f, 1);
+        return e != hipSuccess ? e : dw(dyt, ht, (int)d, (int)f, dW_down, d, 2);   // dW_down[c][n]
+    });
+    return s;
 }
 
 tsp_status_t tsp_mlp_destroy(tsp_mlp_t h) {

@@ -1,0 +1,257 @@
+// Backward pass of one rank's sharded gated MLP (gfx950).
+//
+// The gradients of the forward for an output gradient dY (the method's
+// training step: "Folding Tensor and Sequence Parallelism ...", Abstract;
+// "Tensor Parallelism: Splitting the Math", the paragraph after the
+// walk-through names the backward pass beside the forward). For each shard s,
+// visited in ring order like the forward:
+//   dH_s = dY . Wd_s^T
+//   SwiGLU: dG_s = dH_s * U_s * SiLU'(G_s), dU_s = dH_s * SiLU(G_s)
+//   GeLU:   dU_s = dH_s * GeLU'(U_s)
+//   dX  += dG_s . Wg_s^T + dU_s . Wu_s^T        (local accumulation, ring order)
+//   dWg_s = X^T . dG_s, dWu_s = X^T . dU_s, dWd_s = H_s^T . dY   (the shard's own blocks)
+// G_s, U_s and H_s are recomputed from X with the forward's gate/up kernel
+// and packed records (gateup_bwd_w16), whose epilogue turns them into dG, dU
+// and H. Every product runs on the shape-6 pipeline (w16.h); the backward's
+// products read both operands row-major with the reduction index contiguous
+// (RowSrc), so the token-reduced weight gradients read transposed copies of
+// X, dY, dG, dU and H made by transpose_bf16 (padded with zero tokens to a
+// multiple of 64).
+#include "common.h"
+#include "launch.h"
+#include "w16.h"
+
+namespace tsp {
+
+// ------------------------------------------------------------------ transpose
+// dst[c][r] = src[r][c] for r < R, 0 for R <= r < R_pad; 64 x 64 tiles through
+// LDS, each thread moving 16 elements (two 16-byte accesses) each way.
+__global__ __launch_bounds__(256) void transpose_bf16(const uint16_t* __restrict__ src, int R, int ld_src,
+                                                      uint16_t* __restrict__ dst, int ld_dst) {
+    __shared__ uint16_t tile[64][64 + 8];
+    const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+    const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
+    const int r = r0 + tr;
+    u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+    if (r < R) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(src + (int64_t)r * ld_src + c0 + tc);
+        v0 = p[0];
+        v1 = p[1];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        tile[tr][tc + 2 * e] = (uint16_t)(v0[e] & 0xffffu);
+        tile[tr][tc + 2 * e + 1] = (uint16_t)(v0[e] >> 16);
+        tile[tr][tc + 8 + 2 * e] = (uint16_t)(v1[e] & 0xffffu);
+        tile[tr][tc + 8 + 2 * e + 1] = (uint16_t)(v1[e] >> 16);
+    }
+    __syncthreads();
+    // thread: output row c0 + tr, tokens r0 + tc .. + 15
+    u32x4 o0, o1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        o0[e] = (uint32_t)tile[tc + 2 * e][tr] | ((uint32_t)tile[tc + 2 * e + 1][tr] << 16);
+        o1[e] = (uint32_t)tile[tc + 8 + 2 * e][tr] | ((uint32_t)tile[tc + 8 + 2 * e + 1][tr] << 16);
+    }
+    u32x4* q = reinterpret_cast<u32x4*>(dst + (int64_t)(c0 + tr) * ld_dst + r0 + tc);
+    q[0] = o0;
+    q[1] = o1;
+}
+
+// ------------------------------------------------------------------ NT product
+// C[n][m] = sum_k A[m][k] B[n][k] on the shape-6 pipeline, fp32 out:
+// out[row(n) * ldc + col(m)], n < N. remap 1: column m is a ring-ordered
+// hidden index (ring step m / F) stored at its shard's natural column
+// order[m / F] * F + m % F; remap 2: the same for the row n. F % 256 == 0, so
+// a 256-wide tile never straddles two shards and the remap is one offset per
+// tile.
+template <bool BUF>
+__global__ __launch_bounds__(256) void nt_w16(NtArgs p, int n_mt, int n_nt) {
+    using namespace w16;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
+    poison_lds(lds, sizeof(lds));
+    int ntile, mtile;
+    raster(xcd_remap(blockIdx.x, gridDim.x), n_mt, n_nt, ntile, mtile);
+    const int m0 = mtile * BM, n0 = ntile * BN;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w / WN, wn = w % WN;
+    RowSrc<BUF> src;
+    src.ls = 0;
+    src.j = 0;
+    src.spp = p.spp;
+    src.nseg = p.nseg;
+    src.kinds = p.kinds;
+    src.a_base0 = p.a_base[0];
+    src.a_base1 = p.a_base[1];
+    src.b_base0 = p.b_base[0];
+    src.b_base1 = p.b_base[1];
+    src.a_seg = p.a_seg;
+    src.b_seg = p.b_seg;
+    src.order = p.order;
+    src.lda = p.lda;
+    src.ldb = p.ldb;
+    src.m0 = m0;
+    src.n0 = n0;
+    src.last_m = p.M - 1;
+    src.last_n = p.N - 1;
+    src.w = __builtin_amdgcn_readfirstlane(w);
+    src.wm = wm;
+    src.wn = wn;
+    src.lane = lane;
+    src.seek(0);
+    f32x4 acc[TM][TN];
+    w16::mainloop(lds, acc, p.spp * p.nseg, src);
+
+    int64_t col0 = m0, row_shift = 0;
+    if (p.remap == 1) col0 = (int64_t)p.remap_order[m0 / p.F] * p.F + m0 % p.F;
+    if (p.remap == 2) row_shift = (int64_t)p.remap_order[n0 / p.F] * p.F + n0 % p.F - n0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int64_t col = col0 + (wm * TM + i) * 16 + 4 * (lane >> 4);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = n0 + (wn * TN + j) * 16 + (lane & 15);
+            if (n < p.N) {
+                const f32x4 v = acc[i][j];
+                *reinterpret_cast<float4*>(p.out + (n + row_shift) * p.ldc + col) = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ gate/up backward
+// The forward's gate/up product (packed records in ring order, shape 6), with
+// an epilogue that reads dH at the shard's natural hidden columns and writes
+// dG, dU and H (bf16, ring-ordered hidden columns like the forward's H).
+// SiLU'(g) = sigma (1 + g (1 - sigma)); with z2 = sqrt(8/pi) (u + 0.044715 u^3),
+// GeLU(u) = u sigma2 and GeLU'(u) = sigma2 (1 + u (1 - sigma2) dz2/du), where
+// sigma = 1 / (1 + e^-g) and sigma2 = 1 / (1 + e^-z2) (the tanh form,
+// 1 + tanh(z2 / 2) = 2 sigma2). Reciprocals use v_rcp_f32 as in the forward.
+__device__ inline float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+
+template <int ACT, bool BUF>
+__global__ __launch_bounds__(256) void gateup_bwd_w16(Bf16Args a, BwdArgs b, int n_ft_shard, int n_tt) {
+    using namespace w16;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
+    poison_lds(lds, sizeof(lds));
+    int ttile, flin;
+    raster(xcd_remap(blockIdx.x, gridDim.x), a.P * n_ft_shard, n_tt, ttile, flin);
+    const int k = flin / n_ft_shard;                    // ring step (record index)
+    const int ftile = flin - k * n_ft_shard;
+    const int64_t a_rs = (int64_t)(a.d >> 4) * 512;
+    const uint16_t* a_tile = a.packed + (int64_t)k * a.shard_elems + (int64_t)(ftile * (BM / 32)) * a_rs;
+    const int t0 = ttile * BN;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w / WN, wn = w % WN;
+    PackedSrc<BUF> src{a_tile, 0, 0, a.d >> 5, 0, 0, a_rs, a.x, a.d, t0, a.T,
+                       __builtin_amdgcn_readfirstlane(w), wm, wn, lane};
+    f32x4 acc[TM][TN];
+    w16::mainloop(lds, acc, a.d >> 5, src);
+
+    const int64_t ring0 = (int64_t)k * a.F, nat0 = (int64_t)b.order[k] * a.F;
+    const int fsub = 4 * (lane >> 4);
+    auto store4 = [&](uint16_t* base, int tok, int64_t col, float v0, float v1, float v2, float v3) {
+        *reinterpret_cast<uint2*>(base + (int64_t)tok * a.f + col) = pack4_bf16(v0, v1, v2, v3);
+    };
+    if constexpr (ACT == 1) {
+        // rows of the wave: 16-row blocks 4 q, 4 q + 1 gate and 4 q + 2, 4 q + 3
+        // up of hidden group q (see the forward)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int lc = (ftile * (BM / 64) + wm * 2 + q) * 32 + i * 16 + fsub;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int tok = t0 + (wn * TN + j) * 16 + (lane & 15);
+                    if (tok < a.T) {
+                        const f32x4 g = acc[4 * q + i][j], u = acc[4 * q + 2 + i][j];
+                        const float4 dh = *reinterpret_cast<const float4*>(b.dh + (int64_t)tok * a.f + nat0 + lc);
+                        const float dhv[4] = {dh.x, dh.y, dh.z, dh.w};
+                        float dg[4], du[4], hv[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float sg = sigmoid_f(g[e]);
+                            const float si = g[e] * sg;
+                            dg[e] = dhv[e] * u[e] * (sg * (1.0f + g[e] * (1.0f - sg)));
+                            du[e] = dhv[e] * si;
+                            hv[e] = si * u[e];
+                        }
+                        store4(b.dg, tok, ring0 + lc, dg[0], dg[1], dg[2], dg[3]);
+                        store4(b.du, tok, ring0 + lc, du[0], du[1], du[2], du[3]);
+                        store4(b.h, tok, ring0 + lc, hv[0], hv[1], hv[2], hv[3]);
+                    }
+                }
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int lc = ftile * BM + (wm * TM + i) * 16 + fsub;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int tok = t0 + (wn * TN + j) * 16 + (lane & 15);
+                if (tok < a.T) {
+                    const f32x4 u = acc[i][j];
+                    const float4 dh = *reinterpret_cast<const float4*>(b.dh + (int64_t)tok * a.f + nat0 + lc);
+                    const float dhv[4] = {dh.x, dh.y, dh.z, dh.w};
+                    float du[4], hv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = u[e];
+                        const float z2 = 1.5957691216057308f * (x + 0.044715f * x * x * x);
+                        const float dz2 = 1.5957691216057308f * (1.0f + 3.0f * 0.044715f * x * x);
+                        const float s2 = sigmoid_f(z2);
+                        hv[e] = x * s2;
+                        du[e] = dhv[e] * (s2 * (1.0f + x * (1.0f - s2) * dz2));
+                    }
+                    store4(b.du, tok, ring0 + lc, du[0], du[1], du[2], du[3]);
+                    store4(b.h, tok, ring0 + lc, hv[0], hv[1], hv[2], hv[3]);
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ launchers
+static inline int64_t cdiv64(int64_t x, int64_t y) { return (x + y - 1) / y; }
+
+hipError_t launch_transpose_bf16(const uint16_t* src, int R, int C, int ld_src, uint16_t* dst, int R_pad,
+                                 hipStream_t st) {
+    if (C % 64 || R_pad % 64 || R > R_pad) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(transpose_bf16, dim3((unsigned)(C / 64), (unsigned)(R_pad / 64)), dim3(256), 0, st, src, R,
+                       ld_src, dst, R_pad);
+    return hipGetLastError();
+}
+
+hipError_t launch_nt(const NtArgs& p, hipStream_t st) {
+    using namespace w16;
+    if (p.M % BM || p.N < 1 || (p.spp * p.nseg) % 2 || p.spp * p.nseg < 2 || p.kinds < 1 || p.kinds > 2)
+        return hipErrorInvalidValue;
+    if (p.remap && (p.F % BM || !p.remap_order)) return hipErrorInvalidValue;
+    const int n_mt = p.M / BM, n_nt = (int)cdiv64(p.N, BN);
+    const dim3 grid((unsigned)(n_mt * n_nt));
+    // buffer offsets are 32-bit: every row of either operand must lie within
+    // 2^31 bytes of that operand's base
+    const bool buf = (int64_t)p.M * p.lda * 2 < (int64_t(1) << 31) && (int64_t)p.N * p.ldb * 2 < (int64_t(1) << 31);
+    if (buf) hipLaunchKernelGGL((nt_w16<true>), grid, dim3(256), 0, st, p, n_mt, n_nt);
+    else hipLaunchKernelGGL((nt_w16<false>), grid, dim3(256), 0, st, p, n_mt, n_nt);
+    return hipGetLastError();
+}
+
+hipError_t launch_gateup_bwd(const Bf16Args& a, const BwdArgs& b, hipStream_t st) {
+    const int ngu = a.swiglu ? 2 * a.F : a.F;
+    if (ngu % 256 || a.d % 64) return hipErrorInvalidValue;
+    const int n_ft_shard = ngu / 256, n_tt = (int)cdiv64(a.T, 256);
+    const dim3 grid((unsigned)(a.P * n_ft_shard * n_tt));
+    const bool buf = (int64_t)a.T * a.d * 2 < (int64_t(1) << 31) && (int64_t)a.d * 512 < (int64_t(1) << 31);
+    if (a.swiglu) {
+        if (buf) hipLaunchKernelGGL((gateup_bwd_w16<1, true>), grid, dim3(256), 0, st, a, b, n_ft_shard, n_tt);
+        else hipLaunchKernelGGL((gateup_bwd_w16<1, false>), grid, dim3(256), 0, st, a, b, n_ft_shard, n_tt);
+    } else {
+        if (buf) hipLaunchKernelGGL((gateup_bwd_w16<2, true>), grid, dim3(256), 0, st, a, b, n_ft_shard, n_tt);
+        else hipLaunchKernelGGL((gateup_bwd_w16<2, false>), grid, dim3(256), 0, st, a, b, n_ft_shard, n_tt);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tsp

@@ -60,6 +60,18 @@ __device__ inline int xcd_remap(int bid, int nwg) {
     return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
 }
 
+// Token-tile-grouped raster over a (tokens x features) tile grid: GT token
+// tiles share each feature tile, consecutive ids walk the token tiles first.
+__device__ inline void raster(int L, int n_f, int n_t, int& ttile, int& flin) {
+    constexpr int GT = 8;
+    const int group = L / (GT * n_f);
+    const int first = group * GT;
+    const int gt = min(GT, n_t - first);
+    const int rem = L - group * GT * n_f;
+    ttile = first + rem % gt;
+    flin = rem / gt;
+}
+
 // Both activations divide by 1 + e^x through the hardware reciprocal
 // (v_rcp_f32, 1 ulp) instead of an IEEE division (about ten instructions):
 // their results are rounded to bf16 or summed in fp32 right after, where one

@@ -55,17 +55,6 @@ struct TileCfg {
     static_assert(NS * STAGE * 2 <= 160 * 1024, "LDS");
 };
 
-// Token-tile-grouped raster over a (tokens x features) tile grid: GT token
-// tiles share each feature tile, consecutive ids walk the token tiles first.
-__device__ inline void raster(int L, int n_f, int n_t, int& ttile, int& flin) {
-    constexpr int GT = 8;
-    const int group = L / (GT * n_f);
-    const int first = group * GT;
-    const int gt = min(GT, n_t - first);
-    const int rem = L - group * GT * n_f;
-    ttile = first + rem % gt;
-    flin = rem / gt;
-}
 
 // LDS layout of one stage (32 reduction indices):
 //   A blocks are the packed 32 x 16 fragment blocks, already in MFMA order:

@@ -63,6 +63,35 @@ hipError_t launch_gateup_skinny(const Bf16Args& a, hipStream_t st);
 hipError_t launch_down_skinny(const Bf16Args& a, hipStream_t st);
 bool skinny_supported(int d, int F, int P);
 
+// Backward (bf16). C[n][m] = sum_k A[m][k] B[n][k] over nseg segments of spp
+// 32-deep steps; segment j reads A at a_base[j % kinds] + (order ? order[j /
+// kinds] : j / kinds) * a_seg and B at b_base[j % kinds] + (j / kinds) * b_seg.
+// Output fp32 out[row(n) * ldc + col(m)] for n < N; remap 1 / 2 maps the
+// column / row index from ring order to the shard's natural position
+// (remap_order, shard width F).
+struct NtArgs {
+    const uint16_t* a_base[2];
+    const uint16_t* b_base[2];
+    int64_t a_seg, b_seg;
+    const int32_t* order;
+    int lda, ldb, M, N, spp, nseg, kinds;
+    float* out;
+    int64_t ldc;
+    int remap, F;
+    const int32_t* remap_order;
+};
+struct BwdArgs {
+    const float* dh;          // T x f fp32, natural hidden columns
+    uint16_t* dg;             // T x f bf16, ring-ordered hidden columns (SwiGLU only)
+    uint16_t* du;             // T x f bf16, ring-ordered
+    uint16_t* h;              // T x f bf16, ring-ordered
+    const int32_t* order;     // ring order (device)
+};
+hipError_t launch_transpose_bf16(const uint16_t* src, int R, int C, int ld_src, uint16_t* dst, int R_pad,
+                                 hipStream_t st);
+hipError_t launch_nt(const NtArgs& p, hipStream_t st);
+hipError_t launch_gateup_bwd(const Bf16Args& a, const BwdArgs& b, hipStream_t st);
+
 // fp32 path.
 hipError_t launch_gateup_f32(const F32Args& a, hipStream_t st);
 hipError_t launch_down_f32(const F32Args& a, hipStream_t st);

@@ -144,17 +144,18 @@ struct RowSrc {
     const uint16_t* b;
     int ls, j;                                          // step inside the segment, segment
     int spp, nseg, kinds;
-    const uint16_t* a_base[2];
-    const uint16_t* b_base[2];
+    const uint16_t *a_base0, *a_base1;                  // segment kinds 0 and 1 (no indexed arrays:
+    const uint16_t *b_base0, *b_base1;                  // a runtime index would put them in scratch)
     int64_t a_seg, b_seg;
     const int32_t* order;
     int lda, ldb, m0, n0, last_m, last_n, w, wm, wn, lane;
 
     __device__ void seek(int seg) {
         const int kind = seg % kinds, k = seg / kinds;
-        const int s = order ? order[k] : k;
-        a = a_base[kind] + (int64_t)s * a_seg;
-        b = b_base[kind] + (int64_t)k * b_seg;
+        // wave-uniform (the buffer resource built from it must live in SGPRs)
+        const int s = order ? __builtin_amdgcn_readfirstlane(order[k]) : k;
+        a = (kind ? a_base1 : a_base0) + (int64_t)s * a_seg;
+        b = (kind ? b_base1 : b_base0) + (int64_t)k * b_seg;
     }
     __device__ void issue(int g, uint16_t* lds_stage) {
         if (g < LA) {

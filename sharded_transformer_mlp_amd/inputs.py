@@ -19,6 +19,8 @@ Recipe (the pages give shapes only through their examples; the recipe is ours):
 * Orientation is Y = X W (input x output), row-major.
 * bf16 workloads round each fp32 tensor to bf16 with round-to-nearest-even
   (``Tensor.to(torch.bfloat16)``); fp32 workloads keep the fp32 draw.
+* The backward's output gradient dY ~ N(0, 1), T x d, comes from a generator
+  of its own (``make_output_grad``) and is rounded the same way.
 """
 from __future__ import annotations
 
@@ -151,6 +153,16 @@ def make_inputs(w: Workload, T: Optional[int] = None) -> MLPInputs:
         wu = wu.to(torch.bfloat16)
         wd = wd.to(torch.bfloat16)
     return MLPInputs(x, wg, wu, wd, rows)
+
+
+def make_output_grad(w: Workload, T: Optional[int] = None) -> torch.Tensor:
+    """Seeded output gradient dY for the backward: T x d, N(0, 1) fp32 from
+    its own generator (seed 1000003 + the workload's seed, so it does not
+    disturb the forward's draws), rounded to bf16 (RNE) for bf16 workloads."""
+    T = w.T if T is None else T
+    g = torch.Generator("cpu").manual_seed(1000003 + w.seed)
+    dy = torch.randn(T, w.d, generator=g, dtype=torch.float32)
+    return dy.to(torch.bfloat16) if w.dtype == "bf16" else dy
 
 
 def sample_rows(T: int, n: int, seed: int, must_include=None) -> torch.Tensor:
