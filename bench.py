@@ -6,7 +6,7 @@ the fused gate/up kernel over every weight shard (visited in ring order) and
 the down kernel that accumulates all shards' partial outputs into the fp32 Y.
 Inputs, packed weights and workspace are resident in HBM before timing.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass backward]
 
 Prints one JSON line. The default workload is the Llama-3-8B-shaped SwiGLU
 block (T=4096 tokens, d=4096, f=14336, P=8 shards, ring start 3), reported in
@@ -16,7 +16,9 @@ with HIP events recorded by the library on the stream the kernel runs on,
 over a second region of as many steps right after the (event-free) timed
 region.
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
-workload on this host's cores.
+workload on this host's cores. ``--pass backward`` times the backward instead
+(one step = the gradients for a seeded output gradient; TFLOP/s over the
+gradient products, the recomputed forward product not counted).
 """
 from __future__ import annotations
 
@@ -43,7 +45,14 @@ KERNEL_SOURCES = {
     "gateup_f32": ["gemm_f32.hip", "common.h"],
     "down_f32": ["gemm_f32.hip", "common.h"],
     "reduce_partials": ["gemm_tiled.hip", "common.h"],
+    "bwd_dh": ["backward.hip", "w16.h", "common.h"],
+    "bwd_gateup": ["backward.hip", "w16.h", "common.h"],
+    "bwd_dx": ["backward.hip", "w16.h", "common.h"],
+    "bwd_dw": ["backward.hip", "w16.h", "common.h"],
+    "bwd_transpose_in": ["backward.hip", "common.h"],
+    "bwd_transpose_mid": ["backward.hip", "common.h"],
 }
+METRIC_BWD = "sharded gated-MLP backward TFLOP/s (dX and weight gradients; recomputation not counted)"
 
 
 def log(*a):
@@ -67,6 +76,19 @@ def kernel_work(w, kernel: str, T: int):
     """Algorithmic (flops, bytes) of one launch of `kernel` on workload w."""
     es = 2 if w.dtype == "bf16" else 4
     n_gu = 2 if w.act == "swiglu" else 1
+    d, f = w.d, w.f
+    if kernel == "bwd_dh":                  # dH = dY.Wd^T: Wd, dY in, fp32 dH out
+        return 2 * T * d * f, f * d * es + T * d * es + T * f * 4
+    if kernel == "bwd_gateup":              # recomputed gate/up product + backward epilogue
+        return 2 * n_gu * T * d * f, n_gu * d * f * es + T * d * es + T * f * 4 + (n_gu + 1) * T * f * es
+    if kernel == "bwd_dx":                  # dX = sum dG.Wg^T + dU.Wu^T
+        return 2 * n_gu * T * d * f, n_gu * d * f * es + n_gu * T * f * es + T * d * 4
+    if kernel == "bwd_dw":                  # weight gradients (all of one backward's dW products)
+        return (2 * n_gu + 2) * T * d * f, 2 * T * d * es + (n_gu + 1) * T * f * es + (n_gu + 1) * d * f * 4
+    if kernel == "bwd_transpose_in":        # copies of X and dY: each byte read and written once
+        return 0, 2 * 2 * T * d * es
+    if kernel == "bwd_transpose_mid":       # copies of dG, dU, H
+        return 0, 2 * (n_gu + 1) * T * f * es
     if kernel in ("gateup_tiled", "skinny_gateup", "gateup_f32"):
         flops = 2 * T * w.d * w.f * n_gu
         byts = n_gu * w.d * w.f * es + T * w.d * es + T * w.f * es      # W_gu, X, H out
@@ -99,8 +121,9 @@ def read_traffic(workload_name: str, kernel: str):
         return None
 
 
-def cpu_baseline(w, inp, budget_s: float):
-    """Time the fp64 oracle on the first n token rows, n sized to ~budget_s."""
+def cpu_baseline(w, inp, budget_s: float, dy=None):
+    """Time the fp64 oracle on the first n token rows, n sized to ~budget_s
+    (the backward when dy is given: gradients of those rows' loss)."""
     import numpy as np
     import oracle
     try:
@@ -113,9 +136,14 @@ def cpu_baseline(w, inp, budget_s: float):
     wu, wd = inp.w_up.float().numpy(), inp.w_down.float().numpy()
     order = w.order()
 
+    g = None if dy is None else dy.float().numpy()
+
     def run(n):
         t = time.perf_counter()
-        oracle.mlp_forward(x[:n], wg, wu, wd, w.P, order, w.act)
+        if g is None:
+            oracle.mlp_forward(x[:n], wg, wu, wd, w.P, order, w.act)
+        else:
+            oracle.mlp_backward(x[:n], wg, wu, wd, g[:n], w.P, order, w.act)
         return time.perf_counter() - t
 
     n = min(w.T, 16)
@@ -127,14 +155,18 @@ def cpu_baseline(w, inp, budget_s: float):
     if n == w.T and dt < 0.5 * budget_s:       # whole workload is quick: repeat it, report the mean
         reps = max(1, int(0.5 * budget_s / max(dt, 1e-3)))
         dt = sum(run(n) for _ in range(reps)) / reps
-    if w.T <= 64:                               # decode-like: report bytes streamed per second
+    if g is not None:
+        value = oracle.backward_flops(n, w.d, w.f, w.act) / dt / 1e12
+        unit = "TFLOP/s"
+    elif w.T <= 64:                             # decode-like: report bytes streamed per second
         value = w.bytes(n) / dt / 1e9
         unit = "GB/s"
     else:
         value = w.flops(n) / dt / 1e12
         unit = "TFLOP/s"
+    what = "fp64 numpy oracle backward" if g is not None else "fp64 numpy oracle"
     return {"value": value, "unit": unit, "cores": cores, "kind": "oracle",
-            "sample": f"first {n} of {w.T} token rows, full weights, fp64 numpy oracle, "
+            "sample": f"first {n} of {w.T} token rows, full weights, {what}, "
                       f"{dt:.2f} s per pass, mean of {reps} pass(es)"}
 
 
@@ -161,6 +193,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the HBM-read and MFMA ceiling probes")
     ap.add_argument("--calibrate-copy", action="store_true", help="only run the copy kernel used to scale counters")
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
+                    help="forward (the headline metric) or the backward (gradients for a seeded dY)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -173,7 +207,7 @@ def main():
 
     import torch
     from sharded_transformer_mlp_amd.binding import TspMLP
-    from sharded_transformer_mlp_amd.inputs import make_inputs, workload
+    from sharded_transformer_mlp_amd.inputs import make_inputs, make_output_grad, workload
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -189,39 +223,61 @@ def main():
     t = time.perf_counter()
     mlp = TspMLP(wg, wu, wd, w.P, order=w.order(), act=w.act, T_max=w.T)
     pack_ms = (time.perf_counter() - t) * 1e3
-    del wg, wu, wd
-    y = torch.empty(w.T, w.d, dtype=torch.float32, device=dev)
+    backward = args.which == "backward"
+    if backward:
+        # a step is one backward: the seeded output gradient against the
+        # resident inputs and weights, gradients written into preallocated
+        # fp32 tensors (the first call also allocates the backward workspace,
+        # so the warmup does that)
+        dy = make_output_grad(w)
+        dy_dev = dy.to(dev)
+        grads = {"dX": torch.empty(w.T, w.d, dtype=torch.float32, device=dev),
+                 "dW_gate": None if wg is None else torch.empty(w.d, w.f, dtype=torch.float32, device=dev),
+                 "dW_up": torch.empty(w.d, w.f, dtype=torch.float32, device=dev),
+                 "dW_down": torch.empty(w.f, w.d, dtype=torch.float32, device=dev)}
+
+        def step():
+            mlp.backward(x, dy_dev, wg, wu, wd, out=grads)
+    else:
+        del wg, wu, wd
+        y = torch.empty(w.T, w.d, dtype=torch.float32, device=dev)
+
+        def step():
+            mlp.forward(x, y)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
-        mlp.forward(x, y)
+        step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # Timed region: exactly `steps` forwards, nothing else on the stream.
+    # Timed region: exactly `steps` passes, nothing else on the stream.
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(args.steps):
-        mlp.forward(x, y)
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
-    # Kernel region: the same number of forwards again, with the library
+    # Kernel region: the same number of passes again, with the library
     # recording HIP events around every kernel on the stream it runs on. The
     # events cost ~15 us per step, so they stay out of the timed region above.
     mlp.read_timing()
     mlp.set_timing(True)
     for _ in range(args.steps):
-        mlp.forward(x, y)
+        step()
     torch.cuda.synchronize()
     mlp.set_timing(False)
     kt = mlp.read_timing()
     kernels = {k: v[0] / max(v[1], 1) for k, v in kt.items()}
     log(f"ms/step {ms:.4f}; kernels {kernels}")
 
-    decode = w.T <= 64
-    if decode:
+    decode = w.T <= 64 and not backward
+    if backward:
+        import oracle
+        value, unit = oracle.backward_flops(w.T, w.d, w.f, w.act) / (ms * 1e-3) / 1e12, "TFLOP/s"
+    elif decode:
         value, unit = w.bytes() / (ms * 1e-3) / 1e9, "GB/s"
     else:
         value, unit = w.flops() / (ms * 1e-3) / 1e12, "TFLOP/s"
@@ -242,7 +298,7 @@ def main():
     roof["algorithmic_flops"] = flops
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if backward else METRIC,
         "value": value,
         "unit": unit,
         "n_gpus": 1,
@@ -265,8 +321,14 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if backward:
+        out["pass"] = "backward"
+        out["config"]["parallelism"] = "one TSP rank's backward (shard loop on one GPU)"
+        del grads, dy_dev, wg, wu, wd
+    else:
+        del y
     mlp.close()
-    del x, y
+    del x
     torch.cuda.empty_cache()
     if not args.no_ceilings:
         # Measured ceilings of this GPU beside the datasheet peaks, after the
@@ -288,7 +350,7 @@ def main():
         roof["frac_of_measured_ceiling"] = None if c is None else roof["achieved"] / c
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
-        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, dy if backward else None)
     print(json.dumps(out), flush=True)
 
 

@@ -428,7 +428,7 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
     const auto* wu16 = static_cast<const uint16_t*>(w_up);
     const auto* wd16 = static_cast<const uint16_t*>(w_down);
 
-    tsp_status_t s = timed_launch(h, "bwd_transpose", st, [&] {
+    tsp_status_t s = timed_launch(h, "bwd_transpose_in", st, [&] {
         hipError_t e = tsp::launch_transpose_bf16(x16, (int)T, (int)d, (int)d, xt, Tp, st);
         return e != hipSuccess ? e : tsp::launch_transpose_bf16(dy16, (int)T, (int)d, (int)d, dyt, Tp, st);
     });
@@ -453,7 +453,7 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
     tsp::BwdArgs b{dh, dg, du, hb, h->order_dev};
     s = timed_launch(h, "bwd_gateup", st, [&] { return tsp::launch_gateup_bwd(a, b, st); });
     if (s != TSP_OK) return s;
-    s = timed_launch(h, "bwd_transpose", st, [&] {
+    s = timed_launch(h, "bwd_transpose_mid", st, [&] {
         hipError_t e = hipSuccess;
         if (swiglu) e = tsp::launch_transpose_bf16(dg, (int)T, (int)f, (int)f, dgt, Tp, st);
         if (e == hipSuccess) e = tsp::launch_transpose_bf16(du, (int)T, (int)f, (int)f, dut, Tp, st);

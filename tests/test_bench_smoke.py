@@ -38,3 +38,21 @@ def test_bench_emits_the_contract_line(wl):
     for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert k in roof, k
     assert 0 < roof["frac"] < 1
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("wl", ["gelu", "llama8b"])
+def test_bench_backward_line(wl):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print(f"[gpu] bench --pass backward {wl}", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", wl, "--pass", "backward",
+                        "--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--no-ceilings"],
+                       capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    assert d["pass"] == "backward" and d["unit"] == "TFLOP/s" and d["value"] > 0
+    assert d["roofline"]["kernel"].startswith("bwd_") and 0 < d["roofline"]["frac"] < 1
