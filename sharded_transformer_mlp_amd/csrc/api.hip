@@ -440,7 +440,7 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
     p.lda = (int)d; p.ldb = (int)d; p.M = (int)f; p.N = (int)T;
     p.spp = (int)(d / 32); p.nseg = 1; p.kinds = 1;
     p.out = dh; p.ldc = f;
-    s = timed_launch(h, "bwd_dh", st, [&] { return tsp::launch_nt(p, st); });
+    s = timed_launch(h, "bwd_dh", st, [&] { return tsp::launch_nt(&p, 1, st); });
     if (s != TSP_OK) return s;
     // recompute G, U (H) and form dG, dU, H in ring-ordered hidden columns
     tsp::Bf16Args a{};
@@ -470,9 +470,10 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
     q.lda = (int)f; q.ldb = (int)f; q.M = (int)d; q.N = (int)T;
     q.spp = F / 32; q.kinds = swiglu ? 2 : 1; q.nseg = P * q.kinds;
     q.out = dX; q.ldc = d;
-    s = timed_launch(h, "bwd_dx", st, [&] { return tsp::launch_nt(q, st); });
+    s = timed_launch(h, "bwd_dx", st, [&] { return tsp::launch_nt(&q, 1, st); });
     if (s != TSP_OK) return s;
-    // weight gradients: reductions over the (zero-padded) token dimension
+    // weight gradients: reductions over the (zero-padded) token dimension, all
+    // in one launch
     auto dw = [&](const uint16_t* at, const uint16_t* bt, int M, int N, float* out, int64_t ldc, int remap) {
         tsp::NtArgs r{};
         r.a_base[0] = r.a_base[1] = at;
@@ -480,15 +481,14 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
         r.lda = Tp; r.ldb = Tp; r.M = M; r.N = N;
         r.spp = Tp / 32; r.nseg = 1; r.kinds = 1;
         r.out = out; r.ldc = ldc; r.remap = remap; r.F = F; r.remap_order = h->order_dev;
-        return tsp::launch_nt(r, st);
+        return r;
     };
-    s = timed_launch(h, "bwd_dw", st, [&] {
-        hipError_t e = hipSuccess;
-        if (swiglu) e = dw(dgt, xt, (int)f, (int)d, dW_gate, f, 1);       // dW_gate[i][c]
-        if (e == hipSuccess) e = dw(dut, xt, (int)f, (int)d, dW_up, f, 1);
-        return e != hipSuccess ? e : dw(dyt, ht, (int)d, (int)f, dW_down, d, 2);   // dW_down[c][n]
-    });
-    return s;
+    tsp::NtArgs ws[3];
+    int nw = 0;
+    if (swiglu) ws[nw++] = dw(dgt, xt, (int)f, (int)d, dW_gate, f, 1);   // dW_gate[i][c]
+    ws[nw++] = dw(dut, xt, (int)f, (int)d, dW_up, f, 1);
+    ws[nw++] = dw(dyt, ht, (int)d, (int)f, dW_down, d, 2);               // dW_down[c][n]
+    return timed_launch(h, "bwd_dw", st, [&] { return tsp::launch_nt(ws, nw, st); });
 }
 
 tsp_status_t tsp_mlp_destroy(tsp_mlp_t h) {

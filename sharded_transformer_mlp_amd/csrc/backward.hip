@@ -65,13 +65,21 @@ __global__ __launch_bounds__(256) void transpose_bf16(const uint16_t* __restrict
 // order[m / F] * F + m % F; remap 2: the same for the row n. F % 256 == 0, so
 // a 256-wide tile never straddles two shards and the remap is one offset per
 // tile.
+//
+// One launch runs up to three such products (NtGroup): workgroup ids are
+// dealt out to the products in order, so products whose tile counts are not
+// multiples of the CU count share one tail instead of leaving one each.
 template <bool BUF>
-__global__ __launch_bounds__(256) void nt_w16(NtArgs p, int n_mt, int n_nt) {
+__global__ __launch_bounds__(256) void nt_w16(NtGroup grp) {
     using namespace w16;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
     poison_lds(lds, sizeof(lds));
+    const int lin = xcd_remap(blockIdx.x, gridDim.x);
+    const int gi = lin < grp.first[1] ? 0 : (lin < grp.first[2] ? 1 : 2);
+    const NtArgs& p = gi == 0 ? grp.p[0] : (gi == 1 ? grp.p[1] : grp.p[2]);
+    const int n_mt = p.M / BM, n_nt = (p.N + BN - 1) / BN;
     int ntile, mtile;
-    raster(xcd_remap(blockIdx.x, gridDim.x), n_mt, n_nt, ntile, mtile);
+    raster(lin - grp.first[gi], n_mt, n_nt, ntile, mtile);
     const int m0 = mtile * BM, n0 = ntile * BN;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w / WN, wn = w % WN;
@@ -223,18 +231,30 @@ hipError_t launch_transpose_bf16(const uint16_t* src, int R, int C, int ld_src, 
     return hipGetLastError();
 }
 
-hipError_t launch_nt(const NtArgs& p, hipStream_t st) {
+hipError_t launch_nt(const NtArgs* probs, int n, hipStream_t st) {
     using namespace w16;
-    if (p.M % BM || p.N < 1 || (p.spp * p.nseg) % 2 || p.spp * p.nseg < 2 || p.kinds < 1 || p.kinds > 2)
-        return hipErrorInvalidValue;
-    if (p.remap && (p.F % BM || !p.remap_order)) return hipErrorInvalidValue;
-    const int n_mt = p.M / BM, n_nt = (int)cdiv64(p.N, BN);
-    const dim3 grid((unsigned)(n_mt * n_nt));
+    if (n < 1 || n > 3) return hipErrorInvalidValue;
+    NtGroup grp{};
+    int64_t tiles = 0;
     // buffer offsets are 32-bit: every row of either operand must lie within
     // 2^31 bytes of that operand's base
-    const bool buf = (int64_t)p.M * p.lda * 2 < (int64_t(1) << 31) && (int64_t)p.N * p.ldb * 2 < (int64_t(1) << 31);
-    if (buf) hipLaunchKernelGGL((nt_w16<true>), grid, dim3(256), 0, st, p, n_mt, n_nt);
-    else hipLaunchKernelGGL((nt_w16<false>), grid, dim3(256), 0, st, p, n_mt, n_nt);
+    bool buf = true;
+    for (int i = 0; i < 3; ++i) {
+        grp.first[i] = (int)tiles;
+        if (i >= n) continue;
+        const NtArgs& p = probs[i];
+        if (p.M % BM || p.N < 1 || (p.spp * p.nseg) % 2 || p.spp * p.nseg < 2 || p.kinds < 1 || p.kinds > 2)
+            return hipErrorInvalidValue;
+        if (p.remap && (p.F % BM || !p.remap_order)) return hipErrorInvalidValue;
+        grp.p[i] = p;
+        tiles += (int64_t)(p.M / BM) * cdiv64(p.N, BN);
+        buf = buf && (int64_t)p.M * p.lda * 2 < (int64_t(1) << 31) && (int64_t)p.N * p.ldb * 2 < (int64_t(1) << 31);
+    }
+    for (int i = n; i < 3; ++i) grp.first[i] = (int)tiles;
+    if (tiles > INT32_MAX / 2) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)tiles);
+    if (buf) hipLaunchKernelGGL((nt_w16<true>), grid, dim3(256), 0, st, grp);
+    else hipLaunchKernelGGL((nt_w16<false>), grid, dim3(256), 0, st, grp);
     return hipGetLastError();
 }
 

@@ -89,7 +89,12 @@ struct BwdArgs {
 };
 hipError_t launch_transpose_bf16(const uint16_t* src, int R, int C, int ld_src, uint16_t* dst, int R_pad,
                                  hipStream_t st);
-hipError_t launch_nt(const NtArgs& p, hipStream_t st);
+// Up to three products in one launch; first[i] is product i's first tile.
+struct NtGroup {
+    NtArgs p[3];
+    int first[3];
+};
+hipError_t launch_nt(const NtArgs* probs, int n, hipStream_t st);
 hipError_t launch_gateup_bwd(const Bf16Args& a, const BwdArgs& b, hipStream_t st);
 
 // fp32 path.
