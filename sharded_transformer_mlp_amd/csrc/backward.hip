@@ -156,67 +156,81 @@ __global__ __launch_bounds__(256) void gateup_bwd_w16(Bf16Args a, BwdArgs b, int
     f32x4 acc[TM][TN];
     w16::mainloop(lds, acc, a.d >> 5, src);
 
-    const int64_t ring0 = (int64_t)k * a.F, nat0 = (int64_t)b.order[k] * a.F;
+    // Epilogue. The tile covers hidden columns [lc0, lc0 + COLS) of shard
+    // order[k] (COLS = 128 for SwiGLU, 256 for GeLU): dH is read at the shard's
+    // natural columns, dG, dU and H are written at the ring-ordered columns.
+    // All of them go through the LDS ring (StagedRows16) so that the stores
+    // write whole rows, in two halves of the tokens: a half of all outputs
+    // fits in the ring, and the accumulators a half consumes die with it.
+    constexpr int COLS = ACT == 1 ? BM / 2 : BM;
+    constexpr int NB = ACT == 1 ? 4 : TM;               // 16-column blocks of the wave
+    constexpr int NO = ACT == 1 ? 3 : 2;                // outputs
+    using Stg = StagedRows16<COLS, 128>;
+    static_assert(NO * Stg::ELEMS <= NS * STAGE, "LDS");
+    const int lc0 = ftile * COLS;
+    const int64_t ring0 = (int64_t)k * a.F + lc0, nat0 = (int64_t)b.order[k] * a.F + lc0;
     const int fsub = 4 * (lane >> 4);
-    auto store4 = [&](uint16_t* base, int tok, int64_t col, float v0, float v1, float v2, float v3) {
-        *reinterpret_cast<uint2*>(base + (int64_t)tok * a.f + col) = pack4_bf16(v0, v1, v2, v3);
-    };
-    if constexpr (ACT == 1) {
-        // rows of the wave: 16-row blocks 4 q, 4 q + 1 gate and 4 q + 2, 4 q + 3
-        // up of hidden group q (see the forward)
+    const float* __restrict__ dh = b.dh;
+    Stg sh{lds}, su{lds + Stg::ELEMS}, sg_{lds + 2 * Stg::ELEMS};
+    auto col = [&](int ib) { return ACT == 1 ? (wm * 2 + ib / 2) * 32 + (ib % 2) * 16 + fsub
+                                             : (wm * TM + ib) * 16 + fsub; };
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+    for (int hh = 0; hh < 2; ++hh) {
+        stage_barrier();                                // fragment reads / the last flush's reads are done
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int lc = (ftile * (BM / 64) + wm * 2 + q) * 32 + i * 16 + fsub;
+        for (int ib = 0; ib < NB; ++ib) {
+            const int c = col(ib);
+            // the dH values of the half's four (16-token, 4-column) pieces are
+            // loaded together before any of them is used
+            f32x4 dv[TN / 2];
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int tok = t0 + (wn * TN + j) * 16 + (lane & 15);
-                    if (tok < a.T) {
-                        const f32x4 g = acc[4 * q + i][j], u = acc[4 * q + 2 + i][j];
-                        const float4 dh = *reinterpret_cast<const float4*>(b.dh + (int64_t)tok * a.f + nat0 + lc);
-                        const float dhv[4] = {dh.x, dh.y, dh.z, dh.w};
-                        float dg[4], du[4], hv[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float sg = sigmoid_f(g[e]);
-                            const float si = g[e] * sg;
-                            dg[e] = dhv[e] * u[e] * (sg * (1.0f + g[e] * (1.0f - sg)));
-                            du[e] = dhv[e] * si;
-                            hv[e] = si * u[e];
-                        }
-                        store4(b.dg, tok, ring0 + lc, dg[0], dg[1], dg[2], dg[3]);
-                        store4(b.du, tok, ring0 + lc, du[0], du[1], du[2], du[3]);
-                        store4(b.h, tok, ring0 + lc, hv[0], hv[1], hv[2], hv[3]);
-                    }
-                }
+            for (int jj = 0; jj < TN / 2; ++jj) {
+                const int tok = min(t0 + wn * 128 + hh * 64 + jj * 16 + (lane & 15), a.T - 1);
+                dv[jj] = __builtin_nontemporal_load(
+                    reinterpret_cast<const f32x4*>(dh + (int64_t)tok * a.f + nat0 + c));
             }
-    } else {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int lc = ftile * BM + (wm * TM + i) * 16 + fsub;
+            for (int jj = 0; jj < TN / 2; ++jj) {
+                const int j = hh * (TN / 2) + jj, r = wn * 64 + jj * 16 + (lane & 15);
+                if constexpr (ACT == 1) {
+                    // wave rows: 16-row blocks 4 q + i gate and 4 q + 2 + i up
+                    // of hidden group q = ib / 2, i = ib % 2 (see the forward)
+                    const f32x4 g = acc[4 * (ib / 2) + ib % 2][j], u = acc[4 * (ib / 2) + 2 + ib % 2][j];
+                    float dg[4], du[4], h[4];
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int tok = t0 + (wn * TN + j) * 16 + (lane & 15);
-                if (tok < a.T) {
-                    const f32x4 u = acc[i][j];
-                    const float4 dh = *reinterpret_cast<const float4*>(b.dh + (int64_t)tok * a.f + nat0 + lc);
-                    const float dhv[4] = {dh.x, dh.y, dh.z, dh.w};
-                    float du[4], hv[4];
+                    for (int e = 0; e < 4; ++e) {
+                        const float sg = sigmoid_f(g[e]);
+                        const float si = g[e] * sg;
+                        dg[e] = dv[jj][e] * u[e] * (sg * (1.0f + g[e] * (1.0f - sg)));
+                        du[e] = dv[jj][e] * si;
+                        h[e] = si * u[e];
+                    }
+                    sg_.put4(r, c, pack4_bf16(dg[0], dg[1], dg[2], dg[3]));
+                    su.put4(r, c, pack4_bf16(du[0], du[1], du[2], du[3]));
+                    sh.put4(r, c, pack4_bf16(h[0], h[1], h[2], h[3]));
+                } else {
+                    const f32x4 u = acc[ib][j];
+                    float du[4], h[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float x = u[e];
                         const float z2 = 1.5957691216057308f * (x + 0.044715f * x * x * x);
                         const float dz2 = 1.5957691216057308f * (1.0f + 3.0f * 0.044715f * x * x);
                         const float s2 = sigmoid_f(z2);
-                        hv[e] = x * s2;
-                        du[e] = dhv[e] * (s2 * (1.0f + x * (1.0f - s2) * dz2));
+                        du[e] = dv[jj][e] * (s2 * (1.0f + x * (1.0f - s2) * dz2));
+                        h[e] = x * s2;
                     }
-                    store4(b.du, tok, ring0 + lc, du[0], du[1], du[2], du[3]);
-                    store4(b.h, tok, ring0 + lc, hv[0], hv[1], hv[2], hv[3]);
+                    su.put4(r, c, pack4_bf16(du[0], du[1], du[2], du[3]));
+                    sh.put4(r, c, pack4_bf16(h[0], h[1], h[2], h[3]));
                 }
             }
         }
+        lgkm_zero();
+        stage_barrier();
+        if constexpr (ACT == 1) sg_.flush(b.dg, a.f, t0, a.T, ring0, w, lane, hh);
+        su.flush(b.du, a.f, t0, a.T, ring0, w, lane, hh);
+        sh.flush(b.h, a.f, t0, a.T, ring0, w, lane, hh);
+        lgkm_zero();
     }
 }
 

@@ -813,40 +813,46 @@ __global__ __launch_bounds__(256) void gateup_w16(Bf16Args a, int n_ft_shard, in
     f32x4 acc[TM][TN];
     w16::mainloop(lds, acc, a.d >> 5, src);
 
+    // H through the LDS ring (StagedRows16): every wave's last fragment reads
+    // are done at the first barrier, its LDS writes at the second
     const int fsub = 4 * (lane >> 4);
+    stage_barrier();
     if constexpr (ACT == 1) {
         // the wave's 128 rows are two (32 gate, 32 up) row pairs: 16-row
-        // blocks 4 q, 4 q + 1 gate and 4 q + 2, 4 q + 3 up of hidden group q
+        // blocks 4 q, 4 q + 1 gate and 4 q + 2, 4 q + 3 up of hidden group q;
+        // the tile holds 128 hidden columns
+        StagedRows16<BM / 2> stg{lds};
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int hcol = s * a.F + (ftile * (BM / 64) + wm * 2 + q) * 32 + i * 16 + fsub;
+                const int c = (wm * 2 + q) * 32 + i * 16 + fsub;
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    const int tok = t0 + (wn * TN + j) * 16 + (lane & 15);
-                    if (tok < a.T) {
-                        const f32x4 g = acc[4 * q + i][j], u = acc[4 * q + 2 + i][j];
-                        *reinterpret_cast<uint2*>(a.h + (int64_t)tok * a.f + hcol) =
-                            pack4_bf16(silu_f(g[0]) * u[0], silu_f(g[1]) * u[1], silu_f(g[2]) * u[2],
-                                       silu_f(g[3]) * u[3]);
-                    }
+                    const f32x4 g = acc[4 * q + i][j], u = acc[4 * q + 2 + i][j];
+                    stg.put4((wn * TN + j) * 16 + (lane & 15), c,
+                             pack4_bf16(silu_f(g[0]) * u[0], silu_f(g[1]) * u[1], silu_f(g[2]) * u[2],
+                                        silu_f(g[3]) * u[3]));
                 }
             }
+        lgkm_zero();
+        stage_barrier();
+        stg.flush(a.h, a.f, t0, a.T, (int64_t)s * a.F + ftile * (BM / 2), w, lane);
     } else {
+        StagedRows16<BM> stg{lds};
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const int hcol = s * a.F + ftile * BM + (wm * TM + i) * 16 + fsub;
+            const int c = (wm * TM + i) * 16 + fsub;
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const int tok = t0 + (wn * TN + j) * 16 + (lane & 15);
-                if (tok < a.T) {
-                    const f32x4 u = acc[i][j];
-                    *reinterpret_cast<uint2*>(a.h + (int64_t)tok * a.f + hcol) =
-                        pack4_bf16(gelu_tanh_f(u[0]), gelu_tanh_f(u[1]), gelu_tanh_f(u[2]), gelu_tanh_f(u[3]));
-                }
+                const f32x4 u = acc[i][j];
+                stg.put4((wn * TN + j) * 16 + (lane & 15), c,
+                         pack4_bf16(gelu_tanh_f(u[0]), gelu_tanh_f(u[1]), gelu_tanh_f(u[2]), gelu_tanh_f(u[3])));
             }
         }
+        lgkm_zero();
+        stage_barrier();
+        stg.flush(a.h, a.f, t0, a.T, (int64_t)s * a.F + ftile * BM, w, lane);
     }
 }
 

@@ -255,30 +255,89 @@ __device__ __forceinline__ void step(int& ld_ref, int& rd_ref, Src& src, uint16_
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// One stream of stages through the LDS ring. start() issues the first NS
+// stages and reads stage 0's fragments; tile() runs one tile's ksteps stages
+// (even, >= 2) from the stream, leaving the next tile's stage-0 fragments in
+// (a0, b0) unless END; finish() waits for every load into LDS. A workgroup
+// that runs several tiles back to back (a source whose advance() walks on to
+// the next tile) thus issues the next tile's first loads during this tile's
+// last steps, and they land while it writes its results.
+template <class Src>
+struct Stream {
+    bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
+    int ld = 0, rd = STAGE;                             // buffers of stages t and t + 1
+
+    __device__ __forceinline__ void start(uint16_t* lds, Src& src) {
+        for (int t = 0; t < NS; ++t) {
+#pragma unroll
+            for (int g = 0; g < LOADS; ++g) src.issue(g, lds + t * STAGE);
+            src.advance();
+        }
+        TSP_VMCNT((NS - 1) * LOADS);                    // own loads of stage 0 landed
+        stage_barrier();
+#pragma unroll
+        for (int q = 0; q < TM + TN; ++q) src.read(q, lds, a0, b0);
+        TSP_VMCNT((NS - 2) * LOADS);                    // own loads of stage 1 landed
+        lgkm_zero();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    template <bool END>
+    __device__ __forceinline__ void tile(uint16_t* lds, f32x4 (&acc)[TM][TN], int ksteps, Src& src) {
+        step<true, false>(ld, rd, src, lds, acc, a0, b0, a1, b1);
+        for (int t = 1; t + 2 < ksteps; t += 2) {
+            step<false, false>(ld, rd, src, lds, acc, a1, b1, a0, b0);
+            step<false, false>(ld, rd, src, lds, acc, a0, b0, a1, b1);
+        }
+        step<false, END>(ld, rd, src, lds, acc, a1, b1, a0, b0);
+    }
+    __device__ __forceinline__ void finish() {
+        TSP_VMCNT(0);                                   // no load into LDS outlives the workgroup
+    }
+};
+
+// A workgroup's bf16 result rows staged in the LDS ring once the reduction is
+// done, so that the global stores write whole rows: straight from the MFMA
+// layout, a store covers 16 tokens x 32 bytes, a quarter of a 128-byte line per
+// token (measured: 17 % of the backward gate/up kernel's time went to three
+// such stores). ROWS = 256 stages the whole token tile; ROWS = 128 stages one
+// half hh of each wave row's 128 tokens (tile rows wn * 128 + hh * 64 + [0, 64)
+// at staged rows wn * 64 + [0, 64)), for epilogues with more outputs than the
+// ring holds at full height. put4 takes one lane's four values at a staged row;
+// the row pitch COLS + 8 spreads a put4 instruction's 16 rows over all banks.
+// flush() writes the staged rows of this wave's quarter.
+template <int COLS, int ROWS = 256>
+struct StagedRows16 {
+    static_assert(ROWS == 256 || ROWS == 128, "ROWS");
+    static constexpr int PITCH = COLS + 8;
+    static constexpr int ELEMS = ROWS * PITCH;          // LDS elements one staged tile takes
+    static_assert(ELEMS * 2 <= NS * STAGE * 2, "LDS");
+    uint16_t* lds;
+    __device__ __forceinline__ void put4(int r, int c, uint2 v) {
+        *reinterpret_cast<uint2*>(lds + r * PITCH + c) = v;
+    }
+    __device__ __forceinline__ void flush(uint16_t* __restrict__ dst, int64_t ld, int t0, int T, int64_t col0,
+                                          int w, int lane, int hh = 0) {
+        constexpr int LPR = COLS / 8;                   // lanes per row (16 bytes each)
+        constexpr int RPI = 64 / LPR;                   // rows per store instruction
+        constexpr int RPW = ROWS / 4;                   // staged rows per wave
+#pragma unroll
+        for (int it = 0; it < RPW / RPI; ++it) {
+            const int r = w * RPW + it * RPI + lane / LPR;
+            const int c = (lane % LPR) * 8;
+            const int tr = ROWS == 256 ? r : (r >> 6) * 128 + hh * 64 + (r & 63);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * PITCH + c);
+            if (t0 + tr < T) *reinterpret_cast<u32x4*>(dst + (int64_t)(t0 + tr) * ld + col0 + c) = v;
+        }
+    }
+};
+
 // The reduction over ksteps stages (even, >= 2). src is positioned at stage 0.
 template <class Src>
 __device__ __forceinline__ void mainloop(uint16_t* lds, f32x4 (&acc)[TM][TN], int ksteps, Src& src) {
-    for (int t = 0; t < NS; ++t) {
-#pragma unroll
-        for (int g = 0; g < LOADS; ++g) src.issue(g, lds + t * STAGE);
-        src.advance();
-    }
-    bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
-    TSP_VMCNT((NS - 1) * LOADS);                        // own loads of stage 0 landed
-    stage_barrier();
-#pragma unroll
-    for (int q = 0; q < TM + TN; ++q) src.read(q, lds, a0, b0);
-    TSP_VMCNT((NS - 2) * LOADS);                        // own loads of stage 1 landed
-    lgkm_zero();
-    __builtin_amdgcn_sched_barrier(0);
-    int ld = 0, rd = STAGE;                             // buffers of stages t and t + 1
-    step<true, false>(ld, rd, src, lds, acc, a0, b0, a1, b1);
-    for (int t = 1; t + 2 < ksteps; t += 2) {
-        step<false, false>(ld, rd, src, lds, acc, a1, b1, a0, b0);
-        step<false, false>(ld, rd, src, lds, acc, a0, b0, a1, b1);
-    }
-    step<false, true>(ld, rd, src, lds, acc, a1, b1, a0, b0);
-    TSP_VMCNT(0);                                       // no load into LDS outlives the workgroup
+    Stream<Src> st;
+    st.start(lds, src);
+    st.template tile<true>(lds, acc, ksteps, src);
+    st.finish();
 }
 #undef TSP_VMCNT
 

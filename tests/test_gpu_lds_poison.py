@@ -79,3 +79,35 @@ def test_parity_with_poisoned_lds(name, w, path, tiles):
     else:
         assert np.linalg.norm(dy) / np.linalg.norm(ref) <= 3e-3
         assert np.max(np.abs(dy)) <= 2e-2 * np.max(np.abs(ref))
+
+
+BWD_CASES = [
+    ("backward swiglu", Workload("bs", T=300, d=512, f=2048, P=4, act="swiglu", dtype="bf16", seed=15, r0=1)),
+    ("backward gelu", Workload("bg", T=200, d=256, f=1024, P=2, act="gelu_tanh", dtype="bf16", seed=16)),
+]
+
+
+@pytest.mark.parametrize("name,w", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_backward_with_poisoned_lds(name, w):
+    """The backward kernels stage operands and results in LDS too: NaN in a
+    gradient means a read ran ahead of its data."""
+    from sharded_transformer_mlp_amd.inputs import make_output_grad
+    assert binding.LIB_PATH == DEBUG_LIB
+    say(f"[gpu] LDS poison: {name}")
+    inp, dy = make_inputs(w), make_output_grad(w)
+    dev = torch.device("cuda:0")
+    wg = None if inp.w_gate is None else inp.w_gate.to(dev)
+    wu, wd = inp.w_up.to(dev), inp.w_down.to(dev)
+    mlp = binding.TspMLP(wg, wu, wd, w.P, order=w.order(), act=w.act, T_max=w.T)
+    g = mlp.backward(inp.x.to(dev), dy.to(dev), wg, wu, wd)
+    torch.cuda.synchronize()
+    mlp.close()
+    f = lambda t: None if t is None else t.float().numpy()
+    ref = oracle.mlp_backward(f(inp.x), f(inp.w_gate), f(inp.w_up), f(inp.w_down), f(dy), w.P, w.order(), w.act)
+    for k, r in ref.items():
+        if r is None:
+            continue
+        got = g[k].cpu().double().numpy()
+        assert np.isfinite(got).all(), f"{name} {k}: NaN (a read ran ahead of its data)"
+        assert np.linalg.norm(got - r) / np.linalg.norm(r) <= 3e-3, (name, k)
+        assert np.max(np.abs(got - r)) <= 2e-2 * np.max(np.abs(r)), (name, k)
