@@ -113,17 +113,23 @@ __global__ __launch_bounds__(256) void nt_w16(NtGroup grp) {
     int64_t col0 = m0, row_shift = 0;
     if (p.remap == 1) col0 = (int64_t)p.remap_order[m0 / p.F] * p.F + m0 % p.F;
     if (p.remap == 2) row_shift = (int64_t)p.remap_order[n0 / p.F] * p.F + n0 % p.F - n0;
+    // Output rows are the N side, so a store straight from the MFMA layout
+    // would write 16 rows x 64 bytes; the tile goes out through the LDS ring
+    // instead, half of each wave row's tokens at a time, one 1 KiB row per store.
+    StagedRowsF32 stg{reinterpret_cast<float*>(lds)};
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int64_t col = col0 + (wm * TM + i) * 16 + 4 * (lane >> 4);
+    for (int hh = 0; hh < 2; ++hh) {
+        stage_barrier();                                // fragment reads / the last flush's reads are done
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = n0 + (wn * TN + j) * 16 + (lane & 15);
-            if (n < p.N) {
-                const f32x4 v = acc[i][j];
-                *reinterpret_cast<float4*>(p.out + (n + row_shift) * p.ldc + col) = make_float4(v[0], v[1], v[2], v[3]);
-            }
-        }
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < TN / 2; ++jj)
+                stg.put4(wn * 64 + jj * 16 + (lane & 15), (wm * TM + i) * 16 + 4 * (lane >> 4),
+                         acc[i][hh * (TN / 2) + jj]);
+        lgkm_zero();
+        stage_barrier();
+        stg.flush(p.out, p.ldc, n0, p.N, row_shift, col0, w, lane, hh);
+        lgkm_zero();
     }
 }
 

@@ -880,17 +880,23 @@ __global__ __launch_bounds__(256) void down_w16(Bf16Args a, int n_ft, int n_tt, 
     f32x4 acc[TM][TN];
     w16::mainloop(lds, acc, steps_per_group * spp, src);
 
+    // Y rows through the LDS ring, half of each wave row's tokens at a time,
+    // so that each store writes a whole 1 KiB row (from the MFMA layout a
+    // store covers 16 tokens x 64 bytes)
+    StagedRowsF32 stg{reinterpret_cast<float*>(lds)};
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int n = ftile * BM + (wm * TM + i) * 16 + 4 * (lane >> 4);
+    for (int hh = 0; hh < 2; ++hh) {
+        stage_barrier();                                // fragment reads / the last flush's reads are done
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int tok = t0 + (wn * TN + j) * 16 + (lane & 15);
-            if (tok < a.T) {
-                const f32x4 v = acc[i][j];
-                *reinterpret_cast<float4*>(y + (int64_t)tok * a.d + n) = make_float4(v[0], v[1], v[2], v[3]);
-            }
-        }
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < TN / 2; ++jj)
+                stg.put4(wn * 64 + jj * 16 + (lane & 15), (wm * TM + i) * 16 + 4 * (lane >> 4),
+                         acc[i][hh * (TN / 2) + jj]);
+        lgkm_zero();
+        stage_barrier();
+        stg.flush(y, a.d, t0, a.T, 0, (int64_t)ftile * BM, w, lane, hh);
+        lgkm_zero();
     }
 }
 

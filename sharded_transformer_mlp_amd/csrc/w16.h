@@ -331,6 +331,31 @@ struct StagedRows16 {
     }
 };
 
+// The fp32 counterpart for 256-column result tiles: 128 staged rows, one half
+// hh of each wave row's tokens (as StagedRows16<COLS, 128>), 1 KiB per row so
+// that each flush store writes one whole row. put4 takes one lane's four
+// values; the pitch 260 puts a put4 instruction's 16 rows 4 banks apart.
+struct StagedRowsF32 {
+    static constexpr int COLS = 256, ROWS = 128, PITCH = COLS + 4;
+    static constexpr int ELEMS = ROWS * PITCH;          // floats
+    static_assert(ELEMS * 4 <= NS * STAGE * 2, "LDS");
+    float* lds;
+    __device__ __forceinline__ void put4(int r, int c, f32x4 v) {
+        *reinterpret_cast<f32x4*>(lds + r * PITCH + c) = v;
+    }
+    // rows n0 + tr + row_shift of dst for tile rows tr of half hh below N
+    __device__ __forceinline__ void flush(float* __restrict__ dst, int64_t ld, int n0, int N, int64_t row_shift,
+                                          int64_t col0, int w, int lane, int hh) {
+#pragma unroll 8
+        for (int it = 0; it < ROWS / 4; ++it) {
+            const int r = w * (ROWS / 4) + it;
+            const int tr = (r >> 6) * 128 + hh * 64 + (r & 63);
+            const f32x4 v = *reinterpret_cast<const f32x4*>(lds + r * PITCH + lane * 4);
+            if (n0 + tr < N) *reinterpret_cast<f32x4*>(dst + (n0 + tr + row_shift) * ld + col0 + lane * 4) = v;
+        }
+    }
+};
+
 // The reduction over ksteps stages (even, >= 2). src is positioned at stage 0.
 template <class Src>
 __device__ __forceinline__ void mainloop(uint16_t* lds, f32x4 (&acc)[TM][TN], int ksteps, Src& src) {
