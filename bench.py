@@ -38,13 +38,13 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector / MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 KERNEL_SOURCES = {
-    "gateup_tiled": ["gemm_tiled.hip", "common.h"],
-    "down_tiled": ["gemm_tiled.hip", "common.h"],
+    "gateup_tiled": ["gemm_tiled.hip", "w16.h", "common.h"],
+    "down_tiled": ["gemm_tiled.hip", "w16.h", "common.h"],
     "skinny_gateup": ["gemm_skinny.hip", "common.h"],
     "skinny_down": ["gemm_skinny.hip", "common.h"],
     "gateup_f32": ["gemm_f32.hip", "common.h"],
     "down_f32": ["gemm_f32.hip", "common.h"],
-    "reduce_partials": ["gemm_tiled.hip", "common.h"],
+    "reduce_partials": ["gemm_tiled.hip", "w16.h", "common.h"],
     "bwd_dh": ["backward.hip", "w16.h", "common.h"],
     "bwd_gateup": ["backward.hip", "w16.h", "common.h"],
     "bwd_dx": ["backward.hip", "w16.h", "common.h"],
