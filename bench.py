@@ -6,7 +6,7 @@ the fused gate/up kernel over every weight shard (visited in ring order) and
 the down kernel that accumulates all shards' partial outputs into the fp32 Y.
 Inputs, packed weights and workspace are resident in HBM before timing.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass backward]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass backward|attention]
 
 Prints one JSON line. The default workload is the Llama-3-8B-shaped SwiGLU
 block (T=4096 tokens, d=4096, f=14336, P=8 shards, ring start 3), reported in
@@ -19,6 +19,11 @@ region.
 workload on this host's cores. ``--pass backward`` times the backward instead
 (one step = the gradients for a seeded output gradient; TFLOP/s over the
 gradient products, the recomputed forward product not counted).
+``--pass attention`` times one rank's TSP attention block instead (default
+workload: the Llama-3-8B attention shape, rank 3 of 8, causal; one step =
+the Q/K/V projection of the rank's tokens, attention over the context that
+the other ranks' projections filled before timing, and the output
+projection).
 """
 from __future__ import annotations
 
@@ -51,8 +56,12 @@ KERNEL_SOURCES = {
     "bwd_dw": ["backward.hip", "w16.h", "common.h"],
     "bwd_transpose_in": ["backward.hip", "common.h"],
     "bwd_transpose_mid": ["backward.hip", "common.h"],
+    "attn_qkv": ["attn.hip", "w16.h", "common.h"],
+    "attn_core": ["attn.hip", "common.h"],
+    "attn_out": ["gemm_tiled.hip", "w16.h", "common.h"],
 }
 METRIC_BWD = "sharded gated-MLP backward TFLOP/s (dX and weight gradients; recomputation not counted)"
+METRIC_ATTN = "TSP attention block TFLOP/s, one rank (projections + causal attention over the exchanged context)"
 
 
 def log(*a):
@@ -170,6 +179,134 @@ def cpu_baseline(w, inp, budget_s: float, dy=None):
                       f"{dt:.2f} s per pass, mean of {reps} pass(es)"}
 
 
+def attn_kernel_work(w, kernel: str):
+    """Algorithmic (flops, bytes) of one launch of an attention-block kernel."""
+    T, d, H, Hkv, dh, P = w.T, w.d, w.H, w.Hkv, w.dh, w.P
+    visible = w.rank * T + T if w.causal else w.S          # context rows the rank reads
+    pairs = (w.rank * T * T + T * (T + 1) // 2) if w.causal else T * w.S
+    if kernel == "attn_qkv":           # X . [Wq | Wk | Wv]: weights and X in, Q, K, V out (bf16)
+        n = (H + 2 * Hkv) * dh
+        return 2 * T * d * n, d * n * 2 + T * d * 2 + T * n * 2
+    if kernel == "attn_core":          # Q, the visible K and V rows in, O out
+        return 4 * dh * H * pairs, T * H * dh * 2 * 2 + 2 * visible * Hkv * dh * 2
+    if kernel == "attn_out":           # O . Wo into fp32 Y
+        return 2 * T * H * dh * d, H * dh * d * 2 + T * H * dh * 2 + T * d * 4
+    if kernel == "reduce_partials":
+        return 0, T * d * 4
+    raise KeyError(kernel)
+
+
+def cpu_baseline_attn(w, inp, budget_s: float):
+    """Time the fp64 attention oracle on the rank's first n token rows (it
+    also projects every rank's keys and values, the exchanged context, as the
+    oracle does for any row count), n sized to ~budget_s."""
+    import oracle.attn_oracle as ao
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    X = inp.x_all.float().numpy()
+    Wq, Wk, Wv, Wo = (t.float().numpy() for t in (inp.w_q, inp.w_k, inp.w_v, inp.w_o))
+
+    def run(n):
+        t = time.perf_counter()
+        ao.tsp_attention(X, Wq, Wk, Wv, Wo, w.H, w.Hkv, w.P, w.rank, order=w.order(), causal=w.causal,
+                         rows=list(range(n)))
+        return time.perf_counter() - t
+
+    n = min(w.T, 16)
+    dt = run(n)
+    while dt < 0.25 * budget_s and n < w.T:
+        n = min(w.T, max(n + 1, int(n * min(8.0, 0.6 * budget_s / max(dt, 1e-3)))))
+        dt = run(n)
+    # flops of the sampled rows: their projections, their attention pairs
+    pairs = sum(w.rank * w.T + i + 1 for i in range(n)) if w.causal else n * w.S
+    flops = 4 * n * w.d * w.H * w.dh + 4 * n * w.d * w.Hkv * w.dh + 4 * w.dh * w.H * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} of the rank's {w.T} query rows (the oracle also projects the keys and values "
+                      f"of all {w.S} positions), fp64 numpy attention oracle, {dt:.2f} s"}
+
+
+def bench_attention(args):
+    import torch
+    import oracle.attn_oracle as ao
+    from sharded_transformer_mlp_amd.binding import TspAttn
+    from sharded_transformer_mlp_amd.inputs import attn_workload, make_attn_inputs
+
+    name = args.workload if args.workload != "llama8b" else "attn_llama8b"
+    w = attn_workload(name)
+    dev = torch.device("cuda:0")
+    log(f"attention workload {w.name}: generating inputs")
+    inp = make_attn_inputs(w)
+    x_all = inp.x_all.to(dev)
+    t = time.perf_counter()
+    attn = TspAttn(inp.w_q.to(dev), inp.w_k.to(dev), inp.w_v.to(dev), inp.w_o.to(dev), w.H, w.Hkv, w.P,
+                   order=w.order(), causal=w.causal, T_max=w.T)
+    pack_ms = (time.perf_counter() - t) * 1e3
+    # the exchange, before timing: every other rank's keys and values
+    for rho in range(w.P):
+        if rho != w.rank:
+            attn.project_kv(x_all[rho * w.T:(rho + 1) * w.T].contiguous(), rho)
+    x = x_all[w.rank * w.T:(w.rank + 1) * w.T].contiguous()
+    y = torch.empty(w.T, w.d, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        attn.forward(x, w.rank, y)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} steps")
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    attn.read_timing()
+    attn.set_timing(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    attn.set_timing(False)
+    kernels = {k: v[0] / max(v[1], 1) for k, v in attn.read_timing().items()}
+    log(f"ms/step {ms:.4f}; kernels {kernels}")
+    total = ao.attention_flops(w.T, w.d, w.H, w.Hkv, w.dh, w.P, w.rank, w.causal)
+    value = total / (ms * 1e-3) / 1e12
+    dom = max(kernels, key=lambda k: kernels[k])
+    flops, byts = attn_kernel_work(w, dom)
+    roof = {"bound": "mfma", "achieved": flops / (kernels[dom] * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = read_traffic(w.name, dom)
+    roof.update(kernel=dom, kernel_ms=kernels[dom], algorithmic_bytes=byts, algorithmic_flops=flops)
+    out = {
+        "metric": METRIC_ATTN, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded normal tokens and weights, bf16-rounded)",
+        "config": {"workload": w.name, "T": w.T, "S": w.S, "d": w.d, "H": w.H, "Hkv": w.Hkv, "dh": w.dh,
+                   "P": w.P, "rank": w.rank, "causal": w.causal, "order": w.order(),
+                   "parallelism": "one TSP rank (head-group loop on one GPU; other ranks' keys/values "
+                                  "projected before timing)"},
+        "pct_of_peak": value / PEAK_BF16_TFLOPS * 100.0,
+        "kernels_ms": kernels, "pack_ms": pack_ms, "roofline": roof, "cpu_baseline": None, "pass": "attention",
+        "env": {"gpu": torch.cuda.get_device_name(0), "torch": torch.__version__, "hip": torch.version.hip},
+    }
+    attn.close()
+    del x_all, x, y
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline_attn(w, inp, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
 def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):
     """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
     import torch
@@ -193,8 +330,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the HBM-read and MFMA ceiling probes")
     ap.add_argument("--calibrate-copy", action="store_true", help="only run the copy kernel used to scale counters")
-    ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
-                    help="forward (the headline metric) or the backward (gradients for a seeded dY)")
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward", "attention"), default="forward",
+                    help="forward (the headline metric), the backward (gradients for a seeded dY) or the "
+                         "attention block")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -203,6 +341,13 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.which == "attention":
+        import torch
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(1)
+        bench_attention(args)
         return
 
     import torch

@@ -113,7 +113,7 @@ def attention_unsharded(X, Wq, Wk, Wv, Wo, H: int, Hkv: int, causal: bool = True
 
 def tsp_attention(X_all, Wq, Wk, Wv, Wo, H: int, Hkv: int, P: int, rank: int,
                   order: Optional[Sequence[int]] = None, causal: bool = True,
-                  round_bf16: bool = False) -> np.ndarray:
+                  round_bf16: bool = False, rows: Optional[Sequence[int]] = None) -> np.ndarray:
     """Rank ``rank``'s output rows of the attention block under TSP.
 
     X_all: the whole S x d sequence (rank rho's tokens are rows
@@ -121,7 +121,8 @@ def tsp_attention(X_all, Wq, Wk, Wv, Wo, H: int, Hkv: int, P: int, rank: int,
     key/value exchange delivers. order: the head groups in the order the
     rank visits them (default: rank, rank+1, ... mod P). round_bf16 rounds Q,
     K, V and the attention output to bfloat16 before they are used (a
-    diagnostic of the kernels' stored intermediates, not the bar).
+    diagnostic of the kernels' stored intermediates, not the bar). rows: only
+    these of the rank's token rows (queries are independent of each other).
     """
     X_all = _f64(X_all)
     S, d = X_all.shape
@@ -137,16 +138,19 @@ def tsp_attention(X_all, Wq, Wk, Wv, Wo, H: int, Hkv: int, P: int, rank: int,
     rnd = _round_bf16 if round_bf16 else (lambda a: a)
     X_r = X_all[rank * T:(rank + 1) * T]
     q_pos = np.arange(rank * T, (rank + 1) * T)
+    if rows is not None:
+        X_r, q_pos = X_r[np.asarray(rows)], q_pos[np.asarray(rows)]
+    Tq = len(q_pos)
     k_pos = np.arange(S)
-    Y = np.zeros((T, d))
+    Y = np.zeros((Tq, d))
     for s in order:
         cq, ckv = head_columns(s, Hs, dh), head_columns(s, Hks, dh)
-        Q = rnd(X_r @ _f64(Wq)[:, cq]).reshape(T, Hs, dh)
+        Q = rnd(X_r @ _f64(Wq)[:, cq]).reshape(Tq, Hs, dh)
         # sequence-wise exchange: every rank's keys and values of head group s
         K = rnd(np.concatenate([X_all[rho * T:(rho + 1) * T] @ _f64(Wk)[:, ckv] for rho in range(P)]))
         V = rnd(np.concatenate([X_all[rho * T:(rho + 1) * T] @ _f64(Wv)[:, ckv] for rho in range(P)]))
         O = attention_heads(Q, K.reshape(S, Hks, dh), V.reshape(S, Hks, dh), q_pos, k_pos, causal, Hs // Hks)
-        Y += rnd(O.reshape(T, Hs * dh)) @ _f64(Wo)[cq, :]
+        Y += rnd(O.reshape(Tq, Hs * dh)) @ _f64(Wo)[cq, :]
     return Y
 
 

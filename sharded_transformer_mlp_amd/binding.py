@@ -32,6 +32,15 @@ SIGNATURES = {
     "tsp_mlp_set_timing": (_i32, [_vp, _i32]),
     "tsp_mlp_read_timing": (_i32, [_vp, _i32, _vp, ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(_i64), ctypes.POINTER(_i32)]),
+    "tsp_attn_create": (_i32, [ctypes.POINTER(_vp), _i64, _i64, _i32, _i32, _i32, _i32, _i32,
+                               ctypes.POINTER(_i32), _vp, _vp, _vp, _vp, _vp]),
+    "tsp_attn_project_kv": (_i32, [_vp, _i64, _i32, _vp, _vp]),
+    "tsp_attn_forward": (_i32, [_vp, _i64, _i32, _vp, _vp, _vp]),
+    "tsp_attn_destroy": (_i32, [_vp]),
+    "tsp_attn_set_timing": (_i32, [_vp, _i32]),
+    "tsp_attn_read_timing": (_i32, [_vp, _i32, _vp, ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(_i64), ctypes.POINTER(_i32)]),
+    "tsp_attn_sizes": (_i32, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "tsp_probe_hbm_read": (_i32, [_i64, _i32, _vp, ctypes.POINTER(ctypes.c_double)]),
     "tsp_probe_mfma_bf16": (_i32, [_i32, _vp, ctypes.POINTER(ctypes.c_double)]),
     "tsp_status_string": (ctypes.c_char_p, [_i32]),
@@ -204,6 +213,85 @@ class TspMLP:
     def close(self) -> None:
         if getattr(self, "handle", None):
             check(lib().tsp_mlp_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class TspAttn:
+    """One rank's attention block under TSP on the GPU (bf16).
+
+    w_q: d x (H dh), w_k / w_v: d x (Hkv dh), w_o: (H dh) x d, contiguous
+    bf16 CUDA tensors. ``order``: the head groups in the order the rank visits
+    them (default 0..P-1). The handle owns the sequence-wide key/value
+    context: ``project_kv(x, rank)`` fills rank ``rank``'s rows (what that
+    rank computes and sends), ``forward(x, rank)`` computes rank ``rank``'s
+    output, writing its own rows first.
+    """
+
+    def __init__(self, w_q, w_k, w_v, w_o, H: int, Hkv: int, P: int, order=None, causal: bool = True,
+                 T_max: int = 8, stream=None):
+        import torch
+        for w in (w_q, w_k, w_v, w_o):
+            if not (w.is_cuda and w.is_contiguous() and w.dtype == torch.bfloat16):
+                raise ValueError("weights must be contiguous bf16 CUDA tensors")
+        self.d = w_q.shape[0]
+        self.H, self.Hkv, self.P = H, Hkv, P
+        self.dh = w_q.shape[1] // H
+        self.order = list(range(P)) if order is None else [int(s) for s in order]
+        o = _order_array(self.order)
+        h = _vp()
+        self._stream = _stream_ptr(stream)
+        check(lib().tsp_attn_create(ctypes.byref(h), int(T_max), int(self.d), int(H), int(Hkv), int(self.dh),
+                                    int(P), int(bool(causal)), o[0], w_q.data_ptr(), w_k.data_ptr(),
+                                    w_v.data_ptr(), w_o.data_ptr(), self._stream))
+        self.handle = h
+        self.T_max = int(T_max)
+
+    def _check_x(self, x):
+        import torch
+        if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous() or x.shape[1] != self.d:
+            raise ValueError("x must be a contiguous bf16 CUDA tensor T x d")
+
+    def project_kv(self, x, rank: int, stream=None) -> None:
+        self._check_x(x)
+        check(lib().tsp_attn_project_kv(self.handle, x.shape[0], int(rank), x.data_ptr(), _stream_ptr(stream)))
+
+    def forward(self, x, rank: int, y=None, stream=None):
+        import torch
+        self._check_x(x)
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty(T, self.d, dtype=torch.float32, device=x.device)
+        elif y.dtype != torch.float32 or not y.is_contiguous() or tuple(y.shape) != (T, self.d):
+            raise ValueError("y must be a contiguous fp32 T x d tensor")
+        check(lib().tsp_attn_forward(self.handle, T, int(rank), x.data_ptr(), y.data_ptr(), _stream_ptr(stream)))
+        return y
+
+    def sizes(self):
+        p, w, c = _i64(), _i64(), _i64()
+        check(lib().tsp_attn_sizes(self.handle, ctypes.byref(p), ctypes.byref(w), ctypes.byref(c)))
+        return p.value, w.value, c.value
+
+    def set_timing(self, enable: bool) -> None:
+        check(lib().tsp_attn_set_timing(self.handle, int(bool(enable))))
+
+    def read_timing(self, max_kernels: int = 8):
+        """{kernel name: (total ms, launches)} since the last read."""
+        names = (ctypes.c_char * 64 * max_kernels)()
+        ms = (ctypes.c_double * max_kernels)()
+        n_l = (_i64 * max_kernels)()
+        n = _i32()
+        check(lib().tsp_attn_read_timing(self.handle, max_kernels, names, ms, n_l, ctypes.byref(n)))
+        return {bytes(names[i]).split(b"\0")[0].decode(): (ms[i], n_l[i]) for i in range(n.value)}
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            check(lib().tsp_attn_destroy(self.handle))
             self.handle = None
 
     def __del__(self):

@@ -1,7 +1,9 @@
 // C ABI of the sharded gated-MLP hot path: argument checks, the per-handle
 // packed weights and workspace, and the per-forward launch plan.
 #include "tsp_mlp.h"
+#include "tsp_attn.h"
 
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdint.h>
@@ -10,6 +12,7 @@
 #include <string>
 #include <vector>
 
+#include "attn.h"
 #include "launch.h"
 
 namespace {
@@ -126,16 +129,23 @@ tsp_status_t timed_launch(tsp_mlp* h, const char* name, hipStream_t st, Fn&& lau
     return TSP_OK;
 }
 
-void release(tsp_mlp* h) {
-    if (!h) return;
+void free_buffers(tsp_mlp* h) {
     for (EventPair& e : h->pool) {
         if (e.start) (void)hipEventDestroy(e.start);
         if (e.stop) (void)hipEventDestroy(e.stop);
     }
+    h->pool.clear();
     if (h->order_dev) (void)hipFree(h->order_dev);
     if (h->packed) (void)hipFree(h->packed);
     if (h->work) (void)hipFree(h->work);
     if (h->bwd) (void)hipFree(h->bwd);
+    h->order_dev = nullptr;
+    h->packed = h->work = h->bwd = nullptr;
+}
+
+void release(tsp_mlp* h) {
+    if (!h) return;
+    free_buffers(h);
     delete h;
 }
 
@@ -539,9 +549,22 @@ tsp_status_t tsp_mlp_set_timing(tsp_mlp_t h, int32_t enable) {
     return TSP_OK;
 }
 
+namespace {
+tsp_status_t read_timing(tsp_mlp* h, int32_t max_kernels, char (*names)[64], double* total_ms, int64_t* launches,
+                         int32_t* n_kernels);
+}  // namespace
+
 tsp_status_t tsp_mlp_read_timing(tsp_mlp_t h, int32_t max_kernels, char (*names)[64], double* total_ms,
                                  int64_t* launches, int32_t* n_kernels) {
     if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
+    return read_timing(h, max_kernels, names, total_ms, launches, n_kernels);
+}
+
+}  // extern "C"
+
+namespace {
+tsp_status_t read_timing(tsp_mlp* h, int32_t max_kernels, char (*names)[64], double* total_ms, int64_t* launches,
+                         int32_t* n_kernels) {
     if (max_kernels < 0 || (max_kernels > 0 && (!names || !total_ms || !launches)) || !n_kernels)
         return fail(TSP_ERR_INVALID_ARG, "bad output arrays");
     DeviceGuard guard(h->device);
@@ -560,6 +583,240 @@ tsp_status_t tsp_mlp_read_timing(tsp_mlp_t h, int32_t max_kernels, char (*names)
         kt.launches = 0;
     }
     *n_kernels = n < max_kernels ? n : max_kernels;
+    return TSP_OK;
+}
+}  // namespace
+
+// ---- attention block -------------------------------------------------------
+
+// The attention handle reuses the MLP handle's device, stream, order, event
+// timing and buffers: `packed` holds the Q/K/V records, `work` the query and
+// attention-output buffers and the split partials of the output projection.
+struct tsp_attn : tsp_mlp {
+    int32_t H = 0, Hkv = 0, causal = 1;
+    int64_t Hs = 0, Hks = 0, Fq = 0, Fqkv = 0, S_pad = 0;
+    void* packed_o = nullptr;                  // output-projection records (rows of Wo)
+    int64_t packed_o_bytes = 0, rec_qkv = 0, rec_o = 0;
+    void* ctx = nullptr;                       // K context (S_pad x Hkv 128), then V^T (Hkv 128 x S_pad)
+    int64_t ctx_bytes = 0, o_off = 0;
+};
+
+namespace {
+
+void release_attn(tsp_attn* h) {
+    if (!h) return;
+    free_buffers(h);
+    if (h->packed_o) (void)hipFree(h->packed_o);
+    if (h->ctx) (void)hipFree(h->ctx);
+    delete h;
+}
+
+uint16_t* attn_q(tsp_attn* h) { return static_cast<uint16_t*>(h->work); }
+uint16_t* attn_o(tsp_attn* h) { return reinterpret_cast<uint16_t*>(static_cast<char*>(h->work) + h->o_off); }
+uint16_t* attn_k(tsp_attn* h) { return static_cast<uint16_t*>(h->ctx); }
+uint16_t* attn_vt(tsp_attn* h) { return static_cast<uint16_t*>(h->ctx) + h->S_pad * h->Hkv * tsp::ATT_DH; }
+
+tsp_status_t attn_check_call(tsp_attn* h, int64_t T, int32_t rank, const void* X) {
+    if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
+    if (T < 1 || T > h->T_max) return fail(TSP_ERR_INVALID_ARG, "T=%lld out of [1, T_max=%lld]", (long long)T, (long long)h->T_max);
+    if (T % 8) return fail(TSP_ERR_UNSUPPORTED, "T=%lld is not a multiple of 8", (long long)T);
+    if (rank < 0 || rank >= h->P) return fail(TSP_ERR_INVALID_ARG, "rank=%d out of [0, P=%d)", rank, h->P);
+    if (!X) return fail(TSP_ERR_INVALID_ARG, "X is NULL");
+    if (!aligned16(X)) return fail(TSP_ERR_INVALID_ARG, "X must be 16-byte aligned");
+    return TSP_OK;
+}
+
+tsp_status_t attn_project(tsp_attn* h, int64_t T, int32_t rank, const void* X, hipStream_t st) {
+    tsp::ProjArgs p;
+    p.packed = static_cast<const uint16_t*>(h->packed);
+    p.x = static_cast<const uint16_t*>(X);
+    p.q = attn_q(h);
+    p.kc = attn_k(h);
+    p.vt = attn_vt(h);
+    p.order = h->order_dev;
+    p.rec_elems = h->rec_qkv;
+    p.ldq = h->H * tsp::ATT_DH;
+    p.ldk = h->Hkv * tsp::ATT_DH;
+    p.ldv = h->S_pad;
+    p.row0 = (int64_t)rank * T;
+    p.T = (int)T; p.d = (int)h->d; p.P = h->P; p.Hs = (int)h->Hs; p.Hks = (int)h->Hks;
+    return timed_launch(h, "attn_qkv", st, [&] { return tsp::launch_qkv(p, st); });
+}
+
+}  // namespace
+
+extern "C" {
+
+tsp_status_t tsp_attn_create(tsp_attn_t* out, int64_t T_max, int64_t d, int32_t H, int32_t Hkv, int32_t dh,
+                             int32_t P, int32_t causal, const int32_t* order, const void* w_q, const void* w_k,
+                             const void* w_v, const void* w_o, hipStream_t stream) {
+    if (!out) return fail(TSP_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (T_max < 1 || T_max > kMaxDim) return fail(TSP_ERR_INVALID_ARG, "T_max=%lld out of [1, 2^30]", (long long)T_max);
+    if (d < 1 || d > kMaxDim) return fail(TSP_ERR_INVALID_ARG, "d=%lld out of [1, 2^30]", (long long)d);
+    if (H < 1 || Hkv < 1 || dh < 1 || P < 1) return fail(TSP_ERR_INVALID_ARG, "H, Hkv, dh and P must be positive");
+    if (H % Hkv) return fail(TSP_ERR_INVALID_ARG, "Hkv=%d does not divide H=%d", Hkv, H);
+    if (Hkv % P) return fail(TSP_ERR_INVALID_ARG, "P=%d does not divide Hkv=%d", P, Hkv);
+    if (order) {
+        std::vector<char> seen((size_t)P, 0);
+        for (int32_t k = 0; k < P; ++k) {
+            const int32_t s = order[k];
+            if (s < 0 || s >= P || seen[(size_t)s]) return fail(TSP_ERR_INVALID_ARG, "order is not a permutation of 0..P-1 (entry %d = %d)", k, s);
+            seen[(size_t)s] = 1;
+        }
+    }
+    if (!w_q || !w_k || !w_v || !w_o) return fail(TSP_ERR_INVALID_ARG, "weight pointer is NULL");
+    if (!aligned16(w_q) || !aligned16(w_k) || !aligned16(w_v) || !aligned16(w_o))
+        return fail(TSP_ERR_INVALID_ARG, "weight pointers must be 16-byte aligned");
+    const int32_t G = H / Hkv;
+    if (dh != tsp::ATT_DH) return fail(TSP_ERR_UNSUPPORTED, "dh=%d: the kernels take dh = 128", dh);
+    if (!(G == 1 || G == 2 || G % 4 == 0)) return fail(TSP_ERR_UNSUPPORTED, "H/Hkv=%d is not 1, 2 or a multiple of 4", G);
+    if ((H / P) % 2) return fail(TSP_ERR_UNSUPPORTED, "H/P=%d is odd", H / P);
+    if (d % 256) return fail(TSP_ERR_UNSUPPORTED, "d=%lld is not a multiple of 256", (long long)d);
+    // the context's 32-bit buffer offsets span 128 rows of V^T (one head)
+    if (P * T_max > (int64_t(1) << 22) || T_max * (int64_t)H * dh > (int64_t(1) << 40) / 2)
+        return fail(TSP_ERR_UNSUPPORTED, "T_max too large for this head count");
+
+    tsp_attn* h = new (std::nothrow) tsp_attn;
+    if (!h) return fail(TSP_ERR_OOM, "host allocation failed");
+    h->T_max = T_max; h->d = d; h->P = P; h->H = H; h->Hkv = Hkv; h->causal = causal ? 1 : 0;
+    h->dtype = TSP_DTYPE_BF16; h->stream = stream;
+    h->Hs = H / P; h->Hks = Hkv / P;
+    h->Fq = h->Hs * dh;
+    h->Fqkv = (h->Hs + 2 * h->Hks) * dh;
+    h->f = (int64_t)H * dh; h->F = h->Fq;
+    h->S_pad = (P * T_max + 63) / 64 * 64;
+    h->order.resize((size_t)P);
+    for (int32_t k = 0; k < P; ++k) h->order[(size_t)k] = order ? order[k] : k;
+    hipError_t e = hipGetDevice(&h->device);
+    if (e != hipSuccess) { release_attn(h); return hip_fail(e, "hipGetDevice"); }
+
+    h->rec_qkv = d * h->Fqkv;
+    h->rec_o = h->Fq * d;
+    h->packed_bytes = h->rec_qkv * P * 2;
+    h->packed_o_bytes = h->rec_o * P * 2;
+    const int64_t qo = (T_max * H * dh * 2 + 255) / 256 * 256;
+    h->o_off = qo;
+    h->part_off = 2 * qo;
+    h->work_bytes = 2 * qo + tsp::down_split_bytes(T_max, (int)d, P);
+    h->ctx_bytes = 2 * h->S_pad * Hkv * dh * 2;
+    if ((e = hipMalloc(&h->order_dev, sizeof(int32_t) * (size_t)P)) != hipSuccess ||
+        (e = hipMalloc(&h->packed, (size_t)h->packed_bytes)) != hipSuccess ||
+        (e = hipMalloc(&h->packed_o, (size_t)h->packed_o_bytes)) != hipSuccess ||
+        (e = hipMalloc(&h->work, (size_t)h->work_bytes)) != hipSuccess ||
+        (e = hipMalloc(&h->ctx, (size_t)h->ctx_bytes)) != hipSuccess) {
+        const bool oom = e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation;
+        release_attn(h);
+        (void)hipGetLastError();
+        return oom ? fail(TSP_ERR_OOM, "device allocation of packed weights / workspace / context failed")
+                   : hip_fail(e, "hipMalloc");
+    }
+    e = hipMemcpyAsync(h->order_dev, h->order.data(), sizeof(int32_t) * (size_t)P, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipMemsetAsync(h->ctx, 0, (size_t)h->ctx_bytes, stream);
+    if (e != hipSuccess) { release_attn(h); return hip_fail(e, "context set-up"); }
+    e = tsp::launch_pack_qkv_bf16(w_q, w_k, w_v, h->packed, h->order_dev, h->rec_qkv, (int)d, H, Hkv, dh, P, stream);
+    if (e == hipSuccess)
+        e = tsp::launch_pack_rows_bf16(w_o, h->packed_o, h->order_dev, h->rec_o, (int)d, (int)h->Fq, P, stream);
+    if (e != hipSuccess) { release_attn(h); return hip_fail(e, "pack launch"); }
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) { release_attn(h); return hip_fail(e, "hipStreamSynchronize after packing"); }
+    *out = h;
+    return TSP_OK;
+}
+
+tsp_status_t tsp_attn_project_kv(tsp_attn_t h, int64_t T, int32_t rank, const void* X, hipStream_t stream) {
+    tsp_status_t s = attn_check_call(h, T, rank, X);
+    if (s != TSP_OK) return s;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return fail(TSP_ERR_HIP, "cannot select the handle's device");
+    return attn_project(h, T, rank, X, stream ? stream : h->stream);
+}
+
+tsp_status_t tsp_attn_forward(tsp_attn_t h, int64_t T, int32_t rank, const void* X, float* Y, hipStream_t stream) {
+    tsp_status_t s = attn_check_call(h, T, rank, X);
+    if (s != TSP_OK) return s;
+    if (!Y) return fail(TSP_ERR_INVALID_ARG, "Y is NULL");
+    if (!aligned16(Y)) return fail(TSP_ERR_INVALID_ARG, "Y must be 16-byte aligned");
+    const uintptr_t x0 = reinterpret_cast<uintptr_t>(X), x1 = x0 + (uintptr_t)(T * h->d * 2);
+    const uintptr_t y0 = reinterpret_cast<uintptr_t>(Y), y1 = y0 + (uintptr_t)(T * h->d * 4);
+    if (x0 < y1 && y0 < x1) return fail(TSP_ERR_INVALID_ARG, "Y overlaps X");
+    hipStream_t st = stream ? stream : h->stream;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return fail(TSP_ERR_HIP, "cannot select the handle's device");
+
+    s = attn_project(h, T, rank, X, st);
+    if (s != TSP_OK) return s;
+
+    tsp::AttnArgs a;
+    a.q = attn_q(h);
+    a.kc = attn_k(h);
+    a.vt = attn_vt(h);
+    a.o = attn_o(h);
+    a.order = h->order_dev;
+    a.ldq = h->H * tsp::ATT_DH;
+    a.ldk = h->Hkv * tsp::ATT_DH;
+    a.ldv = h->S_pad;
+    a.T = (int)T; a.S = (int)(h->P * T); a.row0 = (int)(rank * T);
+    a.P = h->P; a.Hs = (int)h->Hs; a.Hks = (int)h->Hks; a.causal = h->causal;
+    const int G = (int)(h->Hs / h->Hks);
+    a.hw = G < 4 ? G : 4;
+    a.qs = 4 / a.hw;
+    a.n_hq = G / a.hw;
+    a.n_qt = (int)((T + 64 * a.qs - 1) / (64 * a.qs));
+    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)tsp::ATT_DH));
+    s = timed_launch(h, "attn_core", st, [&] { return tsp::launch_attn(a, st); });
+    if (s != TSP_OK) return s;
+
+    tsp::Bf16Args o;
+    o.packed = static_cast<const uint16_t*>(h->packed_o);
+    o.x = nullptr;
+    o.h = attn_o(h);
+    o.y = Y;
+    o.part = reinterpret_cast<float*>(static_cast<char*>(h->work) + h->part_off);
+    o.shard_elems = h->rec_o;
+    o.down_off = 0;
+    o.T = (int)T; o.d = (int)h->d; o.f = (int)h->f; o.F = (int)h->Fq; o.P = h->P;
+    o.swiglu = 0;
+    const int cd = tsp::choose_down_cfg(o.T, o.d, o.F, o.P);
+    if (cd < 0) return fail(TSP_ERR_UNSUPPORTED, "no tile shape fits the output projection");
+    const int split = tsp::choose_down_split(o.T, o.d, o.P, cd);
+    if (split > 1 && (int64_t)split * T * o.d * 4 > h->work_bytes - h->part_off)
+        return fail(TSP_ERR_HIP, "internal: split partials exceed the workspace");
+    s = timed_launch(h, "attn_out", st, [&] { return tsp::launch_down_tiled(o, cd, split, st); });
+    if (s != TSP_OK || split == 1) return s;
+    return timed_launch(h, "reduce_partials", st, [&] { return tsp::launch_reduce_partials(o.part, split, T * o.d, Y, st); });
+}
+
+tsp_status_t tsp_attn_destroy(tsp_attn_t h) {
+    if (!h) return TSP_OK;
+    tsp_status_t s = TSP_OK;
+    {
+        DeviceGuard guard(h->device);
+        hipError_t e = hipStreamSynchronize(h->stream);
+        if (e != hipSuccess) s = hip_fail(e, "hipStreamSynchronize in destroy");
+        for (size_t i = 0; i < h->used; ++i) (void)hipEventSynchronize(h->pool[i].stop);
+        release_attn(h);
+    }
+    return s;
+}
+
+tsp_status_t tsp_attn_set_timing(tsp_attn_t h, int32_t enable) {
+    if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
+    h->timing = enable != 0;
+    return TSP_OK;
+}
+
+tsp_status_t tsp_attn_read_timing(tsp_attn_t h, int32_t max_kernels, char (*names)[64], double* total_ms,
+                                  int64_t* launches, int32_t* n_kernels) {
+    if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
+    return read_timing(h, max_kernels, names, total_ms, launches, n_kernels);
+}
+
+tsp_status_t tsp_attn_sizes(tsp_attn_t h, int64_t* packed_bytes, int64_t* workspace_bytes, int64_t* context_bytes) {
+    if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
+    if (packed_bytes) *packed_bytes = h->packed_bytes + h->packed_o_bytes;
+    if (workspace_bytes) *workspace_bytes = h->work_bytes;
+    if (context_bytes) *context_bytes = h->ctx_bytes;
     return TSP_OK;
 }
 

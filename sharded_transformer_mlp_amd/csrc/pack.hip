@@ -141,3 +141,19 @@ hipError_t launch_pack_f32(const void* wg, const void* wu, const void* wd, void*
 }
 
 }  // namespace tsp
+
+namespace tsp {
+
+// Row shards of one (P F) x d matrix, F rows per shard, packed like the down
+// part of an MLP record with no gate/up part before it (the attention
+// block's output projection).
+hipError_t launch_pack_rows_bf16(const void* w, void* dst, const int32_t* order, int64_t rec_elems, int d,
+                                 int F, int P, hipStream_t st) {
+    const int64_t chunks = (int64_t)d * F / 8;
+    dim3 g((unsigned)std::min<int64_t>((chunks + 255) / 256, 4096), P);
+    hipLaunchKernelGGL(pack_down_bf16, g, dim3(256), 0, st, (const uint16_t*)w, (uint16_t*)dst, order, rec_elems,
+                       (int64_t)0, d, F, chunks);
+    return hipGetLastError();
+}
+
+}  // namespace tsp

@@ -178,3 +178,77 @@ def sample_rows(T: int, n: int, seed: int, must_include=None) -> torch.Tensor:
     mask[base] = False
     extra = perm[mask[perm]][: n - len(base)]
     return torch.sort(torch.cat([base, extra]))[0]
+
+
+# ---- attention block ----------------------------------------------------
+#
+# Recipe: g = torch.Generator('cpu').manual_seed(seed); fp32 torch.randn in
+# the order X (the whole S = P T token sequence, S x d), Wq (d x H dh), Wk,
+# Wv (d x Hkv dh), Wo (H dh x d); X ~ N(0, 1), Wq, Wk, Wv ~ N(0, 1/d),
+# Wo ~ N(0, 1/(H dh)); all rounded to bf16 (nearest even). Rank r's tokens
+# are rows [r T, (r + 1) T) of X. With these scales a query and key have
+# O(1) entries and the softmax logits q.k/sqrt(dh) are O(1).
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    """Shape of one rank's TSP attention block."""
+
+    name: str
+    T: int            # tokens per sequence shard (the rank's queries)
+    d: int
+    H: int            # query heads
+    Hkv: int          # key/value heads
+    dh: int
+    P: int            # ranks = head groups = sequence shards
+    rank: int         # the rank whose forward is computed
+    seed: int
+    causal: bool = True
+    note: str = ""
+
+    @property
+    def S(self) -> int:
+        return self.P * self.T
+
+    def order(self):
+        """The rank visits head groups rank, rank + 1, ... mod P."""
+        return [(self.rank + k) % self.P for k in range(self.P)]
+
+    def with_(self, **kw) -> "AttnWorkload":
+        from dataclasses import replace
+        return replace(self, **kw)
+
+
+ATTN_WORKLOADS = {
+    "llama3-8b-attn-bf16-T4096-d4096-H32-Hkv8-P8-rank3": AttnWorkload(
+        "llama3-8b-attn-bf16-T4096-d4096-H32-Hkv8-P8-rank3", T=4096, d=4096, H=32, Hkv=8, dh=128, P=8, rank=3,
+        seed=5, note="Llama-3-8B attention shape; rank 3's shard of a 32768-token sequence"),
+}
+ATTN_ALIASES = {"attn_llama8b": "llama3-8b-attn-bf16-T4096-d4096-H32-Hkv8-P8-rank3"}
+
+
+def attn_workload(name: str) -> AttnWorkload:
+    return ATTN_WORKLOADS[ATTN_ALIASES.get(name, name)]
+
+
+@dataclass
+class AttnInputs:
+    x_all: torch.Tensor   # S x d, bf16
+    w_q: torch.Tensor
+    w_k: torch.Tensor
+    w_v: torch.Tensor
+    w_o: torch.Tensor
+
+    def rank_rows(self, T: int, rank: int) -> torch.Tensor:
+        return self.x_all[rank * T:(rank + 1) * T].contiguous()
+
+
+def make_attn_inputs(w: AttnWorkload) -> AttnInputs:
+    """Draw the attention workload's seeded bf16 tensors (recipe above)."""
+    g = torch.Generator("cpu").manual_seed(w.seed)
+    x = torch.randn(w.S, w.d, generator=g)
+    wq = torch.randn(w.d, w.H * w.dh, generator=g) / math.sqrt(w.d)
+    wk = torch.randn(w.d, w.Hkv * w.dh, generator=g) / math.sqrt(w.d)
+    wv = torch.randn(w.d, w.Hkv * w.dh, generator=g) / math.sqrt(w.d)
+    wo = torch.randn(w.H * w.dh, w.d, generator=g) / math.sqrt(w.H * w.dh)
+    b = lambda t: t.to(torch.bfloat16).contiguous()
+    return AttnInputs(b(x), b(wq), b(wk), b(wv), b(wo))

@@ -1,6 +1,7 @@
 """Host-side checks of the C ABI (no GPU needed, no compute call).
 
-* the library loads and exports every function include/tsp_mlp.h declares;
+* the library loads and exports every function include/tsp_mlp.h and
+  include/tsp_attn.h declare;
 * argument validation returns the documented status before any HIP call.
 """
 import ctypes
@@ -11,18 +12,21 @@ import pytest
 
 from sharded_transformer_mlp_amd import binding as B
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "tsp_mlp.h")
+HEADERS = [os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", h) for h in ("tsp_mlp.h", "tsp_attn.h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tsp_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"\b(tsp_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("tsp_mlp_create", "tsp_mlp_forward", "tsp_mlp_destroy", "tsp_mlp_validate"):
+    for n in ("tsp_mlp_create", "tsp_mlp_forward", "tsp_mlp_destroy", "tsp_mlp_validate", "tsp_attn_create",
+              "tsp_attn_project_kv", "tsp_attn_forward", "tsp_attn_destroy"):
         assert n in names
     assert set(names) == set(B.SIGNATURES), "binding and header disagree"
 
@@ -110,3 +114,30 @@ def test_probes_reject_bad_arguments_before_any_hip_call():
     assert b"reps" in lib.tsp_last_error()
     assert lib.tsp_probe_mfma_bf16(0, None, ctypes.byref(out)) == INV
     assert lib.tsp_probe_mfma_bf16(100, None, None) == INV
+
+
+@pytest.mark.parametrize("args,want", [
+    # T_max, d, H, Hkv, dh, P
+    ((0, 4096, 32, 8, 128, 8), INV),
+    ((16, 4096, 32, 6, 128, 8), INV),             # Hkv does not divide H
+    ((16, 4096, 32, 8, 128, 3), INV),             # P does not divide Hkv
+    ((16, 4096, 32, 8, 64, 8), UNS),              # dh != 128
+    ((16, 4096, 24, 8, 128, 8), UNS),             # H/Hkv = 3
+    ((16, 4096, 24, 8, 128, 8), UNS),
+    ((16, 4096, 8, 8, 128, 8), UNS),              # H/P = 1 is odd
+    ((16, 4000, 32, 8, 128, 8), UNS),             # d % 256
+    ((1 << 21, 4096, 32, 8, 128, 8), UNS),        # context too long for 32-bit offsets
+])
+def test_attn_create_rejects_before_touching_the_device(args, want):
+    lib = B.lib()
+    h = ctypes.c_void_p(1234)
+    fake = ctypes.c_void_p(0x1000)
+    st = lib.tsp_attn_create(ctypes.byref(h), *args, 1, None, fake, fake, fake, fake, None)
+    assert st == want and h.value is None, lib.tsp_last_error()
+
+
+def test_attn_calls_reject_null_handle():
+    lib = B.lib()
+    assert lib.tsp_attn_forward(None, 16, 0, ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), None) == INV
+    assert lib.tsp_attn_project_kv(None, 16, 0, ctypes.c_void_p(0x1000), None) == INV
+    assert lib.tsp_attn_destroy(None) == OK

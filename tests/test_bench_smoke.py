@@ -56,3 +56,19 @@ def test_bench_backward_line(wl):
     d = json.loads(lines[0])
     assert d["pass"] == "backward" and d["unit"] == "TFLOP/s" and d["value"] > 0
     assert d["roofline"]["kernel"].startswith("bwd_") and 0 < d["roofline"]["frac"] < 1
+
+
+def test_bench_attention_line():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print("[gpu] bench --pass attention", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--pass", "attention",
+                        "--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--no-ceilings"],
+                       capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    assert d["pass"] == "attention" and d["unit"] == "TFLOP/s" and d["value"] > 0
+    assert d["roofline"]["kernel"].startswith("attn_") and 0 < d["roofline"]["frac"] < 1

@@ -193,3 +193,11 @@ def test_mutant_no_exchange(monkeypatch):
         return f(Q, K[own], V[own], qp, kp[own], c, g)
     _mutant(monkeypatch, wrap)
     assert not _matches_unsharded()
+
+
+def test_row_subset_equals_full_rows():
+    S, d, H, Hkv, dh, P = 32, 16, 4, 2, 4, 2
+    X, Wq, Wk, Wv, Wo = rand_block(8, S, d, H, Hkv, dh)
+    full = ao.tsp_attention(X, Wq, Wk, Wv, Wo, H, Hkv, P, 1)
+    rows = [0, 5, 15]
+    np.testing.assert_array_equal(ao.tsp_attention(X, Wq, Wk, Wv, Wo, H, Hkv, P, 1, rows=rows), full[rows])
