@@ -58,6 +58,7 @@ def test_bench_backward_line(wl):
     assert d["roofline"]["kernel"].startswith("bwd_") and 0 < d["roofline"]["frac"] < 1
 
 
+@pytest.mark.gpu
 def test_bench_attention_line():
     import torch
     if not torch.cuda.is_available():
