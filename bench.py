@@ -57,7 +57,7 @@ KERNEL_SOURCES = {
     "bwd_transpose_in": ["backward.hip", "common.h"],
     "bwd_transpose_mid": ["backward.hip", "common.h"],
     "attn_qkv": ["attn.hip", "w16.h", "common.h"],
-    "attn_core": ["attn.hip", "common.h"],
+    "attn_core": ["attn_core.hip", "w16.h", "common.h"],
     "attn_out": ["gemm_tiled.hip", "w16.h", "common.h"],
 }
 METRIC_BWD = "sharded gated-MLP backward TFLOP/s (dX and weight gradients; recomputation not counted)"

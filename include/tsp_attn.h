@@ -41,13 +41,17 @@
  * Those rows must have been written by tsp_attn_project_kv with the same T
  * since T last changed; rows never written read as zero.
  *
+ * Context layout (library-owned): K as positions x (Hkv dh); V transposed,
+ * (Hkv dh) x positions, each 32-position group stored as 4 chunks of 8 where
+ * chunk j holds positions 4j..4j+3 and 16+4j..16+4j+3 of the group.
+ *
  * Layouts: row-major, no padding; X is T x d bf16, Y is T x d fp32, w_q is
  * d x (H dh), w_k and w_v are d x (Hkv dh), w_o is (H dh) x d (Y = X W,
  * input x output); head h occupies columns [h dh, (h+1) dh).
  *
  * Shapes the kernels take (else TSP_ERR_UNSUPPORTED): bf16 only; dh = 128;
  * P divides Hkv and Hkv divides H; H / Hkv is 1, 2 or a multiple of 4;
- * H / P even; d a multiple of 256; T a multiple of 8.
+ * H / P even; d a multiple of 256; T a multiple of 32.
  */
 #ifndef TSP_ATTN_H
 #define TSP_ATTN_H
@@ -80,7 +84,7 @@ tsp_status_t tsp_attn_create(tsp_attn_t* out, int64_t T_max, int64_t d, int32_t 
  * The exchange stand-in: projects rank `rank`'s T tokens X (T x d bf16,
  * device) through every head group's K and V columns into the handle's
  * context rows [rank T, (rank + 1) T). Asynchronous on `stream` (NULL = the
- * create stream). 0 <= rank < P, 1 <= T <= T_max, T a multiple of 8.
+ * create stream). 0 <= rank < P, 1 <= T <= T_max, T a multiple of 32.
  */
 tsp_status_t tsp_attn_project_kv(tsp_attn_t h, int64_t T, int32_t rank, const void* X, hipStream_t stream);
 

@@ -42,9 +42,15 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+# Per-source codegen options: the attention kernel keeps its MFMA results in
+# vector registers (its softmax reads every score; results in accumulation
+# registers were copied out one by one).
+EXTRA_FLAGS = {"attn_core.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, tag: str = "", defs=()) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + tag + ".o")
-    cmd = [hipcc(), *HIPFLAGS, *defs, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIPFLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), *defs, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)

@@ -619,7 +619,7 @@ uint16_t* attn_vt(tsp_attn* h) { return static_cast<uint16_t*>(h->ctx) + h->S_pa
 tsp_status_t attn_check_call(tsp_attn* h, int64_t T, int32_t rank, const void* X) {
     if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
     if (T < 1 || T > h->T_max) return fail(TSP_ERR_INVALID_ARG, "T=%lld out of [1, T_max=%lld]", (long long)T, (long long)h->T_max);
-    if (T % 8) return fail(TSP_ERR_UNSUPPORTED, "T=%lld is not a multiple of 8", (long long)T);
+    if (T % 32) return fail(TSP_ERR_UNSUPPORTED, "T=%lld is not a multiple of 32", (long long)T);
     if (rank < 0 || rank >= h->P) return fail(TSP_ERR_INVALID_ARG, "rank=%d out of [0, P=%d)", rank, h->P);
     if (!X) return fail(TSP_ERR_INVALID_ARG, "X is NULL");
     if (!aligned16(X)) return fail(TSP_ERR_INVALID_ARG, "X must be 16-byte aligned");
@@ -685,7 +685,7 @@ tsp_status_t tsp_attn_create(tsp_attn_t* out, int64_t T_max, int64_t d, int32_t 
     h->Fq = h->Hs * dh;
     h->Fqkv = (h->Hs + 2 * h->Hks) * dh;
     h->f = (int64_t)H * dh; h->F = h->Fq;
-    h->S_pad = (P * T_max + 63) / 64 * 64;
+    h->S_pad = (P * T_max + 63) / 64 * 64;           // positions; each 32-group is stored permuted (attn.hip)
     h->order.resize((size_t)P);
     for (int32_t k = 0; k < P; ++k) h->order[(size_t)k] = order ? order[k] : k;
     hipError_t e = hipGetDevice(&h->device);

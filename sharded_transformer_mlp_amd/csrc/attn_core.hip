@@ -1,0 +1,365 @@
+// Causal (or full) softmax attention of one TSP rank's queries over the
+// sequence-wide key/value context, all head groups in one launch (gfx950).
+// Built on its own with MFMA results in vector registers
+// (-mllvm -amdgpu-mfma-vgpr-form): the softmax reads every score, and with
+// accumulation-register results each score was first copied out.
+//
+// "Folding Tensor and Sequence Parallelism for Memory-Efficient Transformer
+// Training & Inference", Abstract: the ranks rebuild the full context through
+// a sequence-wise key/value exchange; "Tensor Parallelism: Splitting the Math",
+// section "Why the column-then-row split - and what happens in attention":
+// a head's attention runs locally on the device that owns the head.
+#include "attn.h"
+#include "common.h"
+#include "w16.h"
+
+namespace tsp {
+
+// ------------------------------------------------------------------ attention
+//
+// Workgroup: 4 waves, each 64 queries of one head against 64-key blocks of
+// the context; the 4 waves share the key/value head (hw heads x qs query
+// sub-tiles, hw * qs = 4), so one K tile and one V tile in LDS serve them all.
+// With v_mfma_f32_16x16x32_bf16 a wave computes S^T = K Q^T (keys as rows:
+// lane l holds 4 consecutive keys of query l % 16), so a query's softmax
+// statistics sit in one lane column and reduce with two cross-lane steps; the
+// probabilities then feed O^T = V^T P^T as the B operand straight from the
+// registers: within a 32-key step, lane group g = l / 16 takes keys 4g..4g+3
+// and 16+4g..16+4g+3 (its own S^T values), and the value context stores each
+// 32-position group in that order (16-byte chunk g = those 8 positions), so
+// the V^T fragment is one 16-byte read. Scores are kept in log2 units (scale log2(e)/sqrt(dh))
+// and exponentiated with v_exp_f32.
+//
+// Context tiles reach LDS by DMA (global_load_lds, 16 bytes per lane, two
+// buffers): K as 64 rows of 256 bytes with the 16-byte chunk c of row r at
+// c ^ (r & 15), V^T as 128 rows of 128 bytes with chunk c at c ^ ((r >> 1) & 7);
+// both make the fragment reads of 16 rows hit distinct banks.
+//
+// Softmax with a fixed exponent reference per query instead of a running
+// maximum: the first block's maximum. O / l does not depend on the reference,
+// and probabilities up to 2^64 (a later block's scores up to 64 above it, in
+// log2 units) are exact enough in fp32 and bf16, so the accumulators are never
+// rescaled (rescaling them, 128 accumulation registers, cost more than the
+// exponentials). A block that exceeds the reference by more than that sets a
+// workgroup flag; the workgroup then finds every query's true maximum in a
+// pass over the keys and starts again with it (rare: logits 44 nats apart).
+
+constexpr int ATT_KROW = 128;   // K tile row (elements)
+constexpr int ATT_VROW = 64;    // V^T tile row (elements)
+
+__device__ __forceinline__ void att_vm_zero() {
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
+}
+
+__device__ inline bf16x8 att_pack8(f32x4 lo, f32x4 hi) {
+    bf16x8 r;
+    r[0] = static_cast<__bf16>(lo[0]); r[1] = static_cast<__bf16>(lo[1]);
+    r[2] = static_cast<__bf16>(lo[2]); r[3] = static_cast<__bf16>(lo[3]);
+    r[4] = static_cast<__bf16>(hi[0]); r[5] = static_cast<__bf16>(hi[1]);
+    r[6] = static_cast<__bf16>(hi[2]); r[7] = static_cast<__bf16>(hi[3]);
+    return r;
+}
+
+__global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds[3][64 * ATT_KROW];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][128 * ATT_VROW];
+    poison_lds(k_lds, sizeof(k_lds));
+    poison_lds(v_lds, sizeof(v_lds));
+
+    // heaviest query tiles first; consecutive workgroups (different XCDs)
+    // take different key/value heads, so each XCD's L2 streams few contexts
+    const int per_qt = a.P * a.Hks * a.n_hq;
+    const int lin = blockIdx.x;
+    const int qt = a.n_qt - 1 - lin / per_qt;
+    int rem = lin - (lin / per_qt) * per_qt;
+    const int hq = rem % a.n_hq;
+    rem /= a.n_hq;
+    const int jl = rem % a.Hks;
+    const int k = rem / a.Hks;
+    const int s = a.order[k];
+    const int64_t kv_col = ((int64_t)s * a.Hks + jl) * 128;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n16 = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = a.Hs / a.Hks;
+    const int hl = jl * G + hq * a.hw + (w % a.hw);
+    const int q_wg = qt * 64 * a.qs;                     // first query of the workgroup
+    const int q0 = q_wg + (w / a.hw) * 64;               // first query of the wave
+    const int64_t qo_col = ((int64_t)k * a.Hs + hl) * 128;
+
+    // Q^T fragments (B operand): query t*16 + n16, head dims ks*32 + 8g .. + 7
+    bf16x8 qf[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int row = min(q0 + t * 16 + n16, a.T - 1);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            qf[t][ks] = *reinterpret_cast<const bf16x8*>(a.q + (int64_t)row * a.ldq + qo_col + ks * 32 + 8 * g);
+    }
+
+    const int q_hi = min(a.T, q_wg + 64 * a.qs);         // queries of the workgroup end here
+    const int kend = a.causal ? min(a.S, a.row0 + q_hi) : a.S;
+    const int nkb = (kend + 63) / 64;
+    const int qpos0 = a.row0 + q0;                       // the wave's first query position
+
+    // DMA of one context block into buffer `buf`: 4 K and 4 V^T instructions
+    // per wave, each 1 KiB of LDS (4 K rows or 8 V^T rows). Buffer loads: the
+    // block's base is scalar, a lane's offset (fixed for the whole loop) 32-bit.
+    int k_off[4], v_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = w * 4 + i;
+        const int kr = j * 4 + (lane >> 4), kc = (lane & 15) ^ (kr & 15);
+        k_off[i] = (int)((kr * a.ldk + kc * 8) * 2);
+        const int vr = j * 8 + (lane >> 3), vc = (lane & 7) ^ ((vr >> 1) & 7);
+        v_off[i] = (int)((vr * a.ldv + vc * 8) * 2);
+    }
+    auto load_k = [&](int kb, int buf) {
+        const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.kc + (int64_t)kb * 64 * a.ldk + kv_col), (short)0, 0x7fffffff, kRawBufferWord3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (TSP_LDS void*)&k_lds[buf][(w * 4 + i) * 512], 16, k_off[i],
+                                                     0, 0, 0);
+    };
+    auto load_v = [&](int kb, int buf) {
+        const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.vt + kv_col * a.ldv + kb * 64), (short)0, 0x7fffffff, kRawBufferWord3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (TSP_LDS void*)&v_lds[buf][(w * 4 + i) * 512], 16, v_off[i],
+                                                     0, 0, 0);
+    };
+
+    __shared__ int restart_flag;
+    f32x4 o[8][4];
+    float m[4], l[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) m[t] = -INFINITY;
+
+    // The key stream runs in 32-key halves of the 64-key tiles: half h of a
+    // tile is its key tiles 2h, 2h+1 (16 keys each) and the P.V step ks2 = h.
+    // K fragments of one 32-dim step of that half (from buffer `buf`), and
+    // the step's 8 MFMAs of S^T = K Q^T (2 key tiles x 4 query tiles); ks == 0
+    // starts the accumulators.
+    auto read_k = [&](int ks, int buf, int h, bf16x8 (&kf)[2]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            kf[u] = *reinterpret_cast<const bf16x8*>(
+                &k_lds[buf][((2 * h + u) * 16 + n16) * ATT_KROW + ((4 * ks + g) ^ n16) * 8]);
+    };
+    auto s_mfma = [&](int ks, const bf16x8 (&kf)[2], f32x4 (&sc)[2][4]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                sc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    kf[u], qf[t][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sc[u][t], 0, 0, 0);
+    };
+    // all four steps, each step's K fragments read one step ahead
+    auto s_half = [&](int buf, int h, f32x4 (&sc)[2][4]) {
+        bf16x8 kf[2][2];
+        read_k(0, buf, h, kf[0]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks + 1 < 4) read_k(ks + 1, buf, h, kf[(ks + 1) & 1]);
+            s_mfma(ks, kf[ks & 1], sc);
+        }
+    };
+    // keys past the query (causal) or past the context end get -inf
+    auto apply_mask = [&](int kb, int h, f32x4 (&sc)[2][4]) {
+        const int kbase = kb * 64 + 32 * h;
+        const int lim_s = a.S - kbase - 4 * g;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int lim_q = a.causal ? qpos0 + t * 16 + n16 - kbase - 4 * g + 1 : 1 << 30;
+            const int lim = min(lim_q, lim_s);
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sc[u][t][i] = u * 16 + i < lim ? sc[u][t][i] : -INFINITY;
+        }
+    };
+    // a query's maximum over the half in log2 units: the lane's 8 keys, then
+    // the 4 lane groups (the scale is positive, so it commutes with the maximum)
+    auto half_max = [&](const f32x4 (&sc)[2][4], int t) {
+        float mx = sc[0][t][0];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[u][t][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        return fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    };
+    // probabilities of query tile t against the fixed reference, added into
+    // the lane's partial sum and packed as the B operand of the P.V step
+    auto softmax_t = [&](f32x4 (&sc)[2][4], int t, bf16x8 (&pb)[4]) {
+        const float ref = m[t] == -INFINITY ? 0.f : m[t];
+        float ls = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][t][i], a.scale_log2, -ref));
+                sc[u][t][i] = pr;
+                ls += pr;
+            }
+        l[t] += ls;
+        pb[t] = att_pack8(sc[0][t], sc[1][t]);
+    };
+    // V^T fragment dt of half h (the 8 keys lane group g multiplies)
+    auto read_v = [&](int buf, int h, int dt) {
+        const int r = dt * 16 + n16;
+        return *reinterpret_cast<const bf16x8*>(&v_lds[buf][r * ATT_VROW + ((4 * h + g) ^ ((r >> 1) & 7)) * 8]);
+    };
+    // O^T += V^T P^T over half h of the V^T tile in buffer `buf`, fragments
+    // read two ahead; vf holds the first two (read early by the caller)
+    auto pv = [&](int buf, int h, const bf16x8 (&pb)[4], bf16x8 (&vf)[3]) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            if (dt + 2 < 8) vf[(dt + 2) % 3] = read_v(buf, h, dt + 2);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                o[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt % 3], pb[t], o[dt][t], 0, 0, 0);
+        }
+    };
+    // half n+1's scores on the matrix cores while the VALU turns half n's
+    // into probabilities, then half n's P.V
+    auto step = [&](int kbuf_next, int h_next, f32x4 (&cur)[2][4], f32x4 (&nxt)[2][4], int vbuf, int h) {
+        bf16x8 pb[4], kf[2][2], vf[3];
+        read_k(0, kbuf_next, h_next, kf[0]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks + 1 < 4) read_k(ks + 1, kbuf_next, h_next, kf[(ks + 1) & 1]);
+            if (ks == 3) {
+                vf[0] = read_v(vbuf, h, 0);
+                vf[1] = read_v(vbuf, h, 1);
+            }
+            s_mfma(ks, kf[ks & 1], nxt);
+            softmax_t(cur, ks, pb);
+        }
+        pv(vbuf, h, pb, vf);
+    };
+    auto last_step = [&](f32x4 (&cur)[2][4], int vbuf, int h) {
+        bf16x8 pb[4], vf[3];
+        vf[0] = read_v(vbuf, h, 0);
+        vf[1] = read_v(vbuf, h, 1);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) softmax_t(cur, t, pb);
+        pv(vbuf, h, pb, vf);
+    };
+
+    // Tiles every query of the workgroup sees in full (no mask) come first and
+    // run software-pipelined (K tiles in 3 buffers, V^T tiles in 2: tile kb's
+    // K is read in its first half and by the previous tile's second half). The
+    // masked tiles (the diagonal, the context end) run one at a time after.
+    const int first_q = a.row0 + q_wg;                   // the workgroup's first query position
+    int n_full = a.causal ? (first_q + 1) / 64 : a.S / 64;
+    n_full = min(n_full, min(nkb, a.S / 64));
+
+    for (int attempt = 0; attempt < 2; ++attempt) {
+        if (tid == 0) restart_flag = 0;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) o[dt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) l[t] = 0.f;
+
+        if (n_full > 0) {
+            f32x4 sa[2][4], sb[2][4];
+            load_k(0, 0);
+            load_v(0, 0);
+            load_k(min(1, nkb - 1), 1);
+            att_vm_zero();
+            __syncthreads();
+            s_half(0, 0, sa);
+            if (attempt == 0) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) m[t] = half_max(sa, t);   // the reference
+            }
+            int kb = 0;
+            for (; kb + 1 < n_full; ++kb) {
+                // buffer (kb+2)%3 held tile kb-1's K, (kb+1)&1 tile kb-1's V^T:
+                // both last read before the previous barrier
+                load_k(min(kb + 2, nkb - 1), (kb + 2) % 3);
+                load_v(kb + 1, (kb + 1) & 1);
+                step(kb % 3, 1, sa, sb, kb & 1, 0);             // scores of this tile's second half
+                step((kb + 1) % 3, 0, sb, sa, kb & 1, 1);       // scores of the next tile's first half
+                att_vm_zero();
+                __syncthreads();
+            }
+            step(kb % 3, 1, sa, sb, kb & 1, 0);
+            last_step(sb, kb & 1, 1);
+            __syncthreads();                             // every read of the buffers is done
+        }
+        // masked tiles, one at a time
+        for (int kb = n_full; kb < nkb; ++kb) {
+            load_k(kb, 0);
+            load_v(kb, 0);
+            att_vm_zero();
+            __syncthreads();
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                f32x4 sc[2][4];
+                s_half(0, h, sc);
+                apply_mask(kb, h, sc);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    if (m[t] == -INFINITY) m[t] = half_max(sc, t);   // the first keys set the reference
+                last_step(sc, 0, h);
+            }
+            __syncthreads();
+        }
+        // a probability above 2^64 (scores more than 64 log2 units above the
+        // reference) shows in the lane's partial sum; an unneeded restart on
+        // many large ones only costs time
+        bool over = false;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) over |= !(l[t] <= 1.8446744e19f);
+        if (__any(over)) restart_flag = 1;
+        __syncthreads();
+        if (!restart_flag) break;                        // same value in every wave
+        // rare: take every query's true maximum over all keys, start again
+        for (int kb = 0; kb < nkb; ++kb) {
+            load_k(kb, 0);
+            att_vm_zero();
+            __syncthreads();
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                f32x4 sc[2][4];
+                s_half(0, h, sc);
+                apply_mask(kb, h, sc);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) m[t] = fmaxf(m[t], half_max(sc, t));
+            }
+            __syncthreads();                             // reads done before the next tile's DMA
+        }
+    }
+
+    // normalise and store: lane holds O[query t*16 + n16][dims dt*16 + 4g .. + 3]
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        float lt = l[t];
+        lt += __shfl_xor(lt, 16);
+        lt += __shfl_xor(lt, 32);
+        const float inv = 1.0f / lt;
+        const int row = q0 + t * 16 + n16;
+        if (row < a.T) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const f32x4 v = o[dt][t] * inv;
+                *reinterpret_cast<uint2*>(a.o + (int64_t)row * a.ldq + qo_col + dt * 16 + 4 * g) =
+                    pack4_bf16(v[0], v[1], v[2], v[3]);
+            }
+        }
+    }
+}
+
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
+    const int64_t wgs = (int64_t)a.n_qt * a.P * a.Hks * a.n_hq;
+    if (wgs < 1 || wgs > (int64_t(1) << 31) - 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_fwd, dim3((unsigned)wgs), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace tsp

@@ -90,16 +90,16 @@ SMALL = {
     "g2-T64-P2-rank1": W("a"),
     "g2-T64-P2-rank0": W("b", rank=0, seed=72),
     # G = 4 (Llama-like), several query tiles, 4 ranks, rank 2
-    "g4-T200-P4-rank2": W("c", T=200, d=512, H=16, Hkv=4, P=4, rank=2, seed=73),
-    # G = 1 (plain multi-head), 256 queries per workgroup, ragged T
-    "g1-T136-P2-rank1": W("d", T=136, H=4, Hkv=4, seed=74),
+    "g4-T224-P4-rank2": W("c", T=224, d=512, H=16, Hkv=4, P=4, rank=2, seed=73),
+    # G = 1 (plain multi-head), 256 queries per workgroup, T not a multiple of 64
+    "g1-T160-P2-rank1": W("d", T=160, H=4, Hkv=4, seed=74),
     # G = 8: two head quarters per key/value head
     "g8-T64-P2-rank1": W("e", d=512, H=16, Hkv=2, seed=75),
     # non-causal: every key of every rank
     "g2-T64-P2-full": W("f", causal=False, seed=76),
     "g4-T96-P4-rank3-full": W("g", T=96, d=512, H=16, Hkv=4, P=4, rank=3, causal=False, seed=77),
     # smallest T the kernels take
-    "g2-T8-P2-rank1": W("h", T=8, seed=78),
+    "g2-T32-P2-rank1": W("h", T=32, seed=78),
 }
 
 
@@ -131,9 +131,9 @@ def test_attention_orders_reuse_and_smaller_T():
         check(f"order {order}", got, ref)
         again, _ = run_attn(w, inp, handle=attn)
         assert np.array_equal(got, again)
-        # T = 40 (a multiple of 8): a shorter sequence of 4 x 40 tokens
-        got40, _ = run_attn(w, inp, handle=attn, T=40)
-        check(f"order {order} T=40", got40, oracle_y(w.with_(T=40), inp, T=40))
+        # T = 96: a shorter sequence of 4 x 96 tokens on the same handle
+        got96, _ = run_attn(w, inp, handle=attn, T=96)
+        check(f"order {order} T=96", got96, oracle_y(w.with_(T=96), inp, T=96))
         attn.close()
 
 
@@ -162,10 +162,10 @@ def test_attention_errors():
         attn.forward(x, 2)                                # rank out of range
     assert e.value.status == TSP_ERR_INVALID_ARG
     with pytest.raises(TspError) as e:
-        attn.forward(inp.x_all[:20].contiguous().to(dev), 0)   # T not a multiple of 8
+        attn.forward(inp.x_all[:40].contiguous().to(dev), 0)   # T not a multiple of 32
     assert e.value.status == TSP_ERR_UNSUPPORTED
     with pytest.raises(TspError) as e:
-        attn.project_kv(inp.x_all[:72].contiguous().to(dev), 0)   # T above T_max
+        attn.project_kv(inp.x_all[:96].contiguous().to(dev), 0)   # T above T_max
     assert e.value.status == TSP_ERR_INVALID_ARG
     y = attn.forward(x, 1)                                 # the handle still works
     torch.cuda.synchronize()
