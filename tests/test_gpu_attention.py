@@ -171,3 +171,20 @@ def test_attention_errors():
     torch.cuda.synchronize()
     assert torch.isfinite(y).all()
     attn.close()
+
+
+def test_attention_scores_far_above_the_reference():
+    """Keys 40..43 of rank 0 scaled by 64: their scores lie up to ~270 log2
+    units above the reference each query takes from its first 32 keys, so the
+    probabilities would overflow unless the kernel takes the true maxima and
+    starts again (the path random inputs never reach; a finite output shows
+    it was taken). Logits of ~190 nats carry the bf16 rounding of Q and K as
+    absolute errors near 1, which moves the softmax weights: the comparison
+    is with the oracle run on the same bf16 Q, K, V and O."""
+    w = W("r", T=64, d=256, H=4, Hkv=2, P=2, rank=1, seed=80)
+    inp = make_attn_inputs(w)
+    inp.x_all[40:44] *= 64                               # a power of two: exact in bf16
+    say("[gpu] attention restart path")
+    got, attn = run_attn(w, inp)
+    attn.close()
+    check("outlier keys (bf16 intermediates)", got, oracle_y(w, inp, round_bf16=True), EL2_ROUNDED, None)
