@@ -60,7 +60,14 @@ __device__ inline bf16x8 att_pack8(f32x4 lo, f32x4 hi) {
     return r;
 }
 
-__global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
+// QT query tiles of 16 per wave, 16 / QT waves per workgroup: 64 query rows
+// per four waves either way. QT = 4 (one wave per SIMD) is kept: QT = 2 (two
+// waves per SIMD, one wave's softmax beside the other's MFMAs) measured 4 %
+// slower, the VALU and matrix work of a SIMD overlapping no better across
+// waves than within one.
+constexpr int QT = 4;
+
+__global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) uint16_t k_lds[3][64 * ATT_KROW];
     __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][128 * ATT_VROW];
     poison_lds(k_lds, sizeof(k_lds));
@@ -83,13 +90,13 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     const int G = a.Hs / a.Hks;
     const int hl = jl * G + hq * a.hw + (w % a.hw);
     const int q_wg = qt * 64 * a.qs;                     // first query of the workgroup
-    const int q0 = q_wg + (w / a.hw) * 64;               // first query of the wave
+    const int q0 = q_wg + (w / a.hw) * (16 * QT);        // first query of the wave
     const int64_t qo_col = ((int64_t)k * a.Hs + hl) * 128;
 
     // Q^T fragments (B operand): query t*16 + n16, head dims ks*32 + 8g .. + 7
-    bf16x8 qf[4][4];
+    bf16x8 qf[QT][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < QT; ++t) {
         const int row = min(q0 + t * 16 + n16, a.T - 1);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
@@ -104,10 +111,10 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     // DMA of one context block into buffer `buf`: 4 K and 4 V^T instructions
     // per wave, each 1 KiB of LDS (4 K rows or 8 V^T rows). Buffer loads: the
     // block's base is scalar, a lane's offset (fixed for the whole loop) 32-bit.
-    int k_off[4], v_off[4];
+    int k_off[QT], v_off[QT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int j = w * 4 + i;
+    for (int i = 0; i < QT; ++i) {
+        const int j = w * QT + i;
         const int kr = j * 4 + (lane >> 4), kc = (lane & 15) ^ (kr & 15);
         k_off[i] = (int)((kr * a.ldk + kc * 8) * 2);
         const int vr = j * 8 + (lane >> 3), vc = (lane & 7) ^ ((vr >> 1) & 7);
@@ -117,24 +124,24 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
         const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(a.kc + (int64_t)kb * 64 * a.ldk + kv_col), (short)0, 0x7fffffff, kRawBufferWord3);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (TSP_LDS void*)&k_lds[buf][(w * 4 + i) * 512], 16, k_off[i],
+        for (int i = 0; i < QT; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (TSP_LDS void*)&k_lds[buf][(w * QT + i) * 512], 16, k_off[i],
                                                      0, 0, 0);
     };
     auto load_v = [&](int kb, int buf) {
         const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(a.vt + kv_col * a.ldv + kb * 64), (short)0, 0x7fffffff, kRawBufferWord3);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (TSP_LDS void*)&v_lds[buf][(w * 4 + i) * 512], 16, v_off[i],
+        for (int i = 0; i < QT; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (TSP_LDS void*)&v_lds[buf][(w * QT + i) * 512], 16, v_off[i],
                                                      0, 0, 0);
     };
 
     __shared__ int restart_flag;
-    f32x4 o[8][4];
-    float m[4], l[4];
+    f32x4 o[8][QT];
+    float m[QT], l[QT];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) m[t] = -INFINITY;
+    for (int t = 0; t < QT; ++t) m[t] = -INFINITY;
 
     // The key stream runs in 32-key halves of the 64-key tiles: half h of a
     // tile is its key tiles 2h, 2h+1 (16 keys each) and the P.V step ks2 = h.
@@ -147,16 +154,16 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
             kf[u] = *reinterpret_cast<const bf16x8*>(
                 &k_lds[buf][((2 * h + u) * 16 + n16) * ATT_KROW + ((4 * ks + g) ^ n16) * 8]);
     };
-    auto s_mfma = [&](int ks, const bf16x8 (&kf)[2], f32x4 (&sc)[2][4]) {
+    auto s_mfma = [&](int ks, const bf16x8 (&kf)[2], f32x4 (&sc)[2][QT]) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < QT; ++t)
                 sc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     kf[u], qf[t][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sc[u][t], 0, 0, 0);
     };
     // all four steps, each step's K fragments read one step ahead
-    auto s_half = [&](int buf, int h, f32x4 (&sc)[2][4]) {
+    auto s_half = [&](int buf, int h, f32x4 (&sc)[2][QT]) {
         bf16x8 kf[2][2];
         read_k(0, buf, h, kf[0]);
 #pragma unroll
@@ -166,11 +173,11 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
         }
     };
     // keys past the query (causal) or past the context end get -inf
-    auto apply_mask = [&](int kb, int h, f32x4 (&sc)[2][4]) {
+    auto apply_mask = [&](int kb, int h, f32x4 (&sc)[2][QT]) {
         const int kbase = kb * 64 + 32 * h;
         const int lim_s = a.S - kbase - 4 * g;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < QT; ++t) {
             const int lim_q = a.causal ? qpos0 + t * 16 + n16 - kbase - 4 * g + 1 : 1 << 30;
             const int lim = min(lim_q, lim_s);
 #pragma unroll
@@ -181,7 +188,7 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     };
     // a query's maximum over the half in log2 units: the lane's 8 keys, then
     // the 4 lane groups (the scale is positive, so it commutes with the maximum)
-    auto half_max = [&](const f32x4 (&sc)[2][4], int t) {
+    auto half_max = [&](const f32x4 (&sc)[2][QT], int t) {
         float mx = sc[0][t][0];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -192,7 +199,7 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     };
     // probabilities of query tile t against the fixed reference, added into
     // the lane's partial sum and packed as the B operand of the P.V step
-    auto softmax_t = [&](f32x4 (&sc)[2][4], int t, bf16x8 (&pb)[4]) {
+    auto softmax_t = [&](f32x4 (&sc)[2][QT], int t, bf16x8 (&pb)[QT]) {
         const float ref = m[t] == -INFINITY ? 0.f : m[t];
         float ls = 0.f;
 #pragma unroll
@@ -213,19 +220,19 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
     };
     // O^T += V^T P^T over half h of the V^T tile in buffer `buf`, fragments
     // read two ahead; vf holds the first two (read early by the caller)
-    auto pv = [&](int buf, int h, const bf16x8 (&pb)[4], bf16x8 (&vf)[3]) {
+    auto pv = [&](int buf, int h, const bf16x8 (&pb)[QT], bf16x8 (&vf)[3]) {
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
             if (dt + 2 < 8) vf[(dt + 2) % 3] = read_v(buf, h, dt + 2);
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < QT; ++t)
                 o[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt % 3], pb[t], o[dt][t], 0, 0, 0);
         }
     };
     // half n+1's scores on the matrix cores while the VALU turns half n's
     // into probabilities, then half n's P.V
-    auto step = [&](int kbuf_next, int h_next, f32x4 (&cur)[2][4], f32x4 (&nxt)[2][4], int vbuf, int h) {
-        bf16x8 pb[4], kf[2][2], vf[3];
+    auto step = [&](int kbuf_next, int h_next, f32x4 (&cur)[2][QT], f32x4 (&nxt)[2][QT], int vbuf, int h) {
+        bf16x8 pb[QT], kf[2][2], vf[3];
         read_k(0, kbuf_next, h_next, kf[0]);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -235,16 +242,16 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
                 vf[1] = read_v(vbuf, h, 1);
             }
             s_mfma(ks, kf[ks & 1], nxt);
-            softmax_t(cur, ks, pb);
+            if (ks % (4 / QT) == 0) softmax_t(cur, ks / (4 / QT), pb);
         }
         pv(vbuf, h, pb, vf);
     };
-    auto last_step = [&](f32x4 (&cur)[2][4], int vbuf, int h) {
-        bf16x8 pb[4], vf[3];
+    auto last_step = [&](f32x4 (&cur)[2][QT], int vbuf, int h) {
+        bf16x8 pb[QT], vf[3];
         vf[0] = read_v(vbuf, h, 0);
         vf[1] = read_v(vbuf, h, 1);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) softmax_t(cur, t, pb);
+        for (int t = 0; t < QT; ++t) softmax_t(cur, t, pb);
         pv(vbuf, h, pb, vf);
     };
 
@@ -261,12 +268,12 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) o[dt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < QT; ++t) o[dt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < 4; ++t) l[t] = 0.f;
+        for (int t = 0; t < QT; ++t) l[t] = 0.f;
 
         if (n_full > 0) {
-            f32x4 sa[2][4], sb[2][4];
+            f32x4 sa[2][QT], sb[2][QT];
             load_k(0, 0);
             load_v(0, 0);
             load_k(min(1, nkb - 1), 1);
@@ -275,7 +282,7 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
             s_half(0, 0, sa);
             if (attempt == 0) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) m[t] = half_max(sa, t);   // the reference
+                for (int t = 0; t < QT; ++t) m[t] = half_max(sa, t);   // the reference
             }
             int kb = 0;
             for (; kb + 1 < n_full; ++kb) {
@@ -300,11 +307,11 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
             __syncthreads();
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                f32x4 sc[2][4];
+                f32x4 sc[2][QT];
                 s_half(0, h, sc);
                 apply_mask(kb, h, sc);
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
+                for (int t = 0; t < QT; ++t)
                     if (m[t] == -INFINITY) m[t] = half_max(sc, t);   // the first keys set the reference
                 last_step(sc, 0, h);
             }
@@ -315,7 +322,7 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
         // many large ones only costs time
         bool over = false;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) over |= !(l[t] <= 1.8446744e19f);
+        for (int t = 0; t < QT; ++t) over |= !(l[t] <= 1.8446744e19f);
         if (__any(over)) restart_flag = 1;
         __syncthreads();
         if (!restart_flag) break;                        // same value in every wave
@@ -326,11 +333,11 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
             __syncthreads();
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                f32x4 sc[2][4];
+                f32x4 sc[2][QT];
                 s_half(0, h, sc);
                 apply_mask(kb, h, sc);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) m[t] = fmaxf(m[t], half_max(sc, t));
+                for (int t = 0; t < QT; ++t) m[t] = fmaxf(m[t], half_max(sc, t));
             }
             __syncthreads();                             // reads done before the next tile's DMA
         }
@@ -338,7 +345,7 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
 
     // normalise and store: lane holds O[query t*16 + n16][dims dt*16 + 4g .. + 3]
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < QT; ++t) {
         float lt = l[t];
         lt += __shfl_xor(lt, 16);
         lt += __shfl_xor(lt, 32);
@@ -358,7 +365,7 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a) {
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     const int64_t wgs = (int64_t)a.n_qt * a.P * a.Hks * a.n_hq;
     if (wgs < 1 || wgs > (int64_t(1) << 31) - 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(attn_fwd, dim3((unsigned)wgs), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(attn_fwd, dim3((unsigned)wgs), dim3(64 * (16 / QT)), 0, st, a);
     return hipGetLastError();
 }
 
