@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include "tsp_mlp.h"
+#include "tsp_attn.h"
 
 static int failures = 0;
 
@@ -69,6 +70,31 @@ int main(void) {
     double r = 0.0;
     expect("probe_hbm_read: bad size", tsp_probe_hbm_read(1000, 1, NULL, &r), TSP_ERR_INVALID_ARG);
     expect("probe_mfma: bad iters", tsp_probe_mfma_bf16(0, NULL, &r), TSP_ERR_INVALID_ARG);
+
+    /* the attention block's host checks */
+    tsp_attn_t ah = (tsp_attn_t)0x1;
+    expect("attn create: out NULL", tsp_attn_create(NULL, 64, 4096, 32, 8, 128, 8, 1, NULL, fake, fake, fake, fake,
+                                                    NULL), TSP_ERR_INVALID_ARG);
+    expect("attn create: Hkv does not divide H", tsp_attn_create(&ah, 64, 4096, 32, 6, 128, 2, 1, NULL, fake, fake,
+                                                                  fake, fake, NULL), TSP_ERR_INVALID_ARG);
+    if (ah != NULL) { printf("FAIL attn create: *out not cleared\n"); ++failures; }
+    expect("attn create: P does not divide Hkv", tsp_attn_create(&ah, 64, 4096, 32, 8, 128, 3, 1, NULL, fake, fake,
+                                                                  fake, fake, NULL), TSP_ERR_INVALID_ARG);
+    expect("attn create: bad order", tsp_attn_create(&ah, 64, 4096, 32, 8, 128, 4, 1, dup_order, fake, fake, fake,
+                                                     fake, NULL), TSP_ERR_INVALID_ARG);
+    expect("attn create: NULL weight", tsp_attn_create(&ah, 64, 4096, 32, 8, 128, 8, 1, NULL, fake, NULL, fake, fake,
+                                                       NULL), TSP_ERR_INVALID_ARG);
+    expect("attn create: dh 64", tsp_attn_create(&ah, 64, 4096, 32, 8, 64, 8, 1, NULL, fake, fake, fake, fake, NULL),
+           TSP_ERR_UNSUPPORTED);
+    expect("attn create: d 4000", tsp_attn_create(&ah, 64, 4000, 32, 8, 128, 8, 1, NULL, fake, fake, fake, fake,
+                                                  NULL), TSP_ERR_UNSUPPORTED);
+    expect("attn forward: NULL handle", tsp_attn_forward(NULL, 32, 0, fake, (float*)fake, NULL), TSP_ERR_INVALID_ARG);
+    expect("attn project_kv: NULL handle", tsp_attn_project_kv(NULL, 32, 0, fake, NULL), TSP_ERR_INVALID_ARG);
+    expect("attn destroy: NULL handle", tsp_attn_destroy(NULL), TSP_OK);
+    expect("attn set_timing: NULL handle", tsp_attn_set_timing(NULL, 1), TSP_ERR_INVALID_ARG);
+    int64_t c = 0;
+    expect("attn sizes: NULL handle", tsp_attn_sizes(NULL, &a, &b, &c), TSP_ERR_INVALID_ARG);
+    expect("attn read_timing: NULL handle", tsp_attn_read_timing(NULL, 0, NULL, NULL, NULL, &n), TSP_ERR_INVALID_ARG);
 
     /* long messages stay bounded and NUL-terminated */
     for (int i = 0; i < 1000; ++i) tsp_mlp_validate(-i, -i, -i, -i, -i, -i, NULL, i & 1);
