@@ -28,7 +28,7 @@ group s (the sequence-wise exchange: rank rho supplies X_rho Wk_s, X_rho Wv_s);
 attend with its queries over that full context; multiply by the head group s
 rows of Wo and add the product into its output Y_r.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 
 * scaled dot-product softmax attention with scale 1/sqrt(dh); no bias terms,
   no rotary or other position encoding, no dropout;

@@ -23,7 +23,7 @@ What it computes, and where that is stated:
   by columns of the first matrix because the nonlinearity is elementwise and
   does not distribute over a sum.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 
 * gated activation = SwiGLU, h = SiLU(x.Wg) * (x.Wu) with SiLU(g) = g/(1+e^-g);
 * the non-gated block uses the tanh form of GeLU,
@@ -189,7 +189,7 @@ def tsp_simulate(X_full, w_gate, w_up, w_down, P: int, act: str = "swiglu",
 # ("Tensor Parallelism: Splitting the Math", the paragraph after the
 # walk-through: the split synchronises in the forward and in the backward
 # pass; "Folding Tensor and Sequence Parallelism ...", Abstract: the method is
-# for training). Reading taken (listed in the design doc): the backward of one
+# for training). Reading taken: the backward of one
 # rank's block is the exact gradient of the forward above for a loss whose
 # gradient with respect to Y is dY. The rank visits the shards in the same ring
 # order; for shard s it forms that shard's part of dX (added into a local
