@@ -337,7 +337,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(multi-GPU ring transfer is not part of this build)", file=sys.stderr)
+              "(the multi-GPU ring transfer is not implemented)", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
