@@ -111,3 +111,37 @@ def test_backward_with_poisoned_lds(name, w):
         assert np.isfinite(got).all(), f"{name} {k}: NaN (a read ran ahead of its data)"
         assert np.linalg.norm(got - r) / np.linalg.norm(r) <= 3e-3, (name, k)
         assert np.max(np.abs(got - r)) <= 2e-2 * np.max(np.abs(r)), (name, k)
+
+
+ATTN_CASES = [
+    ("attention causal g4", dict(T=96, d=512, H=16, Hkv=4, P=4, rank=2, seed=17, causal=True)),
+    ("attention full g1", dict(T=64, d=256, H=4, Hkv=4, P=2, rank=1, seed=18, causal=False)),
+]
+
+
+@pytest.mark.parametrize("name,kw", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+def test_attention_with_poisoned_lds(name, kw):
+    """The attention kernels stage the projection tile and the K / V^T tiles
+    in LDS: NaN in Y means a read ran ahead of its data."""
+    import oracle.attn_oracle as ao
+    from sharded_transformer_mlp_amd.inputs import AttnWorkload, make_attn_inputs
+    assert binding.LIB_PATH == DEBUG_LIB
+    say(f"[gpu] LDS poison: {name}")
+    w = AttnWorkload("p", dh=128, **kw)
+    inp = make_attn_inputs(w)
+    dev = torch.device("cuda:0")
+    attn = binding.TspAttn(inp.w_q.to(dev), inp.w_k.to(dev), inp.w_v.to(dev), inp.w_o.to(dev), w.H, w.Hkv, w.P,
+                           order=w.order(), causal=w.causal, T_max=w.T)
+    x_all = inp.x_all.to(dev)
+    for rho in range(w.P):
+        if rho != w.rank:
+            attn.project_kv(x_all[rho * w.T:(rho + 1) * w.T].contiguous(), rho)
+    y = attn.forward(x_all[w.rank * w.T:(w.rank + 1) * w.T].contiguous(), w.rank)
+    torch.cuda.synchronize()
+    attn.close()
+    y = y.cpu().double().numpy()
+    assert np.isfinite(y).all(), f"{name}: NaN in Y (a read ran ahead of its data)"
+    f = lambda t: t.float().numpy()
+    ref = ao.tsp_attention(f(inp.x_all), f(inp.w_q), f(inp.w_k), f(inp.w_v), f(inp.w_o), w.H, w.Hkv, w.P, w.rank,
+                           order=w.order(), causal=w.causal)
+    assert np.linalg.norm(y - ref) / np.linalg.norm(ref) <= 8e-3, name
