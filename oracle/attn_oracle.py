@@ -113,7 +113,8 @@ def attention_unsharded(X, Wq, Wk, Wv, Wo, H: int, Hkv: int, causal: bool = True
 
 def tsp_attention(X_all, Wq, Wk, Wv, Wo, H: int, Hkv: int, P: int, rank: int,
                   order: Optional[Sequence[int]] = None, causal: bool = True,
-                  round_bf16: bool = False, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+                  round_bf16: bool = False, rows: Optional[Sequence[int]] = None,
+                  q_store_scale: float = 1.0) -> np.ndarray:
     """Rank ``rank``'s output rows of the attention block under TSP.
 
     X_all: the whole S x d sequence (rank rho's tokens are rows
@@ -121,7 +122,9 @@ def tsp_attention(X_all, Wq, Wk, Wv, Wo, H: int, Hkv: int, P: int, rank: int,
     key/value exchange delivers. order: the head groups in the order the
     rank visits them (default: rank, rank+1, ... mod P). round_bf16 rounds Q,
     K, V and the attention output to bfloat16 before they are used (a
-    diagnostic of the kernels' stored intermediates, not the bar). rows: only
+    diagnostic of the kernels' stored intermediates, not the bar); with
+    q_store_scale the queries are rounded as stored times that factor (a
+    store that folds the softmax scale into them) and divided back. rows: only
     these of the rank's token rows (queries are independent of each other).
     """
     X_all = _f64(X_all)
@@ -145,7 +148,7 @@ def tsp_attention(X_all, Wq, Wk, Wv, Wo, H: int, Hkv: int, P: int, rank: int,
     Y = np.zeros((Tq, d))
     for s in order:
         cq, ckv = head_columns(s, Hs, dh), head_columns(s, Hks, dh)
-        Q = rnd(X_r @ _f64(Wq)[:, cq]).reshape(Tq, Hs, dh)
+        Q = (rnd(q_store_scale * (X_r @ _f64(Wq)[:, cq])) / q_store_scale).reshape(Tq, Hs, dh)
         # sequence-wise exchange: every rank's keys and values of head group s
         K = rnd(np.concatenate([X_all[rho * T:(rho + 1) * T] @ _f64(Wk)[:, ckv] for rho in range(P)]))
         V = rnd(np.concatenate([X_all[rho * T:(rho + 1) * T] @ _f64(Wv)[:, ckv] for rho in range(P)]))

@@ -640,6 +640,7 @@ tsp_status_t attn_project(tsp_attn* h, int64_t T, int32_t rank, const void* X, h
     p.ldv = h->S_pad;
     p.row0 = (int64_t)rank * T;
     p.T = (int)T; p.d = (int)h->d; p.P = h->P; p.Hs = (int)h->Hs; p.Hks = (int)h->Hks;
+    p.q_scale = (float)(1.4426950408889634 / sqrt((double)tsp::ATT_DH));
     return timed_launch(h, "attn_qkv", st, [&] { return tsp::launch_qkv(p, st); });
 }
 

@@ -91,17 +91,22 @@ __global__ __launch_bounds__(256) void qkv_w16(ProjArgs a, int n_ft_shard, int n
     w16::mainloop(lds, acc, a.d >> 5, src);
 
     // the tile (256 tokens x 256 features) through the LDS ring, then each
-    // 128-feature half, one head, to its destination
+    // 128-feature half, one head, to its destination. Query heads are scaled
+    // by q_scale (the softmax's log2(e)/sqrt(dh)) before their one rounding,
+    // so that the attention's scores come out in log2 units.
     StagedRows16<BM> stg{lds};
     stage_barrier();
     const int fsub = 4 * (lane >> 4);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i) {
+        const int c = (wm * TM + i) * 16 + fsub;
+        const float sc = ftile * 2 + (c >> 7) < a.Hs ? a.q_scale : 1.0f;   // head slot of column c
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const f32x4 u = acc[i][j];
-            stg.put4((wn * TN + j) * 16 + (lane & 15), (wm * TM + i) * 16 + fsub, pack4_bf16(u[0], u[1], u[2], u[3]));
+            const f32x4 u = acc[i][j] * sc;
+            stg.put4((wn * TN + j) * 16 + (lane & 15), c, pack4_bf16(u[0], u[1], u[2], u[3]));
         }
+    }
     lgkm_zero();
     stage_barrier();
     const int s = a.order[k];

@@ -102,6 +102,8 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
         for (int ks = 0; ks < 4; ++ks)
             qf[t][ks] = *reinterpret_cast<const bf16x8*>(a.q + (int64_t)row * a.ldq + qo_col + ks * 32 + 8 * g);
     }
+    // (the projection stored the queries scaled by log2(e)/sqrt(dh): the
+    // scores come out in log2 units)
 
     const int q_hi = min(a.T, q_wg + 64 * a.qs);         // queries of the workgroup end here
     const int kend = a.causal ? min(a.S, a.row0 + q_hi) : a.S;
@@ -154,14 +156,17 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
             kf[u] = *reinterpret_cast<const bf16x8*>(
                 &k_lds[buf][((2 * h + u) * 16 + n16) * ATT_KROW + ((4 * ks + g) ^ n16) * 8]);
     };
-    auto s_mfma = [&](int ks, const bf16x8 (&kf)[2], f32x4 (&sc)[2][QT]) {
+    // init[t]: the accumulators' start for ks == 0 (zero, or minus the
+    // query's reference so that the scores come out already shifted)
+    auto s_mfma = [&](int ks, const bf16x8 (&kf)[2], f32x4 (&sc)[2][QT], const float (&init)[QT]) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int t = 0; t < QT; ++t)
                 sc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    kf[u], qf[t][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sc[u][t], 0, 0, 0);
+                    kf[u], qf[t][ks], ks == 0 ? f32x4{init[t], init[t], init[t], init[t]} : sc[u][t], 0, 0, 0);
     };
+    const float zero_init[QT] = {};
     // all four steps, each step's K fragments read one step ahead
     auto s_half = [&](int buf, int h, f32x4 (&sc)[2][QT]) {
         bf16x8 kf[2][2];
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             if (ks + 1 < 4) read_k(ks + 1, buf, h, kf[(ks + 1) & 1]);
-            s_mfma(ks, kf[ks & 1], sc);
+            s_mfma(ks, kf[ks & 1], sc, zero_init);
         }
     };
     // keys past the query (causal) or past the context end get -inf
@@ -195,18 +200,18 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[u][t][i]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
-        return fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+        return fmaxf(mx, __shfl_xor(mx, 32));
     };
     // probabilities of query tile t against the fixed reference, added into
     // the lane's partial sum and packed as the B operand of the P.V step
-    auto softmax_t = [&](f32x4 (&sc)[2][QT], int t, bf16x8 (&pb)[QT]) {
+    auto softmax_t = [&](f32x4 (&sc)[2][QT], int t, bf16x8 (&pb)[QT], bool shifted) {
         const float ref = m[t] == -INFINITY ? 0.f : m[t];
         float ls = 0.f;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][t][i], a.scale_log2, -ref));
+                const float pr = __builtin_amdgcn_exp2f(shifted ? sc[u][t][i] : sc[u][t][i] - ref);
                 sc[u][t][i] = pr;
                 ls += pr;
             }
@@ -231,7 +236,10 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
     };
     // half n+1's scores on the matrix cores while the VALU turns half n's
     // into probabilities, then half n's P.V
-    auto step = [&](int kbuf_next, int h_next, f32x4 (&cur)[2][QT], f32x4 (&nxt)[2][QT], int vbuf, int h) {
+    // cur_shifted: cur's scores already have the reference subtracted; the
+    // next half's always do (init = minus the reference)
+    auto step = [&](int kbuf_next, int h_next, f32x4 (&cur)[2][QT], f32x4 (&nxt)[2][QT], int vbuf, int h,
+                    bool cur_shifted, const float (&negref)[QT]) {
         bf16x8 pb[QT], kf[2][2], vf[3];
         read_k(0, kbuf_next, h_next, kf[0]);
 #pragma unroll
@@ -241,17 +249,17 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
                 vf[0] = read_v(vbuf, h, 0);
                 vf[1] = read_v(vbuf, h, 1);
             }
-            s_mfma(ks, kf[ks & 1], nxt);
-            if (ks % (4 / QT) == 0) softmax_t(cur, ks / (4 / QT), pb);
+            s_mfma(ks, kf[ks & 1], nxt, negref);
+            if (ks % (4 / QT) == 0) softmax_t(cur, ks / (4 / QT), pb, cur_shifted);
         }
         pv(vbuf, h, pb, vf);
     };
-    auto last_step = [&](f32x4 (&cur)[2][QT], int vbuf, int h) {
+    auto last_step = [&](f32x4 (&cur)[2][QT], int vbuf, int h, bool shifted) {
         bf16x8 pb[QT], vf[3];
         vf[0] = read_v(vbuf, h, 0);
         vf[1] = read_v(vbuf, h, 1);
 #pragma unroll
-        for (int t = 0; t < QT; ++t) softmax_t(cur, t, pb);
+        for (int t = 0; t < QT; ++t) softmax_t(cur, t, pb, shifted);
         pv(vbuf, h, pb, vf);
     };
 
@@ -284,19 +292,32 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
 #pragma unroll
                 for (int t = 0; t < QT; ++t) m[t] = half_max(sa, t);   // the reference
             }
+            // every later half's scores start from minus the reference
+            float negref[QT];
+#pragma unroll
+            for (int t = 0; t < QT; ++t) negref[t] = -m[t];
             int kb = 0;
+            if (n_full > 1) {                            // tile 0: its first half's scores are not shifted
+                load_k(min(2, nkb - 1), 2);
+                load_v(1, 1);
+                step(0, 1, sa, sb, 0, 0, false, negref);
+                step(1, 0, sb, sa, 0, 1, true, negref);
+                att_vm_zero();
+                __syncthreads();
+                kb = 1;
+            }
             for (; kb + 1 < n_full; ++kb) {
                 // buffer (kb+2)%3 held tile kb-1's K, (kb+1)&1 tile kb-1's V^T:
                 // both last read before the previous barrier
                 load_k(min(kb + 2, nkb - 1), (kb + 2) % 3);
                 load_v(kb + 1, (kb + 1) & 1);
-                step(kb % 3, 1, sa, sb, kb & 1, 0);             // scores of this tile's second half
-                step((kb + 1) % 3, 0, sb, sa, kb & 1, 1);       // scores of the next tile's first half
+                step(kb % 3, 1, sa, sb, kb & 1, 0, true, negref);        // scores of this tile's second half
+                step((kb + 1) % 3, 0, sb, sa, kb & 1, 1, true, negref);  // scores of the next tile's first half
                 att_vm_zero();
                 __syncthreads();
             }
-            step(kb % 3, 1, sa, sb, kb & 1, 0);
-            last_step(sb, kb & 1, 1);
+            step(kb % 3, 1, sa, sb, kb & 1, 0, kb > 0, negref);
+            last_step(sb, kb & 1, 1, true);
             __syncthreads();                             // every read of the buffers is done
         }
         // masked tiles, one at a time
@@ -313,7 +334,7 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
 #pragma unroll
                 for (int t = 0; t < QT; ++t)
                     if (m[t] == -INFINITY) m[t] = half_max(sc, t);   // the first keys set the reference
-                last_step(sc, 0, h);
+                last_step(sc, 0, h, false);
             }
             __syncthreads();
         }

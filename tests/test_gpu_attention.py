@@ -9,8 +9,9 @@ the output projection), each a relative error of up to 2^-9 (RMS ~1.7e-3 on
 Gaussian-like values); Q and K enter the logits, whose error moves the
 softmax weights, so the expected total is ~3-4e-3, not the MLP's ~1.7e-3.
 A diagnostic against the oracle run with Q, K, V and O rounded the same way
-(round_bf16=True) leaves the probabilities' rounding and summation order:
-its bar is 3e-3.
+(round_bf16=True; the queries as the projection stores them, times the
+softmax scale) leaves the probabilities' rounding and summation order: its
+bar is 3e-3.
 
 Every rank's context rows come from tsp_attn_project_kv (the exchange
 stand-in) before the forward of the rank under test.
@@ -62,10 +63,16 @@ def run_attn(w: AttnWorkload, inp, ranks_kv=None, T_max=None, handle=None, T=Non
     return y.cpu().double().numpy(), attn
 
 
+# the projection stores the queries times log2(e)/sqrt(dh) (the softmax scale,
+# so that scores come out in log2 units): the diagnostic rounds them likewise
+Q_STORE_SCALE = float(np.log2(np.e) / np.sqrt(128))
+
+
 def oracle_y(w, inp, round_bf16=False, rows=None, T=None):
     x = _np(inp.x_all) if T is None else _np(inp.x_all[:w.P * T])
     return ao.tsp_attention(x, _np(inp.w_q), _np(inp.w_k), _np(inp.w_v), _np(inp.w_o), w.H, w.Hkv, w.P, w.rank,
-                            order=w.order(), causal=w.causal, round_bf16=round_bf16, rows=rows)
+                            order=w.order(), causal=w.causal, round_bf16=round_bf16, rows=rows,
+                            q_store_scale=Q_STORE_SCALE if round_bf16 else 1.0)
 
 
 def check(name, got, ref, el2=EL2, emax=EMAX):

@@ -201,3 +201,15 @@ def test_row_subset_equals_full_rows():
     full = ao.tsp_attention(X, Wq, Wk, Wv, Wo, H, Hkv, P, 1)
     rows = [0, 5, 15]
     np.testing.assert_array_equal(ao.tsp_attention(X, Wq, Wk, Wv, Wo, H, Hkv, P, 1, rows=rows), full[rows])
+
+
+def test_query_store_scale_only_changes_the_rounding():
+    S, d, H, Hkv, dh, P = 32, 16, 4, 2, 4, 2
+    X, Wq, Wk, Wv, Wo = rand_block(9, S, d, H, Hkv, dh)
+    exact = ao.tsp_attention(X, Wq, Wk, Wv, Wo, H, Hkv, P, 1)
+    # without rounding the factor cancels exactly up to fp64 rounding
+    np.testing.assert_allclose(ao.tsp_attention(X, Wq, Wk, Wv, Wo, H, Hkv, P, 1, q_store_scale=0.3), exact,
+                               rtol=0, atol=1e-12 * np.max(np.abs(exact)))
+    # a power of two commutes with the bf16 rounding
+    np.testing.assert_array_equal(ao.tsp_attention(X, Wq, Wk, Wv, Wo, H, Hkv, P, 1, round_bf16=True, q_store_scale=4.0),
+                                  ao.tsp_attention(X, Wq, Wk, Wv, Wo, H, Hkv, P, 1, round_bf16=True))
