@@ -195,3 +195,16 @@ def test_attention_scores_far_above_the_reference():
     got, attn = run_attn(w, inp)
     attn.close()
     check("outlier keys (bf16 intermediates)", got, oracle_y(w, inp, round_bf16=True), EL2_ROUNDED, None)
+
+
+def test_attention_70b_shape_sampled_rows():
+    """70B-style attention (d 8192, 64 query and 8 key/value heads: 8 query
+    heads per key/value head, two head quarters per workgroup), P 8, T 2048
+    of a 16384-token sequence, rank 5, at full size on sampled query rows."""
+    w = AttnWorkload("70b-attn", T=2048, d=8192, H=64, Hkv=8, dh=128, P=8, rank=5, seed=81)
+    say("[gpu] attention 70B shape full size")
+    inp = make_attn_inputs(w)
+    got, attn = run_attn(w, inp)
+    attn.close()
+    rows = np.sort(np.concatenate([[0, w.T - 1], np.random.default_rng(94).choice(w.T, 6, replace=False)]))
+    check("70B shape sampled rows", got[rows], oracle_y(w, inp, rows=rows))
