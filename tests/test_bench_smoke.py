@@ -73,3 +73,16 @@ def test_bench_attention_line():
     d = json.loads(lines[0])
     assert d["pass"] == "attention" and d["unit"] == "TFLOP/s" and d["value"] > 0
     assert d["roofline"]["kernel"].startswith("attn_") and 0 < d["roofline"]["frac"] < 1
+
+
+def test_attention_kernel_work_adds_up_to_the_block():
+    """The per-kernel algorithmic flops the attention bench prices each kernel
+    with add up to the oracle's flop count of the whole block."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import oracle.attn_oracle as ao
+    from sharded_transformer_mlp_amd.inputs import AttnWorkload, attn_workload
+    for w in (attn_workload("attn_llama8b"),
+              AttnWorkload("x", T=96, d=512, H=16, Hkv=4, dh=128, P=4, rank=3, seed=0, causal=False)):
+        total = sum(bench.attn_kernel_work(w, k)[0] for k in ("attn_qkv", "attn_core", "attn_out"))
+        assert total == ao.attention_flops(w.T, w.d, w.H, w.Hkv, w.dh, w.P, w.rank, w.causal)
