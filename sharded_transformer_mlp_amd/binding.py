@@ -100,6 +100,12 @@ def _stream_ptr(stream) -> Optional[int]:
     return s.cuda_stream
 
 
+def _check_shape(name, t, shape) -> None:
+    if t is None or tuple(int(n) for n in t.shape) != tuple(shape):
+        got = None if t is None else tuple(t.shape)
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {got}")
+
+
 def probe_hbm_read(nbytes: int = 4 << 30, reps: int = 10, stream=None) -> float:
     """Sustained HBM read rate in GB/s (nontemporal 16-byte loads)."""
     out = ctypes.c_double()
@@ -125,9 +131,23 @@ class TspMLP:
     def __init__(self, w_gate, w_up, w_down, P: int, order=None, act: str = "swiglu",
                  T_max: int = 1, stream=None):
         import torch
+        # The C ABI cannot see buffer sizes: a weight of the wrong shape would
+        # make the packing kernels read past its end, so shapes are checked here.
+        if w_up.dim() != 2:
+            raise ValueError("w_up must be a d x f matrix")
+        self.d, self.f = (int(n) for n in w_up.shape)
+        _check_shape("w_up", w_up, (self.d, self.f))
+        if act == "swiglu":
+            if w_gate is None:
+                raise ValueError("the SwiGLU block needs w_gate")
+            _check_shape("w_gate", w_gate, (self.d, self.f))
+        elif w_gate is not None:
+            raise ValueError("the GeLU block takes no w_gate")
+        _check_shape("w_down", w_down, (self.f, self.d))
+        if w_up.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("weights must be float32 or bfloat16")
         self.dtype = {torch.float32: "f32", torch.bfloat16: "bf16"}[w_up.dtype]
         self.tdtype = w_up.dtype
-        self.d, self.f = w_up.shape
         self.P, self.act = P, act
         self.order = list(range(P)) if order is None else [int(s) for s in order]
         for w in (w_gate, w_up, w_down):
@@ -236,12 +256,18 @@ class TspAttn:
     def __init__(self, w_q, w_k, w_v, w_o, H: int, Hkv: int, P: int, order=None, causal: bool = True,
                  T_max: int = 8, stream=None):
         import torch
+        # shapes first: the C ABI cannot see buffer sizes (see TspMLP)
+        if w_q.dim() != 2 or H < 1 or Hkv < 1 or w_q.shape[1] % H:
+            raise ValueError("w_q must be a d x (H dh) matrix")
+        self.d = int(w_q.shape[0])
+        self.H, self.Hkv, self.P = H, Hkv, P
+        self.dh = int(w_q.shape[1]) // H
+        _check_shape("w_k", w_k, (self.d, Hkv * self.dh))
+        _check_shape("w_v", w_v, (self.d, Hkv * self.dh))
+        _check_shape("w_o", w_o, (H * self.dh, self.d))
         for w in (w_q, w_k, w_v, w_o):
             if not (w.is_cuda and w.is_contiguous() and w.dtype == torch.bfloat16):
                 raise ValueError("weights must be contiguous bf16 CUDA tensors")
-        self.d = w_q.shape[0]
-        self.H, self.Hkv, self.P = H, Hkv, P
-        self.dh = w_q.shape[1] // H
         self.order = list(range(P)) if order is None else [int(s) for s in order]
         o = _order_array(self.order)
         h = _vp()

@@ -141,3 +141,46 @@ def test_attn_calls_reject_null_handle():
     assert lib.tsp_attn_forward(None, 16, 0, ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), None) == INV
     assert lib.tsp_attn_project_kv(None, 16, 0, ctypes.c_void_p(0x1000), None) == INV
     assert lib.tsp_attn_destroy(None) == OK
+
+
+@pytest.mark.parametrize("case", ["up_cols", "gate_shape", "down_transposed", "gate_missing", "gate_on_gelu", "up_1d"])
+def test_binding_rejects_mismatched_weight_shapes(case):
+    """The C ABI takes bare pointers, so the binding checks every weight's
+    shape against (d, f) before create: a wrong one would be read past its
+    end by the packing kernels. CPU tensors suffice, the check comes first."""
+    import torch
+    d, f = 64, 256
+    wg, wu, wd = torch.zeros(d, f), torch.zeros(d, f), torch.zeros(f, d)
+    act = "swiglu"
+    if case == "up_cols":
+        wu = torch.zeros(d, f + 64)
+    elif case == "gate_shape":
+        wg = torch.zeros(d + 64, f)
+    elif case == "down_transposed":
+        wd = torch.zeros(d, f)
+    elif case == "gate_missing":
+        wg = None
+    elif case == "gate_on_gelu":
+        act = "gelu_tanh"
+    elif case == "up_1d":
+        wu = torch.zeros(d * f)
+    with pytest.raises(ValueError):
+        B.TspMLP(wg, wu, wd, 2, act=act, T_max=8)
+
+
+@pytest.mark.parametrize("case", ["k_heads", "v_width", "o_transposed", "q_not_heads"])
+def test_binding_rejects_mismatched_attention_shapes(case):
+    import torch
+    d, H, Hkv, dh = 256, 4, 2, 128
+    wq, wk, wv, wo = (torch.zeros(d, H * dh), torch.zeros(d, Hkv * dh), torch.zeros(d, Hkv * dh),
+                      torch.zeros(H * dh, d))
+    if case == "k_heads":
+        wk = torch.zeros(d, H * dh)
+    elif case == "v_width":
+        wv = torch.zeros(d, Hkv * dh - 8)
+    elif case == "o_transposed":
+        wo = torch.zeros(d, H * dh)
+    elif case == "q_not_heads":
+        wq = torch.zeros(d, H * dh + 8)
+    with pytest.raises(ValueError):
+        B.TspAttn(wq, wk, wv, wo, H, Hkv, 2, T_max=32)
