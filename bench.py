@@ -39,7 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "sharded gated-MLP TFLOP/s + % bf16 MFMA peak (large T); HBM GB/s % peak (T=16)"
-PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector / MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 KERNEL_SOURCES = {
@@ -62,6 +62,12 @@ KERNEL_SOURCES = {
 }
 METRIC_BWD = "sharded gated-MLP backward TFLOP/s (dX and weight gradients; recomputation not counted)"
 METRIC_ATTN = "TSP attention block TFLOP/s, one rank (projections + causal attention over the exchanged context)"
+
+
+def is_decode(w) -> bool:
+    """The weight-streaming (decode-like) workloads, priced in GB/s against
+    HBM: bf16 with at most 48 tokens (the skinny kernels' range)."""
+    return w.dtype == "bf16" and w.T <= 48
 
 
 def log(*a):
@@ -130,16 +136,32 @@ def read_traffic(workload_name: str, kernel: str):
         return None
 
 
+def oracle_threads(fn, *a, **kw):
+    """Run a CPU-baseline body with the BLAS pool set to every CPU of this
+    process's affinity mask; `cores` is the thread count the pool then
+    reports (the threads the oracle's matrix products actually use)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:  # pragma: no cover
+        return fn(*a, cores=n, **kw)
+    with threadpool_limits(limits=n):
+        used = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        return fn(*a, cores=max(used) if used else 1, **kw)
+
+
 def cpu_baseline(w, inp, budget_s: float, dy=None):
+    return oracle_threads(_cpu_baseline, w, inp, budget_s, dy)
+
+
+def cpu_baseline_attn(w, inp, budget_s: float):
+    return oracle_threads(_cpu_baseline_attn, w, inp, budget_s)
+
+
+def _cpu_baseline(w, inp, budget_s: float, dy=None, cores=1):
     """Time the fp64 oracle on the first n token rows, n sized to ~budget_s
     (the backward when dy is given: gradients of those rows' loss)."""
-    import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
     x = inp.x.float().numpy()
     wg = None if inp.w_gate is None else inp.w_gate.float().numpy()
     wu, wd = inp.w_up.float().numpy(), inp.w_down.float().numpy()
@@ -167,7 +189,7 @@ def cpu_baseline(w, inp, budget_s: float, dy=None):
     if g is not None:
         value = oracle.backward_flops(n, w.d, w.f, w.act) / dt / 1e12
         unit = "TFLOP/s"
-    elif w.T <= 64:                             # decode-like: report bytes streamed per second
+    elif is_decode(w):                          # decode-like: report bytes streamed per second
         value = w.bytes(n) / dt / 1e9
         unit = "GB/s"
     else:
@@ -196,16 +218,11 @@ def attn_kernel_work(w, kernel: str):
     raise KeyError(kernel)
 
 
-def cpu_baseline_attn(w, inp, budget_s: float):
+def _cpu_baseline_attn(w, inp, budget_s: float, cores=1):
     """Time the fp64 attention oracle on the rank's first n token rows (it
     also projects every rank's keys and values, the exchanged context, as the
     oracle does for any row count), n sized to ~budget_s."""
     import oracle.attn_oracle as ao
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
     X = inp.x_all.float().numpy()
     Wq, Wk, Wv, Wo = (t.float().numpy() for t in (inp.w_q, inp.w_k, inp.w_v, inp.w_o))
 
@@ -320,12 +337,154 @@ def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):
     log(f"copy calibration: {reps} copies of {nbytes} bytes")
 
 
+def time_steps(step, steps: int, warmup: int):
+    """W untimed warmup steps, then exactly `steps` steps between two device
+    synchronisations, with an event at every step boundary on the stream the
+    steps run on. Returns (ms per step over the whole region, per-step ms)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return evs[0].elapsed_time(evs[steps]) / steps, per
+
+
+def step_stats(per):
+    s = sorted(per)
+    n = len(s)
+    med = s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+    return {"median_ms": med, "min_ms": s[0], "max_ms": s[-1], "first_ms": per[0]}
+
+
+def measure_mlp(w, args, backward: bool = False, with_cpu: bool = False):
+    """One workload's timed region, kernel region and roofline (a dict in the
+    shape of the bench's JSON line)."""
+    import torch
+    from sharded_transformer_mlp_amd.binding import TspMLP
+    from sharded_transformer_mlp_amd.inputs import make_inputs, make_output_grad
+
+    dev = torch.device("cuda:0")
+    log(f"workload {w.name}: generating inputs")
+    inp = make_inputs(w)
+    x = inp.x.to(dev)
+    wg = None if inp.w_gate is None else inp.w_gate.to(dev)
+    wu, wd = inp.w_up.to(dev), inp.w_down.to(dev)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    mlp = TspMLP(wg, wu, wd, w.P, order=w.order(), act=w.act, T_max=w.T)
+    pack_ms = (time.perf_counter() - t) * 1e3
+    # the handle holds packed copies: the caller's weights are not needed again
+    del wg, wu, wd
+    dy = None
+    if backward:
+        # a step is one backward: the seeded output gradient against the
+        # resident inputs and the handle's weights, gradients written into
+        # preallocated fp32 tensors (the first call also allocates the
+        # backward workspace, so the warmup does that)
+        dy = make_output_grad(w)
+        dy_dev = dy.to(dev)
+        grads = {"dX": torch.empty(w.T, w.d, dtype=torch.float32, device=dev),
+                 "dW_gate": None if w.act != "swiglu" else torch.empty(w.d, w.f, dtype=torch.float32, device=dev),
+                 "dW_up": torch.empty(w.d, w.f, dtype=torch.float32, device=dev),
+                 "dW_down": torch.empty(w.f, w.d, dtype=torch.float32, device=dev)}
+
+        def step():
+            mlp.backward(x, dy_dev, out=grads)
+    else:
+        y = torch.empty(w.T, w.d, dtype=torch.float32, device=dev)
+
+        def step():
+            mlp.forward(x, y)
+
+    log(f"warmup {args.warmup}, timing {args.steps} steps")
+    ms, per = time_steps(step, args.steps, args.warmup)
+    # Kernel region: the same number of passes again, with the library
+    # recording HIP events around every kernel on the stream it runs on. The
+    # events cost ~15 us per step, so they stay out of the timed region above.
+    mlp.read_timing()
+    mlp.set_timing(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    mlp.set_timing(False)
+    kt = mlp.read_timing()
+    kernels = {k: v[0] / max(v[1], 1) for k, v in kt.items()}
+    log(f"ms/step {ms:.4f}; kernels {kernels}")
+
+    decode = is_decode(w) and not backward
+    if backward:
+        import oracle
+        flops_step = oracle.backward_flops(w.T, w.d, w.f, w.act)
+        value, unit = flops_step / (ms * 1e-3) / 1e12, "TFLOP/s"
+    elif decode:
+        value, unit = w.bytes() / (ms * 1e-3) / 1e9, "GB/s"
+    else:
+        value, unit = w.flops() / (ms * 1e-3) / 1e12, "TFLOP/s"
+    peak = PEAK_HBM_GBS if decode else (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS)
+
+    dom = max(kernels, key=lambda k: kernels[k])
+    flops, byts = kernel_work(w, dom, w.T)
+    dom_s = kernels[dom] * 1e-3
+    if decode:
+        roof = {"bound": "hbm", "achieved": byts / dom_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / dom_s / 1e12, "peak": peak, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = read_traffic(w.name, dom)
+    roof["kernel"] = dom
+    roof["kernel_ms"] = kernels[dom]
+    roof["algorithmic_bytes"] = byts
+    roof["algorithmic_flops"] = flops
+
+    st = step_stats(per)
+    scale = (w.bytes() / 1e9 if decode else (flops_step if backward else w.flops()) / 1e12) * 1e3
+    out = {
+        "value": value,
+        "unit": unit,
+        "ms_per_step": ms,
+        **st,
+        "value_at_median": scale / st["median_ms"],
+        "value_at_min": scale / st["min_ms"],
+        "pct_of_peak": value / peak * 100.0,
+        "dtype": w.dtype,
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "P": w.P, "act": w.act,
+                   "ring_order": w.order(), "parallelism": "one TSP rank (shard loop on one GPU)"},
+        "kernels_ms": kernels,
+        "kernel_sum_ms": sum(kernels.values()),
+        "pack_ms": pack_ms,
+        "roofline": roof,
+    }
+    if backward:
+        out["config"]["parallelism"] = "one TSP rank's backward (shard loop on one GPU)"
+        del grads, dy_dev
+    else:
+        del y
+    mlp.close()
+    del x
+    torch.cuda.empty_cache()
+    if with_cpu:
+        log("cpu baseline (fp64 oracle)")
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, dy)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--also", default="long70b,decode70b",
+                    help="comma-separated workloads timed after the headline one, in the same process and with "
+                         "the same --steps/--warmup, reported under 'also' (empty: none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the HBM-read and MFMA ceiling probes")
@@ -342,139 +501,53 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
-    if args.which == "attention":
-        import torch
-        if not torch.cuda.is_available():
-            print("bench.py needs a GPU", file=sys.stderr)
-            sys.exit(1)
-        bench_attention(args)
-        return
-
     import torch
-    from sharded_transformer_mlp_amd.binding import TspMLP
-    from sharded_transformer_mlp_amd.inputs import make_inputs, make_output_grad, workload
-
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.which == "attention":
+        bench_attention(args)
+        return
+
+    from sharded_transformer_mlp_amd.inputs import workload
+
     w = workload(args.workload)
-    dev = torch.device("cuda:0")
-    log(f"workload {w.name}: generating inputs")
-    inp = make_inputs(w)
-    x = inp.x.to(dev)
-    wg = None if inp.w_gate is None else inp.w_gate.to(dev)
-    wu, wd = inp.w_up.to(dev), inp.w_down.to(dev)
-    torch.cuda.synchronize()
-    t = time.perf_counter()
-    mlp = TspMLP(wg, wu, wd, w.P, order=w.order(), act=w.act, T_max=w.T)
-    pack_ms = (time.perf_counter() - t) * 1e3
     backward = args.which == "backward"
-    if backward:
-        # a step is one backward: the seeded output gradient against the
-        # resident inputs and weights, gradients written into preallocated
-        # fp32 tensors (the first call also allocates the backward workspace,
-        # so the warmup does that)
-        dy = make_output_grad(w)
-        dy_dev = dy.to(dev)
-        grads = {"dX": torch.empty(w.T, w.d, dtype=torch.float32, device=dev),
-                 "dW_gate": None if wg is None else torch.empty(w.d, w.f, dtype=torch.float32, device=dev),
-                 "dW_up": torch.empty(w.d, w.f, dtype=torch.float32, device=dev),
-                 "dW_down": torch.empty(w.f, w.d, dtype=torch.float32, device=dev)}
-
-        def step():
-            mlp.backward(x, dy_dev, wg, wu, wd, out=grads)
-    else:
-        del wg, wu, wd
-        y = torch.empty(w.T, w.d, dtype=torch.float32, device=dev)
-
-        def step():
-            mlp.forward(x, y)
-
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # Timed region: exactly `steps` passes, nothing else on the stream.
-    log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
-    # Kernel region: the same number of passes again, with the library
-    # recording HIP events around every kernel on the stream it runs on. The
-    # events cost ~15 us per step, so they stay out of the timed region above.
-    mlp.read_timing()
-    mlp.set_timing(True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    mlp.set_timing(False)
-    kt = mlp.read_timing()
-    kernels = {k: v[0] / max(v[1], 1) for k, v in kt.items()}
-    log(f"ms/step {ms:.4f}; kernels {kernels}")
-
-    decode = w.T <= 64 and not backward
-    if backward:
-        import oracle
-        value, unit = oracle.backward_flops(w.T, w.d, w.f, w.act) / (ms * 1e-3) / 1e12, "TFLOP/s"
-    elif decode:
-        value, unit = w.bytes() / (ms * 1e-3) / 1e9, "GB/s"
-    else:
-        value, unit = w.flops() / (ms * 1e-3) / 1e12, "TFLOP/s"
-
-    dom = max(kernels, key=lambda k: kernels[k])
-    flops, byts = kernel_work(w, dom, w.T)
-    dom_s = kernels[dom] * 1e-3
-    if decode:
-        roof = {"bound": "hbm", "achieved": byts / dom_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    else:
-        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-        roof = {"bound": "mfma", "achieved": flops / dom_s / 1e12, "peak": peak, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = read_traffic(w.name, dom)
-    roof["kernel"] = dom
-    roof["kernel_ms"] = kernels[dom]
-    roof["algorithmic_bytes"] = byts
-    roof["algorithmic_flops"] = flops
-
+    res = measure_mlp(w, args, backward=backward)
+    decode = is_decode(w) and not backward
     out = {
         "metric": METRIC_BWD if backward else METRIC,
-        "value": value,
-        "unit": unit,
+        "value": res["value"],
+        "unit": res["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded normal tokens and weights, bf16-rounded)",
-        "config": {"workload": w.name, "T": w.T, "d": w.d, "f": w.f, "P": w.P, "act": w.act,
-                   "ring_order": w.order(), "parallelism": "one TSP rank (shard loop on one GPU)"},
-        "pct_of_peak": (value / (PEAK_HBM_GBS if decode else roof["peak"])) * 100.0,
+        "config": res["config"],
+        "pct_of_peak": res["pct_of_peak"],
         "env": {"gpu": torch.cuda.get_device_name(0),
                 "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
                 "torch": torch.__version__, "hip": torch.version.hip},
-        "kernels_ms": kernels,
-        "pack_ms": pack_ms,
-        "roofline": roof,
-        "cpu_baseline": None,
     }
+    for k in ("median_ms", "min_ms", "max_ms", "first_ms", "value_at_median", "value_at_min", "kernels_ms",
+              "kernel_sum_ms", "pack_ms", "roofline"):
+        out[k] = res[k]
+    out["cpu_baseline"] = None
     if backward:
         out["pass"] = "backward"
-        out["config"]["parallelism"] = "one TSP rank's backward (shard loop on one GPU)"
-        del grads, dy_dev, wg, wu, wd
-    else:
-        del y
-    mlp.close()
-    del x
-    torch.cuda.empty_cache()
+    also = [a for a in args.also.split(",") if a.strip()] if not backward else []
+    if also:
+        out["also"] = []
+        for name in also:
+            wa = workload(name.strip())
+            ra = measure_mlp(wa, args)
+            ra.pop("dtype")
+            out["also"].append(ra)
     if not args.no_ceilings:
         # Measured ceilings of this GPU beside the datasheet peaks, after the
         # timed regions so they do not heat the GPU before them.
@@ -482,7 +555,8 @@ def main():
         log("ceiling probes")
         # The read rate depends on the buffer size (measured: ~7.0 TB/s at
         # 1 GiB, 6.8 at 2 GiB, 6.3 at 4 GiB), so the probe reads as many bytes
-        # as the workload's weights, at least 1 GiB (4x the last-level cache).
+        # as the headline workload's weights, at least 1 GiB (4x the
+        # last-level cache).
         chunk = 64 << 20
         probe_bytes = max(1 << 30, -(-w.bytes() // chunk) * chunk)
         ceil = {"hbm_read_GBs": probe_hbm_read(probe_bytes, 10),
@@ -491,11 +565,14 @@ def main():
                        "loads; 16 independent 16x16x32 bf16 MFMAs per wave, 2 waves per SIMD, "
                        "pseudo-random operands"}
         out["ceilings"] = ceil
+        roof = out["roofline"]
         c = ceil["hbm_read_GBs"] if decode else (ceil["mfma_bf16_TFLOPs"] if w.dtype == "bf16" else None)
         roof["frac_of_measured_ceiling"] = None if c is None else roof["achieved"] / c
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
-        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, dy if backward else None)
+        from sharded_transformer_mlp_amd.inputs import make_inputs, make_output_grad
+        out["cpu_baseline"] = cpu_baseline(w, make_inputs(w), args.cpu_budget,
+                                           make_output_grad(w) if backward else None)
     print(json.dumps(out), flush=True)
 
 

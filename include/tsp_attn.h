@@ -29,9 +29,12 @@
  *
  * The mask hides keys at positions after the query's own (causal) when the
  * handle is causal; otherwise every key is visible. No biases, no position
- * encoding. Q, K, V, the probabilities and O are rounded to bf16 (nearest
- * even) where the kernels store or multiply them; scores, softmax sums and Y
- * accumulate in fp32. Y is fp32 and overwritten.
+ * encoding. Q, K, V and the probabilities are rounded to fp16 (nearest
+ * even, 11 significant bits) where the kernels store or multiply them, O to
+ * bf16 (like the MLP's hidden activations) before the output projection;
+ * scores, softmax sums and Y accumulate in fp32. Y is fp32 and overwritten.
+ * fp16 bounds the projections: an entry of X Wq / sqrt(dh) log2(e), X Wk or
+ * X Wv beyond 65504 in magnitude becomes infinite and the output NaN.
  *
  * The exchange on one GPU: the handle owns the context, keys and values of
  * all S positions for every key/value head. tsp_attn_project_kv(rank rho)

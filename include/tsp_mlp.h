@@ -133,22 +133,23 @@ tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y,
  *   dW_gate[:, s] = X^T . dG_s, dW_up[:, s] = X^T . dU_s,
  *   dW_down[s, :] = H_s^T . dY           (each shard's own blocks),
  * with G_s, U_s, H_s recomputed from X and the handle's packed weights.
+ * Every weight the backward reads comes from the handle: the products with dY
+ * and with dG / dU read a row-major copy that the first backward call unpacks
+ * from the packed records (bit-exact) into the backward workspace, so the
+ * gradients always belong to the weights the handle was created with.
  * bf16 handles only (TSP_ERR_UNSUPPORTED for fp32), and d % 256 == 0 and
  * F % 256 == 0 (TSP_ERR_UNSUPPORTED otherwise).
- * X, dY: device, T x d row-major bf16. w_gate, w_up (d x f) and w_down
- * (f x d): device, row-major bf16, the same values the handle was created
- * with (w_gate NULL for GeLU); they are read for dH and dX. Outputs, device,
- * fp32, overwritten: dX T x d; dW_gate, dW_up d x f (dW_gate NULL for GeLU);
- * dW_down f x d, the weights' own layouts. All pointers 16-byte aligned;
- * outputs must not overlap each other or the inputs. 1 <= T <= T_max
+ * X, dY: device, T x d row-major bf16. Outputs, device, fp32, overwritten:
+ * dX T x d; dW_gate, dW_up d x f (dW_gate NULL for GeLU, required for
+ * SwiGLU); dW_down f x d, the weights' own layouts. All pointers 16-byte
+ * aligned; outputs must not overlap each other or the inputs. 1 <= T <= T_max
  * (T == 0 is a no-op). The first call allocates a backward workspace sized
- * for T_max (TSP_ERR_OOM if that fails); it is freed by tsp_mlp_destroy.
- * Asynchronous like forward, on `stream` (NULL: the handle's stream); it
- * shares nothing with a forward's workspace, but one backward at a time per
- * handle.
+ * for T_max plus the unpacked weights (TSP_ERR_OOM if that fails); it is
+ * freed by tsp_mlp_destroy. Asynchronous like forward, on `stream` (NULL: the
+ * handle's stream); it shares nothing with a forward's workspace, but one
+ * backward at a time per handle.
  */
 tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void* dY,
-                              const void* w_gate, const void* w_up, const void* w_down,
                               float* dX, float* dW_gate, float* dW_up, float* dW_down,
                               hipStream_t stream);
 
@@ -163,12 +164,11 @@ tsp_status_t tsp_mlp_set_path(tsp_mlp_t h, int32_t path);
 
 /* Tuning and test hook for the bf16 tiled path: fix the tile shape of the
  * gate/up and down kernels (-1 = choose per forward from T and the shape).
- * Shapes (features x tokens): 0 = 256 x 256, 1 = 256 x 128, 2 = 128 x 128,
- * 3 = 64 x 128, 4 = 256 x 256 with one wave per SIMD, 5 = 256 x 256 with
- * 16x16x32 MFMAs over global-to-LDS loads, two wave groups in ping-pong,
- * 6 = the same tile with four waves of 128 x 128 (the automatic choice at
- * large T). Shapes 5 and 6 compute bitwise identical results. With down
- * shape 5 or 6 and fewer than 256 output tiles, the ring is split into
+ * Shapes (features x tokens): 0 = 256 x 256 with 16x16x32 MFMAs, four waves of
+ * 128 x 128 over global-to-LDS loads (the automatic choice at large T),
+ * 1 = 256 x 128, 2 = 128 x 128, 3 = 64 x 128 (32x32x16 MFMAs, register-staged
+ * loads; for small T and shard widths that are not multiples of 256). With
+ * down shape 0 and fewer than 256 output tiles, the ring is split into
  * groups of consecutive shards whose fp32 partials are added in ring order.
  * TSP_ERR_UNSUPPORTED if the shape does not divide the shard's
  * packed width (gate/up) or d (down), or for an fp32 handle. */

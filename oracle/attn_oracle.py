@@ -59,15 +59,6 @@ def _f64(a) -> np.ndarray:
     return np.asarray(a, dtype=np.float64)
 
 
-def _round_bf16(a: np.ndarray) -> np.ndarray:
-    """Round float64 values to bfloat16 (nearest, ties to even) and back; a
-    diagnostic of the intermediates the bf16 kernels store, never the bar."""
-    f = np.asarray(a, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).astype(np.float64)
-
-
 def attention_heads(Q, K, V, q_pos, k_pos, causal: bool, group: int) -> np.ndarray:
     """Softmax attention per head.
 
@@ -113,19 +104,14 @@ def attention_unsharded(X, Wq, Wk, Wv, Wo, H: int, Hkv: int, causal: bool = True
 
 def tsp_attention(X_all, Wq, Wk, Wv, Wo, H: int, Hkv: int, P: int, rank: int,
                   order: Optional[Sequence[int]] = None, causal: bool = True,
-                  round_bf16: bool = False, rows: Optional[Sequence[int]] = None,
-                  q_store_scale: float = 1.0) -> np.ndarray:
+                  rows: Optional[Sequence[int]] = None) -> np.ndarray:
     """Rank ``rank``'s output rows of the attention block under TSP.
 
     X_all: the whole S x d sequence (rank rho's tokens are rows
     [rho T, (rho+1) T), T = S / P); the other ranks' rows stand for what the
     key/value exchange delivers. order: the head groups in the order the
-    rank visits them (default: rank, rank+1, ... mod P). round_bf16 rounds Q,
-    K, V and the attention output to bfloat16 before they are used (a
-    diagnostic of the kernels' stored intermediates, not the bar); with
-    q_store_scale the queries are rounded as stored times that factor (a
-    store that folds the softmax scale into them) and divided back. rows: only
-    these of the rank's token rows (queries are independent of each other).
+    rank visits them (default: rank, rank+1, ... mod P). rows: only these of
+    the rank's token rows (queries are independent of each other).
     """
     X_all = _f64(X_all)
     S, d = X_all.shape
@@ -138,7 +124,6 @@ def tsp_attention(X_all, Wq, Wk, Wv, Wo, H: int, Hkv: int, P: int, rank: int,
         order = [(rank + k) % P for k in range(P)]
     if sorted(order) != list(range(P)):
         raise ValueError("order must be a permutation of 0..P-1")
-    rnd = _round_bf16 if round_bf16 else (lambda a: a)
     X_r = X_all[rank * T:(rank + 1) * T]
     q_pos = np.arange(rank * T, (rank + 1) * T)
     if rows is not None:
@@ -148,12 +133,12 @@ def tsp_attention(X_all, Wq, Wk, Wv, Wo, H: int, Hkv: int, P: int, rank: int,
     Y = np.zeros((Tq, d))
     for s in order:
         cq, ckv = head_columns(s, Hs, dh), head_columns(s, Hks, dh)
-        Q = (rnd(q_store_scale * (X_r @ _f64(Wq)[:, cq])) / q_store_scale).reshape(Tq, Hs, dh)
+        Q = (X_r @ _f64(Wq)[:, cq]).reshape(Tq, Hs, dh)
         # sequence-wise exchange: every rank's keys and values of head group s
-        K = rnd(np.concatenate([X_all[rho * T:(rho + 1) * T] @ _f64(Wk)[:, ckv] for rho in range(P)]))
-        V = rnd(np.concatenate([X_all[rho * T:(rho + 1) * T] @ _f64(Wv)[:, ckv] for rho in range(P)]))
+        K = np.concatenate([X_all[rho * T:(rho + 1) * T] @ _f64(Wk)[:, ckv] for rho in range(P)])
+        V = np.concatenate([X_all[rho * T:(rho + 1) * T] @ _f64(Wv)[:, ckv] for rho in range(P)])
         O = attention_heads(Q, K.reshape(S, Hks, dh), V.reshape(S, Hks, dh), q_pos, k_pos, causal, Hs // Hks)
-        Y += rnd(O.reshape(Tq, Hs * dh)) @ _f64(Wo)[cq, :]
+        Y += O.reshape(Tq, Hs * dh) @ _f64(Wo)[cq, :]
     return Y
 
 

@@ -7,6 +7,7 @@ file, where the binding loads it.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -48,14 +49,40 @@ def sources():
 EXTRA_FLAGS = {"attn_core.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
+# Every kernel's register use is reported by the compiler; a kernel that
+# needs scratch memory (registers spilled to memory) fails the build: such a
+# spill once came with wrong accumulator values, and it always costs memory
+# traffic in the hot loops. Spills into free accumulation registers use no
+# memory and are allowed.
+RESOURCE_REMARKS = ["-Rpass-analysis=kernel-resource-usage", "-fno-caret-diagnostics"]
+
+
+def _check_spills(src: str, remarks) -> None:
+    fn, bad = None, []
+    for line in remarks:
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            fn = m.group(1)
+            continue
+        m = re.search(r"(ScratchSize \[bytes/lane\]): (\d+)", line)
+        if m and int(m.group(2)) > 0:
+            bad.append(f"{fn}: {m.group(1)} {m.group(2)}")
+    if bad:
+        raise RuntimeError(f"{src}: kernels use scratch memory:\n  " + "\n  ".join(bad))
+
+
 def _compile(src: str, tag: str = "", defs=()) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + tag + ".o")
-    cmd = [hipcc(), *HIPFLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), *defs, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIPFLAGS, *RESOURCE_REMARKS, *EXTRA_FLAGS.get(os.path.basename(src), []), *defs, "-c", src,
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+    lines = [l for l in r.stderr.splitlines() if noise not in l]
+    remarks = [l for l in lines if "kernel-resource-usage" in l]
+    err = "\n".join(l for l in lines if "kernel-resource-usage" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{err}")
+    _check_spills(src, remarks)
     if err.strip():
         sys.stderr.write(err + "\n")
     return obj

@@ -64,6 +64,7 @@ struct tsp_mlp {
     int64_t work_bytes = 0;
     void* bwd = nullptr;                       // backward workspace (first backward call)
     int64_t bwd_bytes = 0;
+    bool bwd_unpacked = false;                 // the weights in the backward workspace are filled
     int64_t part_off = 0;                      // byte offset of the down-split partials in work
     int32_t path = TSP_PATH_AUTO;
     int32_t cfg_gateup = -1, cfg_down = -1;   // tiled shapes; -1 = chosen per forward
@@ -278,68 +279,97 @@ tsp_status_t tsp_mlp_create(tsp_mlp_t* out, int64_t T_max, int64_t d, int64_t f,
     return TSP_OK;
 }
 
-tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y, hipStream_t stream) {
-    if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
-    if (T < 0 || T > h->T_max) return fail(TSP_ERR_INVALID_ARG, "T=%lld out of [0, T_max=%lld]", (long long)T, (long long)h->T_max);
-    if (T == 0) return TSP_OK;
+}  // extern "C"
+
+namespace {
+
+// Workspace bytes a forward of T tokens needs (the hidden activations, then
+// the down-split partials at part_off), for the path and tile shapes the
+// forward will take.
+struct FwdPlan {
+    bool skinny = false;
+    int cg = -1, cd = -1, split = 1;
+    int64_t h_bytes = 0, part_off = 0, total = 0;
+};
+
+tsp_status_t plan_forward(const tsp_mlp* h, int64_t T, FwdPlan& pl) {
+    const int64_t d = h->d, f = h->f;
+    if (h->dtype == TSP_DTYPE_BF16) {
+        const bool sk_ok = T <= tsp::SKINNY_T_MAX && tsp::skinny_supported((int)d, (int)h->F, h->P);
+        if (h->path == TSP_PATH_SKINNY) {
+            if (!sk_ok) return fail(TSP_ERR_UNSUPPORTED, "skinny path needs T <= %d, d %% 256 == 0 and P*F %% 1024 == 0", tsp::SKINNY_T_MAX);
+            pl.skinny = true;
+        } else if (h->path == TSP_PATH_AUTO) {
+            pl.skinny = sk_ok;
+        }
+        if (pl.skinny) {
+            pl.h_bytes = (T + 31) / 32 * 32 * f * 2;
+        } else {
+            const int swiglu = h->act == TSP_ACT_SWIGLU ? 1 : 0;
+            pl.cg = h->cfg_gateup >= 0 ? h->cfg_gateup : tsp::choose_gateup_cfg((int)T, (int)d, (int)h->F, h->P, swiglu);
+            pl.cd = h->cfg_down >= 0 ? h->cfg_down : tsp::choose_down_cfg((int)T, (int)d, (int)h->F, h->P);
+            if (pl.cg < 0 || pl.cd < 0) return fail(TSP_ERR_UNSUPPORTED, "no tile shape fits d=%lld F=%lld", (long long)d, (long long)h->F);
+            pl.split = tsp::choose_down_split((int)T, (int)d, h->P, pl.cd);
+            const int64_t n_tok_tiles = (T + 63) / 64;
+            if (n_tok_tiles * (2 * f / 64 + d / 64) > INT32_MAX / 2) return fail(TSP_ERR_UNSUPPORTED, "grid too large");
+            pl.h_bytes = T * f * 2;
+        }
+    } else {
+        if (h->path == TSP_PATH_SKINNY) return fail(TSP_ERR_UNSUPPORTED, "skinny path is bf16 only");
+        pl.h_bytes = T * f * 4;
+    }
+    pl.part_off = (pl.h_bytes + 255) / 256 * 256;
+    pl.total = pl.part_off + (pl.split > 1 ? (int64_t)pl.split * T * d * 4 : 0);
+    return TSP_OK;
+}
+
+tsp_status_t check_forward_args(const tsp_mlp* h, int64_t T, const void* X, const float* Y) {
     if (!X || !Y) return fail(TSP_ERR_INVALID_ARG, "X or Y is NULL");
     if (!aligned16(X) || !aligned16(Y)) return fail(TSP_ERR_INVALID_ARG, "X and Y must be 16-byte aligned");
     const int64_t es = h->dtype == TSP_DTYPE_BF16 ? 2 : 4;
     const uintptr_t x0 = reinterpret_cast<uintptr_t>(X), x1 = x0 + (uintptr_t)(T * h->d * es);
     const uintptr_t y0 = reinterpret_cast<uintptr_t>(Y), y1 = y0 + (uintptr_t)(T * h->d * 4);
     if (x0 < y1 && y0 < x1) return fail(TSP_ERR_INVALID_ARG, "Y overlaps X");
-    hipStream_t st = stream ? stream : h->stream;
+    return TSP_OK;
+}
+
+// The forward's launches with the workspace at `work` (hidden activations at
+// 0, split partials at pl.part_off). timing = false launches nothing but the
+// kernels (no events are created or recorded).
+tsp_status_t run_forward(tsp_mlp* h, int64_t T, const void* X, float* Y, hipStream_t st, const FwdPlan& pl,
+                         void* work, bool timing) {
     const bool swiglu = h->act == TSP_ACT_SWIGLU;
-
-    DeviceGuard guard(h->device);
-    if (!guard.ok) return fail(TSP_ERR_HIP, "cannot select the handle's device");
-
+    const bool saved = h->timing;
+    h->timing = h->timing && timing;
+    struct Restore { tsp_mlp* h; bool v; ~Restore() { h->timing = v; } } restore{h, saved};
     tsp_status_t s;
     if (h->dtype == TSP_DTYPE_BF16) {
         tsp::Bf16Args a;
         a.packed = static_cast<const uint16_t*>(h->packed);
         a.x = static_cast<const uint16_t*>(X);
-        a.h = static_cast<uint16_t*>(h->work);
+        a.h = static_cast<uint16_t*>(work);
         a.y = Y;
-        a.part = reinterpret_cast<float*>(static_cast<char*>(h->work) + h->part_off);
+        a.part = reinterpret_cast<float*>(static_cast<char*>(work) + pl.part_off);
         a.shard_elems = h->shard_elems;
         a.down_off = h->down_off;
         a.T = (int)T; a.d = (int)h->d; a.f = (int)h->f; a.F = (int)h->F; a.P = h->P;
         a.swiglu = swiglu ? 1 : 0;
-        const bool sk_ok = T <= tsp::SKINNY_T_MAX && tsp::skinny_supported(a.d, a.F, a.P);
-        bool skinny = false;
-        if (h->path == TSP_PATH_SKINNY) {
-            if (!sk_ok) return fail(TSP_ERR_UNSUPPORTED, "skinny path needs T <= %d, d %% 256 == 0 and P*F %% 1024 == 0", tsp::SKINNY_T_MAX);
-            skinny = true;
-        } else if (h->path == TSP_PATH_AUTO) {
-            skinny = sk_ok;
-        }
-        if (skinny) {
+        if (pl.skinny) {
             s = timed_launch(h, "skinny_gateup", st, [&] { return tsp::launch_gateup_skinny(a, st); });
             if (s != TSP_OK) return s;
             return timed_launch(h, "skinny_down", st, [&] { return tsp::launch_down_skinny(a, st); });
         }
-        const int cg = h->cfg_gateup >= 0 ? h->cfg_gateup : tsp::choose_gateup_cfg(a.T, a.d, a.F, a.P, a.swiglu);
-        const int cd = h->cfg_down >= 0 ? h->cfg_down : tsp::choose_down_cfg(a.T, a.d, a.F, a.P);
-        const int split = tsp::choose_down_split(a.T, a.d, a.P, cd);
-        if (split > 1 && (int64_t)split * T * a.d * 4 > h->work_bytes - h->part_off)
-            return fail(TSP_ERR_HIP, "internal: split partials exceed the workspace");
-        const int64_t n_tok_tiles = (T + 63) / 64;
-        if (n_tok_tiles * (int64_t)(2 * a.f / 64 + a.d / 64) > INT32_MAX / 2)
-            return fail(TSP_ERR_UNSUPPORTED, "grid too large");
-        if (cg < 0 || cd < 0) return fail(TSP_ERR_UNSUPPORTED, "no tile shape fits d=%d F=%d", a.d, a.F);
-        s = timed_launch(h, "gateup_tiled", st, [&] { return tsp::launch_gateup_tiled(a, cg, st); });
+        s = timed_launch(h, "gateup_tiled", st, [&] { return tsp::launch_gateup_tiled(a, pl.cg, st); });
         if (s != TSP_OK) return s;
-        s = timed_launch(h, "down_tiled", st, [&] { return tsp::launch_down_tiled(a, cd, split, st); });
-        if (s != TSP_OK || split == 1) return s;
+        s = timed_launch(h, "down_tiled", st, [&] { return tsp::launch_down_tiled(a, pl.cd, pl.split, st); });
+        if (s != TSP_OK || pl.split == 1) return s;
         return timed_launch(h, "reduce_partials", st,
-                            [&] { return tsp::launch_reduce_partials(a.part, split, T * a.d, Y, st); });
+                            [&] { return tsp::launch_reduce_partials(a.part, pl.split, T * a.d, Y, st); });
     }
-    if (h->path == TSP_PATH_SKINNY) return fail(TSP_ERR_UNSUPPORTED, "skinny path is bf16 only");
     tsp::F32Args a;
     a.packed = static_cast<const float*>(h->packed);
     a.x = static_cast<const float*>(X);
-    a.h = static_cast<float*>(h->work);
+    a.h = static_cast<float*>(work);
     a.y = Y;
     a.shard_elems = h->shard_elems;
     a.T = (int)T; a.d = (int)h->d; a.f = (int)h->f; a.F = (int)h->F; a.P = h->P;
@@ -349,13 +379,39 @@ tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y, hi
     return timed_launch(h, "down_f32", st, [&] { return tsp::launch_down_f32(a, st); });
 }
 
+}  // namespace
+
+extern "C" {
+
+tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y, hipStream_t stream) {
+    if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
+    if (T < 0 || T > h->T_max) return fail(TSP_ERR_INVALID_ARG, "T=%lld out of [0, T_max=%lld]", (long long)T, (long long)h->T_max);
+    if (T == 0) return TSP_OK;
+    tsp_status_t s = check_forward_args(h, T, X, Y);
+    if (s != TSP_OK) return s;
+    FwdPlan pl;
+    s = plan_forward(h, T, pl);
+    if (s != TSP_OK) return s;
+    if (pl.h_bytes > h->part_off || pl.total - pl.part_off > h->work_bytes - h->part_off)
+        return fail(TSP_ERR_HIP, "internal: the forward's workspace exceeds the handle's");
+    pl.part_off = h->part_off;                  // the handle's layout: partials after T_max tokens of H
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return fail(TSP_ERR_HIP, "cannot select the handle's device");
+    return run_forward(h, T, X, Y, stream ? stream : h->stream, pl, h->work, true);
+}
+
+}  // extern "C"
+
+extern "C" {
+
 namespace {
 
 // Backward workspace, regions in bytes for T_max tokens (each 256-aligned):
 // transposed X and dY (d x Tp), dH (T x f fp32), dG, dU, H (T x f bf16) and
-// their transposes (f x Tp), Tp = T_max rounded up to 64.
+// their transposes (f x Tp), Tp = T_max rounded up to 64; then the weights
+// (bf16, row-major Wg, Wu d x f and Wd f x d) unpacked from the records.
 struct BwdLayout {
-    int64_t xt, dyt, dh, dg, du, hb, dgt, dut, ht, total;
+    int64_t xt, dyt, dh, dg, du, hb, dgt, dut, ht, wg, wu, wd, total;
 };
 
 BwdLayout bwd_layout(int64_t T_max, int64_t d, int64_t f) {
@@ -372,6 +428,9 @@ BwdLayout bwd_layout(int64_t T_max, int64_t d, int64_t f) {
     L.dgt = o; o += up(f * Tp * 2);
     L.dut = o; o += up(f * Tp * 2);
     L.ht = o; o += up(f * Tp * 2);
+    L.wg = o; o += up(d * f * 2);                   // row-major weights unpacked from the records
+    L.wu = o; o += up(d * f * 2);
+    L.wd = o; o += up(f * d * 2);
     L.total = o;
     return L;
 }
@@ -383,33 +442,31 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 
 }  // namespace
 
-tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void* dY, const void* w_gate,
-                              const void* w_up, const void* w_down, float* dX, float* dW_gate, float* dW_up,
-                              float* dW_down, hipStream_t stream) {
+tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void* dY, float* dX, float* dW_gate,
+                              float* dW_up, float* dW_down, hipStream_t stream) {
     if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
     if (T < 0 || T > h->T_max) return fail(TSP_ERR_INVALID_ARG, "T=%lld out of [0, T_max=%lld]", (long long)T, (long long)h->T_max);
     if (h->dtype != TSP_DTYPE_BF16) return fail(TSP_ERR_UNSUPPORTED, "the backward is bf16 only");
     if (h->d % 256 || h->F % 256) return fail(TSP_ERR_UNSUPPORTED, "the backward needs d %% 256 == 0 and F %% 256 == 0");
     if (T == 0) return TSP_OK;
     const bool swiglu = h->act == TSP_ACT_SWIGLU;
-    if (!X || !dY || !w_up || !w_down || !dX || !dW_up || !dW_down)
-        return fail(TSP_ERR_INVALID_ARG, "a required pointer is NULL");
-    if (swiglu != (w_gate != nullptr) || swiglu != (dW_gate != nullptr))
-        return fail(TSP_ERR_INVALID_ARG, "w_gate and dW_gate are required for SwiGLU and must be NULL for GeLU");
-    const void* ptrs[] = {X, dY, w_gate, w_up, w_down, dX, dW_gate, dW_up, dW_down};
+    if (!X || !dY || !dX || !dW_up || !dW_down) return fail(TSP_ERR_INVALID_ARG, "a required pointer is NULL");
+    if (swiglu != (dW_gate != nullptr))
+        return fail(TSP_ERR_INVALID_ARG, "dW_gate is required for SwiGLU and must be NULL for GeLU");
+    const void* ptrs[] = {X, dY, dX, dW_gate, dW_up, dW_down};
     for (const void* q : ptrs)
         if (q && !aligned16(q)) return fail(TSP_ERR_INVALID_ARG, "every pointer must be 16-byte aligned");
     const int64_t d = h->d, f = h->f;
     struct Span { const void* p; int64_t n; };
     const Span outs[] = {{dX, T * d * 4}, {dW_gate, d * f * 4}, {dW_up, d * f * 4}, {dW_down, f * d * 4}};
-    const Span ins[] = {{X, T * d * 2}, {dY, T * d * 2}, {w_gate, d * f * 2}, {w_up, d * f * 2}, {w_down, f * d * 2}};
+    const Span ins[] = {{X, T * d * 2}, {dY, T * d * 2}};
     for (int i = 0; i < 4; ++i) {
         if (!outs[i].p) continue;
         for (int j = i + 1; j < 4; ++j)
             if (outs[j].p && overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
                 return fail(TSP_ERR_INVALID_ARG, "gradient outputs overlap each other");
         for (const Span& in : ins)
-            if (in.p && overlaps(outs[i].p, outs[i].n, in.p, in.n))
+            if (overlaps(outs[i].p, outs[i].n, in.p, in.n))
                 return fail(TSP_ERR_INVALID_ARG, "a gradient output overlaps an input");
     }
     hipStream_t st = stream ? stream : h->stream;
@@ -424,6 +481,7 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
             return fail(TSP_ERR_OOM, "backward workspace of %lld bytes: %s", (long long)L.total, hipGetErrorString(e));
         }
         h->bwd_bytes = L.total;
+        h->bwd_unpacked = false;
     }
     char* wsp = static_cast<char*>(h->bwd);
     auto bf = [&](int64_t off) { return reinterpret_cast<uint16_t*>(wsp + off); };
@@ -434,9 +492,19 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
     const int F = (int)h->F, P = h->P;
     const auto* x16 = static_cast<const uint16_t*>(X);
     const auto* dy16 = static_cast<const uint16_t*>(dY);
-    const auto* wg16 = static_cast<const uint16_t*>(w_gate);
-    const auto* wu16 = static_cast<const uint16_t*>(w_up);
-    const auto* wd16 = static_cast<const uint16_t*>(w_down);
+    const uint16_t* wg16 = swiglu ? bf(L.wg) : nullptr;
+    const uint16_t* wu16 = bf(L.wu);
+    const uint16_t* wd16 = bf(L.wd);
+    if (!h->bwd_unpacked) {
+        // the handle's weights in the row-major layout the dY and dG / dU
+        // products read, once per handle (the records never change)
+        tsp_status_t su = timed_launch(h, "bwd_unpack", st, [&] {
+            return tsp::launch_unpack_bf16(h->packed, bf(L.wg), bf(L.wu), bf(L.wd), h->order_dev, h->shard_elems,
+                                           h->down_off, (int)d, (int)f, (int)h->F, h->P, swiglu ? 1 : 0, st);
+        });
+        if (su != TSP_OK) return su;
+        h->bwd_unpacked = true;
+    }
 
     tsp_status_t s = timed_launch(h, "bwd_transpose_in", st, [&] {
         hipError_t e = tsp::launch_transpose_bf16(x16, (int)T, (int)d, (int)d, xt, Tp, st);

@@ -17,10 +17,11 @@
 //   pack_qkv_bf16  packs head group s's columns of Wq, Wk, Wv as one record
 //                  (Q heads, then K heads, then V heads), in the MLP's
 //                  fragment-block layout, records in visiting order.
-//   qkv_w16        the projection: the MLP's shape-6 pipeline (w16.h) over
-//                  the records with a plain epilogue that sends each 128-column
-//                  head to its place: Q to the rank's query buffer, K rows to
-//                  the key context, V transposed to the value context.
+//   qkv_w16        the projection: the MLP's 256 x 256 pipeline (w16.h) over
+//                  the records with a plain epilogue that rounds to fp16 and
+//                  sends each 128-column head to its place: Q to the rank's
+//                  query buffer, K rows to the key context, V transposed to
+//                  the value context.
 //   attn_fwd       (attn_core.hip) the attention itself; the output
 //                  projection is the MLP's down product (gemm_tiled.hip).
 #include "attn.h"
@@ -74,7 +75,7 @@ __global__ void pack_qkv_bf16(const uint16_t* __restrict__ wq, const uint16_t* _
 template <bool BUF>
 __global__ __launch_bounds__(256) void qkv_w16(ProjArgs a, int n_ft_shard, int n_tt) {
     using namespace w16;
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
     poison_lds(lds, sizeof(lds));
     int ttile, flin;
     raster(xcd_remap(blockIdx.x, gridDim.x), a.P * n_ft_shard, n_tt, ttile, flin);
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(256) void qkv_w16(ProjArgs a, int n_ft_shard, int n
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const f32x4 u = acc[i][j] * sc;
-            stg.put4((wn * TN + j) * 16 + (lane & 15), c, pack4_bf16(u[0], u[1], u[2], u[3]));
+            stg.put4((wn * TN + j) * 16 + (lane & 15), c, pack4_f16(u[0], u[1], u[2], u[3]));
         }
     }
     lgkm_zero();

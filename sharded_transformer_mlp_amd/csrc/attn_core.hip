@@ -20,7 +20,7 @@ namespace tsp {
 // Workgroup: 4 waves, each 64 queries of one head against 64-key blocks of
 // the context; the 4 waves share the key/value head (hw heads x qs query
 // sub-tiles, hw * qs = 4), so one K tile and one V tile in LDS serve them all.
-// With v_mfma_f32_16x16x32_bf16 a wave computes S^T = K Q^T (keys as rows:
+// With v_mfma_f32_16x16x32_f16 a wave computes S^T = K Q^T (keys as rows:
 // lane l holds 4 consecutive keys of query l % 16), so a query's softmax
 // statistics sit in one lane column and reduce with two cross-lane steps; the
 // probabilities then feed O^T = V^T P^T as the B operand straight from the
@@ -37,12 +37,18 @@ namespace tsp {
 //
 // Softmax with a fixed exponent reference per query instead of a running
 // maximum: the first block's maximum. O / l does not depend on the reference,
-// and probabilities up to 2^64 (a later block's scores up to 64 above it, in
-// log2 units) are exact enough in fp32 and bf16, so the accumulators are never
-// rescaled (rescaling them, 128 accumulation registers, cost more than the
-// exponentials). A block that exceeds the reference by more than that sets a
+// so the accumulators are never rescaled (rescaling them, 128 accumulation
+// registers, cost more than the exponentials). The probabilities enter the
+// P.V product as fp16, whose range bounds them: a block whose scores exceed
+// the reference by more than ~16 log2 units (a probability above 65504) sets a
 // workgroup flag; the workgroup then finds every query's true maximum in a
-// pass over the keys and starts again with it (rare: logits 44 nats apart).
+// pass over the keys and starts again with it (rare: logits 11 nats above the
+// first block's largest).
+//
+// Precision: queries, keys and values arrive as fp16 from the projection and
+// the probabilities are rounded to fp16 (11 significant bits: each rounding
+// a relative 2^-11 at most, 8x finer than bf16); the fp32 output is rounded
+// once, to bf16, for the output projection.
 
 constexpr int ATT_KROW = 128;   // K tile row (elements)
 constexpr int ATT_VROW = 64;    // V^T tile row (elements)
@@ -51,12 +57,12 @@ __device__ __forceinline__ void att_vm_zero() {
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
 }
 
-__device__ inline bf16x8 att_pack8(f32x4 lo, f32x4 hi) {
-    bf16x8 r;
-    r[0] = static_cast<__bf16>(lo[0]); r[1] = static_cast<__bf16>(lo[1]);
-    r[2] = static_cast<__bf16>(lo[2]); r[3] = static_cast<__bf16>(lo[3]);
-    r[4] = static_cast<__bf16>(hi[0]); r[5] = static_cast<__bf16>(hi[1]);
-    r[6] = static_cast<__bf16>(hi[2]); r[7] = static_cast<__bf16>(hi[3]);
+__device__ inline f16x8 att_pack8(f32x4 lo, f32x4 hi) {
+    f16x8 r;
+    r[0] = static_cast<_Float16>(lo[0]); r[1] = static_cast<_Float16>(lo[1]);
+    r[2] = static_cast<_Float16>(lo[2]); r[3] = static_cast<_Float16>(lo[3]);
+    r[4] = static_cast<_Float16>(hi[0]); r[5] = static_cast<_Float16>(hi[1]);
+    r[6] = static_cast<_Float16>(hi[2]); r[7] = static_cast<_Float16>(hi[3]);
     return r;
 }
 
@@ -94,13 +100,13 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
     const int64_t qo_col = ((int64_t)k * a.Hs + hl) * 128;
 
     // Q^T fragments (B operand): query t*16 + n16, head dims ks*32 + 8g .. + 7
-    bf16x8 qf[QT][4];
+    f16x8 qf[QT][4];
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
         const int row = min(q0 + t * 16 + n16, a.T - 1);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-            qf[t][ks] = *reinterpret_cast<const bf16x8*>(a.q + (int64_t)row * a.ldq + qo_col + ks * 32 + 8 * g);
+            qf[t][ks] = *reinterpret_cast<const f16x8*>(a.q + (int64_t)row * a.ldq + qo_col + ks * 32 + 8 * g);
     }
     // (the projection stored the queries scaled by log2(e)/sqrt(dh): the
     // scores come out in log2 units)
@@ -150,26 +156,26 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
     // K fragments of one 32-dim step of that half (from buffer `buf`), and
     // the step's 8 MFMAs of S^T = K Q^T (2 key tiles x 4 query tiles); ks == 0
     // starts the accumulators.
-    auto read_k = [&](int ks, int buf, int h, bf16x8 (&kf)[2]) {
+    auto read_k = [&](int ks, int buf, int h, f16x8 (&kf)[2]) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-            kf[u] = *reinterpret_cast<const bf16x8*>(
+            kf[u] = *reinterpret_cast<const f16x8*>(
                 &k_lds[buf][((2 * h + u) * 16 + n16) * ATT_KROW + ((4 * ks + g) ^ n16) * 8]);
     };
     // init[t]: the accumulators' start for ks == 0 (zero, or minus the
     // query's reference so that the scores come out already shifted)
-    auto s_mfma = [&](int ks, const bf16x8 (&kf)[2], f32x4 (&sc)[2][QT], const float (&init)[QT]) {
+    auto s_mfma = [&](int ks, const f16x8 (&kf)[2], f32x4 (&sc)[2][QT], const float (&init)[QT]) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int t = 0; t < QT; ++t)
-                sc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                sc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                     kf[u], qf[t][ks], ks == 0 ? f32x4{init[t], init[t], init[t], init[t]} : sc[u][t], 0, 0, 0);
     };
     const float zero_init[QT] = {};
     // all four steps, each step's K fragments read one step ahead
     auto s_half = [&](int buf, int h, f32x4 (&sc)[2][QT]) {
-        bf16x8 kf[2][2];
+        f16x8 kf[2][2];
         read_k(0, buf, h, kf[0]);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
     };
     // probabilities of query tile t against the fixed reference, added into
     // the lane's partial sum and packed as the B operand of the P.V step
-    auto softmax_t = [&](f32x4 (&sc)[2][QT], int t, bf16x8 (&pb)[QT], bool shifted) {
+    auto softmax_t = [&](f32x4 (&sc)[2][QT], int t, f16x8 (&pb)[QT], bool shifted) {
         const float ref = m[t] == -INFINITY ? 0.f : m[t];
         float ls = 0.f;
 #pragma unroll
@@ -221,17 +227,17 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
     // V^T fragment dt of half h (the 8 keys lane group g multiplies)
     auto read_v = [&](int buf, int h, int dt) {
         const int r = dt * 16 + n16;
-        return *reinterpret_cast<const bf16x8*>(&v_lds[buf][r * ATT_VROW + ((4 * h + g) ^ ((r >> 1) & 7)) * 8]);
+        return *reinterpret_cast<const f16x8*>(&v_lds[buf][r * ATT_VROW + ((4 * h + g) ^ ((r >> 1) & 7)) * 8]);
     };
     // O^T += V^T P^T over half h of the V^T tile in buffer `buf`, fragments
     // read two ahead; vf holds the first two (read early by the caller)
-    auto pv = [&](int buf, int h, const bf16x8 (&pb)[QT], bf16x8 (&vf)[3]) {
+    auto pv = [&](int buf, int h, const f16x8 (&pb)[QT], f16x8 (&vf)[3]) {
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
             if (dt + 2 < 8) vf[(dt + 2) % 3] = read_v(buf, h, dt + 2);
 #pragma unroll
             for (int t = 0; t < QT; ++t)
-                o[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt % 3], pb[t], o[dt][t], 0, 0, 0);
+                o[dt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[dt % 3], pb[t], o[dt][t], 0, 0, 0);
         }
     };
     // half n+1's scores on the matrix cores while the VALU turns half n's
@@ -240,7 +246,7 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
     // next half's always do (init = minus the reference)
     auto step = [&](int kbuf_next, int h_next, f32x4 (&cur)[2][QT], f32x4 (&nxt)[2][QT], int vbuf, int h,
                     bool cur_shifted, const float (&negref)[QT]) {
-        bf16x8 pb[QT], kf[2][2], vf[3];
+        f16x8 pb[QT], kf[2][2], vf[3];
         read_k(0, kbuf_next, h_next, kf[0]);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
         pv(vbuf, h, pb, vf);
     };
     auto last_step = [&](f32x4 (&cur)[2][QT], int vbuf, int h, bool shifted) {
-        bf16x8 pb[QT], vf[3];
+        f16x8 pb[QT], vf[3];
         vf[0] = read_v(vbuf, h, 0);
         vf[1] = read_v(vbuf, h, 1);
 #pragma unroll
@@ -338,12 +344,13 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
             }
             __syncthreads();
         }
-        // a probability above 2^64 (scores more than 64 log2 units above the
-        // reference) shows in the lane's partial sum; an unneeded restart on
+        // a probability beyond fp16's range (above 65504: a score more than
+        // ~16 log2 units above the reference) shows in the lane's partial sum,
+        // which bounds every probability it adds up; an unneeded restart on
         // many large ones only costs time
         bool over = false;
 #pragma unroll
-        for (int t = 0; t < QT; ++t) over |= !(l[t] <= 1.8446744e19f);
+        for (int t = 0; t < QT; ++t) over |= !(l[t] <= 65000.0f);
         if (__any(over)) restart_flag = 1;
         __syncthreads();
         if (!restart_flag) break;                        // same value in every wave

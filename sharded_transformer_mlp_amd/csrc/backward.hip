@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void transpose_bf16(const uint16_t* __restrict
 template <bool BUF>
 __global__ __launch_bounds__(256) void nt_w16(NtGroup grp) {
     using namespace w16;
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
     poison_lds(lds, sizeof(lds));
     const int lin = xcd_remap(blockIdx.x, gridDim.x);
     const int gi = lin < grp.first[1] ? 0 : (lin < grp.first[2] ? 1 : 2);
@@ -86,6 +86,8 @@ __global__ __launch_bounds__(256) void nt_w16(NtGroup grp) {
     RowSrc<BUF> src;
     src.ls = 0;
     src.j = 0;
+    src.lsb = 0;
+    src.jb = 0;
     src.spp = p.spp;
     src.nseg = p.nseg;
     src.kinds = p.kinds;
@@ -106,7 +108,8 @@ __global__ __launch_bounds__(256) void nt_w16(NtGroup grp) {
     src.wm = wm;
     src.wn = wn;
     src.lane = lane;
-    src.seek(0);
+    src.seek_a(0);
+    src.seek_b(0);
     f32x4 acc[TM][TN];
     w16::mainloop(lds, acc, p.spp * p.nseg, src);
 
@@ -146,7 +149,7 @@ __device__ inline float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.0f +
 template <int ACT, bool BUF>
 __global__ __launch_bounds__(256) void gateup_bwd_w16(Bf16Args a, BwdArgs b, int n_ft_shard, int n_tt) {
     using namespace w16;
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
     poison_lds(lds, sizeof(lds));
     int ttile, flin;
     raster(xcd_remap(blockIdx.x, gridDim.x), a.P * n_ft_shard, n_tt, ttile, flin);
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(256) void gateup_bwd_w16(Bf16Args a, BwdArgs b, int
     constexpr int NB = ACT == 1 ? 4 : TM;               // 16-column blocks of the wave
     constexpr int NO = ACT == 1 ? 3 : 2;                // outputs
     using Stg = StagedRows16<COLS, 128>;
-    static_assert(NO * Stg::ELEMS <= NS * STAGE, "LDS");
+    static_assert(NO * Stg::ELEMS <= LDS_ELEMS, "LDS");
     const int lc0 = ftile * COLS;
     const int64_t ring0 = (int64_t)k * a.F + lc0, nat0 = (int64_t)b.order[k] * a.F + lc0;
     const int fsub = 4 * (lane >> 4);
@@ -230,6 +233,10 @@ __global__ __launch_bounds__(256) void gateup_bwd_w16(Bf16Args a, BwdArgs b, int
                     sh.put4(r, c, pack4_bf16(h[0], h[1], h[2], h[3]));
                 }
             }
+            // one block's dH loads in flight at a time: hoisting every block's
+            // loads ahead of the arithmetic (8 blocks x 16 registers for GeLU)
+            // ran the kernel out of registers
+            __builtin_amdgcn_sched_barrier(0);
         }
         lgkm_zero();
         stage_barrier();

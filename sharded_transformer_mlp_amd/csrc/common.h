@@ -22,6 +22,7 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -91,6 +92,20 @@ __device__ inline float gelu_tanh_f(float u) {
 __device__ inline uint16_t bf16_bits(float x) {
     __bf16 b = static_cast<__bf16>(x);    // round to nearest even
     return __builtin_bit_cast(uint16_t, b);
+}
+
+// fp16 (IEEE half) storage, round to nearest even; magnitudes above 65504
+// become infinite.
+__device__ inline uint16_t f16_bits(float x) {
+    _Float16 h = static_cast<_Float16>(x);
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ inline uint2 pack4_f16(float a, float b, float c, float d) {
+    uint2 r;
+    r.x = (uint32_t)f16_bits(a) | ((uint32_t)f16_bits(b) << 16);
+    r.y = (uint32_t)f16_bits(c) | ((uint32_t)f16_bits(d) << 16);
+    return r;
 }
 
 __device__ inline uint2 pack4_bf16(float a, float b, float c, float d) {

@@ -1,121 +1,177 @@
-// fp32 kernels of the sharded MLP: LDS-tiled FMA, any shape.
+// fp32 kernels of the sharded MLP: v_mfma_f32_16x16x4_f32 over LDS tiles, any
+// shape (ragged edges are zero-filled in LDS and masked at the store).
 //
 // Used for fp32 storage (the parity-grade path). Same schedule as the bf16
 // path: gate/up (or first-matrix) products per shard with the activation
-// applied on the shard's own columns, then the down products accumulated
-// over the shards in ring order into an fp32 Y.
+// applied on the shard's own columns ("Tensor Parallelism: Splitting the
+// Math", section "Why the column-then-row split": the nonlinearity is exact on
+// a shard's own columns), then the down products accumulated over the shards
+// in ring order into an fp32 Y ("Folding Tensor and Sequence Parallelism
+// ...", Abstract: partial outputs accumulate locally).
 // Per-shard fp32 record: [gate d x F][up d x F][down F x d], row-major
 // (GeLU: [A d x F][B F x d]); records and the hidden columns of the
 // workspace are stored in ring order, record k holding shard order[k].
+//
+// Both products put output features on the MFMA rows and tokens on its
+// columns: a workgroup tile is 64 features x 64 tokens, four waves of 32 x 32
+// (2 x 2 blocks of 16 x 16), 16 reduction indices per LDS stage. For
+// v_mfma_f32_16x16x4_f32 lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]
+// and receives D[4 (l / 16) + r][l % 16], r = 0..3: four consecutive features
+// of one token.
 #include "common.h"
 #include "launch.h"
 
 namespace tsp {
 
-constexpr int FT = 32;   // tile edge (tokens, features, reduction)
+constexpr int F32_MT = 64;   // features per workgroup tile
+constexpr int F32_NT = 64;   // tokens per workgroup tile
+constexpr int F32_KT = 16;   // reduction indices per stage
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// One stage of a k-major weight tile ws[k][feature] (k < F32_KT, feature <
+// F32_MT) from a row-major matrix w (rows = reduction index, ld columns),
+// zero outside [k_lim) x [f_lim).
+__device__ __forceinline__ void load_w_tile(float (*ws)[F32_MT + 4], const float* __restrict__ w, int64_t ld,
+                                            int k0, int k_lim, int c0, int f_lim) {
+    for (int i = threadIdx.x; i < F32_KT * F32_MT; i += 256) {
+        const int r = i / F32_MT, c = i % F32_MT;
+        const int k = k0 + r, fc = c0 + c;
+        ws[r][c] = (k < k_lim && fc < f_lim) ? w[(int64_t)k * ld + fc] : 0.f;
+    }
+}
+
+// One stage of a token tile xs[token][k] from a row-major activation matrix
+// (rows = tokens, ld columns, the stage's reduction indices at col0 + k0..).
+__device__ __forceinline__ void load_x_tile(float (*xs)[F32_KT + 1], const float* __restrict__ x, int64_t ld,
+                                            int64_t col0, int t0, int T, int k0, int k_lim) {
+    for (int i = threadIdx.x; i < F32_NT * F32_KT; i += 256) {
+        const int r = i / F32_KT, c = i % F32_KT;
+        const int tok = t0 + r, k = k0 + c;
+        xs[r][c] = (tok < T && k < k_lim) ? x[(int64_t)tok * ld + col0 + k] : 0.f;
+    }
+}
 
 template <int ACT>
 __global__ __launch_bounds__(256) void gateup_f32(F32Args a) {
-    __shared__ float xs[FT][FT + 1];
-    __shared__ float gs[FT][FT + 1];
-    __shared__ float us[FT][FT + 1];
+    constexpr int NM = ACT == 1 ? 2 : 1;                 // weight matrices: gate and up, or A
+    __shared__ float xs[F32_NT][F32_KT + 1];
+    __shared__ float ws[NM][F32_KT][F32_MT + 4];
     poison_lds(xs, sizeof(xs));
-    poison_lds(gs, sizeof(gs));
-    poison_lds(us, sizeof(us));
+    poison_lds(ws, sizeof(ws));
     const int s = blockIdx.z;                            // ring step = packed record
-    const int c0 = blockIdx.x * FT;                      // local hidden column
-    const int t0 = blockIdx.y * FT;
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    const int c0 = blockIdx.x * F32_MT;                  // first local hidden column
+    const int t0 = blockIdx.y * F32_NT;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w >> 1, wn = w & 1;
     const int64_t dF = (int64_t)a.d * a.F;
     const float* rec = a.packed + (int64_t)s * a.shard_elems;
-    const float* wg = rec;                               // gate (SwiGLU only)
-    const float* wu = (ACT == 1) ? rec + dF : rec;       // up, or A
-    float g[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, u[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-    for (int k0 = 0; k0 < a.d; k0 += FT) {
-        for (int i = threadIdx.x; i < FT * FT; i += 256) {
-            const int r = i / FT, c = i % FT;
-            const int tok = t0 + r, k = k0 + c;
-            xs[r][c] = (tok < a.T && k < a.d) ? a.x[(int64_t)tok * a.d + k] : 0.f;
-            const int kr = k0 + r, hc = c0 + c;
-            const bool ok = kr < a.d && hc < a.F;
-            us[r][c] = ok ? wu[(int64_t)kr * a.F + hc] : 0.f;
-            if (ACT == 1) gs[r][c] = ok ? wg[(int64_t)kr * a.F + hc] : 0.f;
+    f32x4 acc[NM][2][2];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < a.d; k0 += F32_KT) {
+        load_x_tile(xs, a.x, a.d, 0, t0, a.T, k0, a.d);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) load_w_tile(ws[m], rec + m * dF, a.F, k0, a.d, c0, a.F);
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < F32_KT / 4; ++ks) {
+            const int kk = ks * 4 + (lane >> 4);
+            float bx[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bx[j] = xs[wn * 32 + j * 16 + (lane & 15)][kk];
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const float aw = ws[m][kk][wm * 32 + i * 16 + (lane & 15)];
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) acc[m][i][j] = mfma_f32(aw, bx[j], acc[m][i][j]);
+                }
         }
         __syncthreads();
-        for (int k = 0; k < FT; ++k) {
+    }
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const float xv = xs[ty * 2 + i][k];
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    u[i][j] = fmaf(xv, us[k][tx * 2 + j], u[i][j]);
-                    if (ACT == 1) g[i][j] = fmaf(xv, gs[k][tx * 2 + j], g[i][j]);
+        for (int j = 0; j < 2; ++j) {
+            const int tok = t0 + wn * 32 + j * 16 + (lane & 15);
+            if (tok >= a.T) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int hc = c0 + wm * 32 + i * 16 + 4 * (lane >> 4) + r;
+                if (hc < a.F) {
+                    const float h = (ACT == 1) ? silu_f(acc[0][i][j][r]) * acc[NM - 1][i][j][r]
+                                               : gelu_tanh_f(acc[0][i][j][r]);
+                    a.h[(int64_t)tok * a.f + (int64_t)s * a.F + hc] = h;
                 }
             }
         }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int tok = t0 + ty * 2 + i;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int hc = c0 + tx * 2 + j;
-            if (tok < a.T && hc < a.F) {
-                const float h = (ACT == 1) ? silu_f(g[i][j]) * u[i][j] : gelu_tanh_f(u[i][j]);
-                a.h[(int64_t)tok * a.f + (int64_t)s * a.F + hc] = h;
-            }
-        }
-    }
 }
 
 __global__ __launch_bounds__(256) void down_f32(F32Args a) {
-    __shared__ float hs[FT][FT + 1];
-    __shared__ float ds[FT][FT + 1];
+    __shared__ float hs[F32_NT][F32_KT + 1];
+    __shared__ float ds[F32_KT][F32_MT + 4];
     poison_lds(hs, sizeof(hs));
     poison_lds(ds, sizeof(ds));
-    const int n0 = blockIdx.x * FT;
-    const int t0 = blockIdx.y * FT;
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    const int64_t dF = (int64_t)a.d * a.F;
-    const int64_t down_off = (a.swiglu ? 2 : 1) * dF;
-    float y[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-    for (int step = 0; step < a.P; ++step) {
-        const int s = step;                              // records in ring order
-        const float* wd = a.packed + (int64_t)s * a.shard_elems + down_off;   // F x d
-        for (int k0 = 0; k0 < a.F; k0 += FT) {
-            for (int i = threadIdx.x; i < FT * FT; i += 256) {
-                const int r = i / FT, c = i % FT;
-                const int tok = t0 + r, k = k0 + c;
-                hs[r][c] = (tok < a.T && k < a.F) ? a.h[(int64_t)tok * a.f + (int64_t)s * a.F + k] : 0.f;
-                const int kr = k0 + r, n = n0 + c;
-                ds[r][c] = (kr < a.F && n < a.d) ? wd[(int64_t)kr * a.d + n] : 0.f;
-            }
+    const int n0 = blockIdx.x * F32_MT;                  // first output feature
+    const int t0 = blockIdx.y * F32_NT;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int64_t down_off = (a.swiglu ? 2 : 1) * (int64_t)a.d * a.F;
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int step = 0; step < a.P; ++step) {             // records and H columns in ring order
+        const float* wd = a.packed + (int64_t)step * a.shard_elems + down_off;   // F x d
+        for (int k0 = 0; k0 < a.F; k0 += F32_KT) {
+            load_x_tile(hs, a.h, a.f, (int64_t)step * a.F, t0, a.T, k0, a.F);
+            load_w_tile(ds, wd, a.d, k0, a.F, n0, a.d);
             __syncthreads();
-            for (int k = 0; k < FT; ++k) {
+#pragma unroll
+            for (int ks = 0; ks < F32_KT / 4; ++ks) {
+                const int kk = ks * 4 + (lane >> 4);
+                float bh[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) bh[j] = hs[wn * 32 + j * 16 + (lane & 15)][kk];
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    const float hv = hs[ty * 2 + i][k];
+                    const float aw = ds[kk][wm * 32 + i * 16 + (lane & 15)];
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) y[i][j] = fmaf(hv, ds[k][tx * 2 + j], y[i][j]);
+                    for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f32(aw, bh[j], acc[i][j]);
                 }
             }
             __syncthreads();
         }
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int tok = t0 + ty * 2 + i;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int n = n0 + tx * 2 + j;
-            if (tok < a.T && n < a.d) a.y[(int64_t)tok * a.d + n] = y[i][j];
+            const int tok = t0 + wn * 32 + j * 16 + (lane & 15);
+            if (tok >= a.T) continue;
+            const int n = n0 + wm * 32 + i * 16 + 4 * (lane >> 4);
+            float* yrow = a.y + (int64_t)tok * a.d;
+            if (n + 3 < a.d && (a.d & 3) == 0) {
+                *reinterpret_cast<f32x4*>(yrow + n) = acc[i][j];
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < a.d) yrow[n + r] = acc[i][j][r];
+            }
         }
-    }
 }
 
 hipError_t launch_gateup_f32(const F32Args& a, hipStream_t st) {
-    const dim3 grid((unsigned)((a.F + FT - 1) / FT), (unsigned)((a.T + FT - 1) / FT), (unsigned)a.P);
+    const dim3 grid((unsigned)((a.F + F32_MT - 1) / F32_MT), (unsigned)((a.T + F32_NT - 1) / F32_NT), (unsigned)a.P);
     if (a.swiglu)
         hipLaunchKernelGGL(gateup_f32<1>, grid, dim3(256), 0, st, a);
     else
@@ -124,7 +180,7 @@ hipError_t launch_gateup_f32(const F32Args& a, hipStream_t st) {
 }
 
 hipError_t launch_down_f32(const F32Args& a, hipStream_t st) {
-    const dim3 grid((unsigned)((a.d + FT - 1) / FT), (unsigned)((a.T + FT - 1) / FT));
+    const dim3 grid((unsigned)((a.d + F32_MT - 1) / F32_MT), (unsigned)((a.T + F32_NT - 1) / F32_NT));
     hipLaunchKernelGGL(down_f32, grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }

@@ -18,18 +18,16 @@
 //   whole walk, so Y is written once ("Folding Tensor and Sequence
 //   Parallelism ...", Abstract: partial outputs accumulate locally).
 //
-// Main loop: 32 reduction indices per stage. Global memory is loaded into
-// registers two stages ahead and written to a 3-deep LDS ring laid out in
-// fragment blocks, so every operand fragment read is one contiguous (or
-// XOR-swizzled) 16-byte-per-lane access without bank conflicts. The waves
-// run a two-group ping-pong (see mainloop): on every SIMD one wave issues
-// MFMAs while the other moves data. Shapes 0-4 use this register-staged
-// loop with 32x32x16 MFMAs; shape 5 (namespace pp16) keeps the ping-pong but
-// loads global memory straight into LDS and uses 16x16x32 MFMAs; shape 6
-// (namespace w16, the automatic choice at large T) loads like shape 5 but
-// runs one wave per SIMD holding a 128 x 128 piece in all 256 accumulation
-// registers. The choice between them is empirical: shape 6 measured fastest
-// on every large-T workload, shape 5 next.
+// Shapes 1-3 (smaller tiles, for token counts and shard widths that 256 x 256
+// tiles would leave with too few workgroups): 32 reduction indices per
+// stage, global memory loaded into registers two stages ahead and written to
+// a 3-deep LDS ring laid out in fragment blocks, so every operand fragment
+// read is one contiguous (or XOR-swizzled) 16-byte-per-lane access without
+// bank conflicts; the waves run a two-group ping-pong (see mainloop): on every
+// SIMD one wave issues MFMAs while the other moves data. Shape 0 (w16.h, the
+// automatic choice at large T) loads global memory straight into LDS, uses
+// 16x16x32 MFMAs and runs one wave per SIMD holding a 128 x 128 piece in all
+// 256 accumulation registers; it measured fastest on every large-T workload.
 #include "common.h"
 #include "launch.h"
 #include "w16.h"
@@ -266,171 +264,11 @@ __device__ __forceinline__ void mainloop(uint16_t* lds, f32x16 (&acc)[C::TM][C::
     if (!g1) stage_barrier();                           // b_{2K}: group 0 matches group 1's count
 }
 
-// ---- one wave per SIMD: 4 waves, each a 128 x 128 sub-tile ----------------
-//
-// Single instruction stream per SIMD: the wave keeps 256 fp32 accumulators
-// (16 blocks of 32 x 32, in AGPRs) and interleaves everything else with its
-// MFMAs. Per step t (32 reduction indices, two 16-wide halves):
-//   barrier                       stage t + 1 visible, stage t - 1 free
-//   MFMAs of stage t, half 0      (fragments read during step t - 1)
-//     + read half 1 of stage t, write the registers holding stage t + 2 to
-//       LDS buffer (t + 2) % 3, load stage t + 4 into those registers
-//   MFMAs of stage t, half 1
-//     + read half 0 of stage t + 1
-//   drain LDS traffic (lgkmcnt 0)
-// Global data is loaded two steps before it is written to LDS; two register
-// sets alternate, so the loop is unrolled by two (K is even).
-template <class C>
-struct StageRegs8 {
-    static constexpr int N = (C::A_BLK + C::B_BLK) / C::NW;   // 16-byte pieces per thread
-    u32x4 v[N];
-};
-
-template <class C>
-__device__ __forceinline__ void load_stage8(StageRegs8<C>& r, const uint16_t* __restrict__ a_base, int64_t a_rs,
-                                            const uint16_t* __restrict__ b_src, int ldb, int64_t b_koff,
-                                            int t0, int T, int w, int lane) {
-#pragma unroll
-    for (int i = 0; i < StageRegs8<C>::N; ++i) {
-        const int b = i * C::NW + w;
-        if (b < C::A_BLK) {
-            r.v[i] = *reinterpret_cast<const u32x4*>(a_base + (b >> 1) * a_rs + (b & 1) * 512 + lane * 8);
-        } else {
-            const int bb = b - C::A_BLK;
-            const int tok = min(t0 + bb * 16 + (lane >> 2), T - 1);
-            r.v[i] = *reinterpret_cast<const u32x4*>(b_src + (int64_t)tok * ldb + b_koff + (lane & 3) * 8);
-        }
-    }
-}
-
-template <class C>
-__device__ __forceinline__ void store_stage8(uint16_t* lds_stage, const StageRegs8<C>& r, int w, int lane) {
-    u32x4* as = reinterpret_cast<u32x4*>(lds_stage);
-    u32x4* bs = reinterpret_cast<u32x4*>(lds_stage + C::A_BLK * 512);
-    const int slot = tok_slot(lane >> 2, lane & 3);
-#pragma unroll
-    for (int i = 0; i < StageRegs8<C>::N; ++i) {
-        const int b = i * C::NW + w;
-        if (b < C::A_BLK) as[b * 64 + lane] = r.v[i];
-        else bs[(b - C::A_BLK) * 64 + slot] = r.v[i];
-    }
-}
-
-template <class C>
-__device__ __forceinline__ void read_half(const uint16_t* lds_stage, int kk, bf16x8 (&af)[C::TM],
-                                          bf16x8 (&bv)[C::TN], int wm, int wn, int lane) {
-    const bf16x8* as = reinterpret_cast<const bf16x8*>(lds_stage);
-    const bf16x8* bs = reinterpret_cast<const bf16x8*>(lds_stage + C::A_BLK * 512);
-    const int r = lane & 15, half = (lane >> 4) & 1, hi = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) af[i] = as[((wm * C::TM + i) * 2 + kk) * 64 + lane];
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) bv[j] = bs[((wn * C::TN + j) * 2 + half) * 64 + tok_slot(r, 2 * kk + hi)];
-}
-
-template <class C>
-__device__ __forceinline__ void mfma_half(f32x16 (&acc)[C::TM][C::TN], const bf16x8 (&af)[C::TM],
-                                          const bf16x8 (&bv)[C::TN]) {
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bv[j], acc[i][j], 0, 0, 0);
-}
-
-template <class C, class Src>
-__device__ __forceinline__ void w4_step(int t, int K, uint16_t* lds, StageRegs8<C>& rr,
-                                        f32x16 (&acc)[C::TM][C::TN], bf16x8 (&a0)[C::TM], bf16x8 (&b0)[C::TN],
-                                        bf16x8 (&a1)[C::TM], bf16x8 (&b1)[C::TN], int64_t a_rs,
-                                        const uint16_t* b_src, int ldb, int t0, int T, int w, int wm, int wn,
-                                        int lane, Src& src) {
-    constexpr int NLD = StageRegs8<C>::N;
-    stage_barrier();
-    // half 0 of stage t (in a0, b0) while reading half 1 and moving stage t + 2
-    read_half<C>(lds + (t % C::NS) * C::STAGE, 1, a1, b1, wm, wn, lane);
-    vmcnt_le(NLD);                                      // stage t + 2 landed in rr
-    store_stage8<C>(lds + ((t + 2) % C::NS) * C::STAGE, rr, w, lane);
-    {
-        const uint16_t* ab;
-        int64_t bk;
-        src(min(t + 4, K - 1), ab, bk);                 // past the end: refetch, never read
-        load_stage8<C>(rr, ab, a_rs, b_src, ldb, bk, t0, T, w, lane);
-    }
-    mfma_half<C>(acc, a0, b0);
-#pragma unroll
-    for (int r = 0; r < C::TM + C::TN; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-    }
-#pragma unroll
-    for (int r = 0; r < NLD; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-    }
-    // half 1 of stage t while reading half 0 of stage t + 1 (visible since
-    // the barrier: it was written during step t - 1)
-    read_half<C>(lds + ((t + 1) % C::NS) * C::STAGE, 0, a0, b0, wm, wn, lane);
-    mfma_half<C>(acc, a1, b1);
-#pragma unroll
-    for (int r = 0; r < C::TM + C::TN; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
-    lgkm_zero();
-}
-
-template <class C, class Src>
-__device__ __forceinline__ void mainloop_4w(uint16_t* lds, f32x16 (&acc)[C::TM][C::TN], int K,
-                                            int64_t a_rs, const uint16_t* b_src, int ldb, int t0, int T,
-                                            Src src) {
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = w / C::WN, wn = w % C::WN;
-    constexpr int NLD = StageRegs8<C>::N;
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-    StageRegs8<C> r0, r1;
-    const uint16_t* ab;
-    int64_t bk;
-    src(0, ab, bk);
-    load_stage8<C>(r0, ab, a_rs, b_src, ldb, bk, t0, T, w, lane);
-    src(min(1, K - 1), ab, bk);
-    load_stage8<C>(r1, ab, a_rs, b_src, ldb, bk, t0, T, w, lane);
-    vmcnt_le(NLD);
-    store_stage8<C>(lds, r0, w, lane);
-    vmcnt_le(0);
-    store_stage8<C>(lds + C::STAGE, r1, w, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    src(min(2, K - 1), ab, bk);
-    load_stage8<C>(r0, ab, a_rs, b_src, ldb, bk, t0, T, w, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    src(min(3, K - 1), ab, bk);
-    load_stage8<C>(r1, ab, a_rs, b_src, ldb, bk, t0, T, w, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    lgkm_zero();
-    stage_barrier();
-    bf16x8 a0[C::TM], b0[C::TN], a1[C::TM], b1[C::TN];
-    read_half<C>(lds, 0, a0, b0, wm, wn, lane);
-    lgkm_zero();
-    for (int t = 0; t < K; t += 2) {                    // K is even
-        w4_step<C>(t, K, lds, r0, acc, a0, b0, a1, b1, a_rs, b_src, ldb, t0, T, w, wm, wn, lane, src);
-        w4_step<C>(t + 1, K, lds, r1, acc, a0, b0, a1, b1, a_rs, b_src, ldb, t0, T, w, wm, wn, lane, src);
-    }
-}
-
 template <class C, class Src>
 __device__ __forceinline__ void run_mainloop(uint16_t* lds, f32x16 (&acc)[C::TM][C::TN], int K,
                                              int64_t a_rs, const uint16_t* b_src, int ldb, int t0, int T,
                                              Src src) {
-    if constexpr (C::NW == 4 && C::TM == 4 && C::TN == 4)
-        mainloop_4w<C>(lds, acc, K, a_rs, b_src, ldb, t0, T, src);
-    else
-        mainloop<C>(lds, acc, K, a_rs, b_src, ldb, t0, T, src);
+    mainloop<C>(lds, acc, K, a_rs, b_src, ldb, t0, T, src);
 }
 
 // act: 1 = SwiGLU (packed 32-row blocks alternate gate / up), 2 = GeLU (tanh form)
@@ -543,261 +381,20 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
     }
 }
 
-// ---- 16x16x32 ping-pong over global-to-LDS loads --------------------------
-//
-// Same packed layout, tile 256 features x 256 tokens, 8 waves as 4 x 2 (wave
-// tile 64 x 128 as 4 x 8 MFMA blocks of 16 x 16). Global data goes straight
-// into a 5-deep LDS ring (4 stages in flight) with buffer_load ... lds or
-// global_load_lds (no staging registers), and the waves run the two-group
-// ping-pong with 16x16x32 MFMAs. A 16x16x32 A fragment (16 rows x 32
-// indices) is gathered from two 32 x 16 blocks; a 16x16x32 B fragment is
-// exactly one 16-token LDS block.
-namespace pp16 {
-
-constexpr int BM = 256, BN = 256, NW = 8, WN = 2;
-constexpr int TM = 4, TN = 8;                           // 16-row / 16-token MFMA blocks per wave
-constexpr int A_BLK = BM / 16, B_BLK = BN / 16;         // 1 KiB blocks per 32-wide stage
-constexpr int LOADS = (A_BLK + B_BLK) / NW;
-constexpr int STAGE = (A_BLK + B_BLK) * 512;
-constexpr int NS = 5;                                   // LDS ring depth: 5 x 32 KiB = all 160 KiB
-// B blocks use the conflict-free slot swizzle b_slot (w16.h).
-
-// One stage's global-to-LDS loads for this wave. BUF selects buffer loads
-// (buffer_load_dwordx4 ... lds: 128-bit resource + 32-bit per-lane offset)
-// instead of global_load_lds with 64-bit per-lane addresses; the caller
-// guarantees every offset stays below 2^31 bytes from the slab's start.
-template <bool BUF>
-__device__ __forceinline__ void issue(uint16_t* lds_stage, const uint16_t* __restrict__ a_base, int64_t a_rs,
-                                      const uint16_t* __restrict__ b_src, int ldb, int64_t b_koff, int t0,
-                                      int T, int w, int lane) {
-    const int r = lane >> 2;                            // token inside a B block
-    const int c = (lane & 3) ^ ((r >> 1) & 3);          // chunk this lane fetches (slot = lane = b_slot(r, c))
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-        const int b = i * NW + w;                       // wave-uniform block id
-        TSP_LDS void* dst = (TSP_LDS void*)(lds_stage + b * 512);
-        if (b < A_BLK) {
-            const int64_t off = (b >> 1) * a_rs + (b & 1) * 512 + lane * 8;
-            if constexpr (BUF) {
-                const __amdgpu_buffer_rsrc_t rs =
-                    __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, 0x7fffffff, kRawBufferWord3);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (int)(off * 2), 0, 0, 0);
-            } else {
-                __builtin_amdgcn_global_load_lds(a_base + off, dst, 16, 0, 0);
-            }
-        } else {
-            const int tok = min(t0 + (b - A_BLK) * 16 + r, T - 1);
-            const int64_t off = (int64_t)tok * ldb + c * 8;
-            if constexpr (BUF) {
-                const __amdgpu_buffer_rsrc_t rs =
-                    __builtin_amdgcn_make_buffer_rsrc((void*)(b_src + b_koff), (short)0, 0x7fffffff, kRawBufferWord3);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (int)(off * 2), 0, 0, 0);
-            } else {
-                __builtin_amdgcn_global_load_lds(b_src + b_koff + off, dst, 16, 0, 0);
-            }
-        }
-    }
-}
-
-__device__ __forceinline__ void wait_stages(int newer) {
-#define TSP_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-    if (newer >= 3) TSP_VMCNT(3 * LOADS);
-    else if (newer == 2) TSP_VMCNT(2 * LOADS);
-    else if (newer == 1) TSP_VMCNT(LOADS);
-    else TSP_VMCNT(0);
-#undef TSP_VMCNT
-}
-
-__device__ __forceinline__ void read_frags(const uint16_t* lds_stage, bf16x8 (&af)[TM], bf16x8 (&bv)[TN],
-                                           int wm, int wn, int lane) {
-    const bf16x8* as = reinterpret_cast<const bf16x8*>(lds_stage);
-    const bf16x8* bs = reinterpret_cast<const bf16x8*>(lds_stage + A_BLK * 512);
-    const int r = lane & 15, c = lane >> 4;             // row / token, 8-index chunk (0..3)
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int ib = wm * TM + i;                     // 16-row block in the tile
-        // rows 16 (ib % 2) + r of 32-row block ib / 2, reduction block c / 2
-        af[i] = as[((ib >> 1) * 2 + (c >> 1)) * 64 + (c & 1) * 32 + (ib & 1) * 16 + r];
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) bv[j] = bs[(wn * TN + j) * 64 + b_slot(r, c)];
-}
-
-// Ping-pong over stages t = 0 .. ksteps-1. Waves 0-3 (group 0) and 4-7
-// (group 1), one of each per SIMD, alternate a memory phase M(t) (issue the
-// loads of stage t + 4 into the buffer stage t - 1 used, read stage t's
-// fragments, wait for them) and a compute phase C(t) (the 32 MFMAs). Group 1
-// runs one phase behind, and every phase boundary is a workgroup barrier, so
-// on each SIMD one wave computes while the other moves data. Each wave waits
-// for its own loads of stage t + 1 before the barrier that precedes M(t + 1)
-// (group 1 at the end of M(t), group 0 after C(t)); the barrier then makes
-// every wave's share visible. Stage t - 1's buffer was last read in M(t - 1)
-// of both groups, which ended before M(t) of group 0 starts.
-template <bool BUF>
-__device__ __forceinline__ void mainloop(uint16_t* lds, f32x4 (&acc)[TM][TN], int ksteps, int64_t a_rs,
-                                         const uint16_t* b_src, int ldb, int t0, int T,
-                                         const uint16_t* a_tile, int64_t a_rec, int spp) {
-    // a_rec / spp: when spp > 0 the reduction walks shard records (down
-    // product): step t is local step t % spp of record t / spp.
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = w / WN, wn = w % WN;
-    const bool g1 = w >= NW / 2;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto src = [&](int t) {
-        if (spp > 0) {
-            const int k = t / spp, ls = t - k * spp;
-            return a_tile + (int64_t)k * a_rec + (int64_t)ls * 1024;
-        }
-        return a_tile + (int64_t)t * 1024;
-    };
-    constexpr int AHEAD = NS - 1;
-    const int pro = min(AHEAD, ksteps);
-    for (int t = 0; t < pro; ++t)
-        issue<BUF>(lds + (t % NS) * STAGE, src(t), a_rs, b_src, ldb, (int64_t)t * 32, t0, T, w, lane);
-    wait_stages(pro - 1);
-    if (g1) stage_barrier();
-    bf16x8 af[TM], bv[TN];
-    for (int t = 0; t < ksteps; ++t) {
-        stage_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        if (t + AHEAD < ksteps)
-            issue<BUF>(lds + ((t + AHEAD) % NS) * STAGE, src(t + AHEAD), a_rs, b_src, ldb,
-                  (int64_t)(t + AHEAD) * 32, t0, T, w, lane);
-        read_frags(lds + (t % NS) * STAGE, af, bv, wm, wn, lane);
-        lgkm_zero();
-        const int newer = min(t + AHEAD, ksteps - 1) - (t + 1);
-        if (g1) wait_stages(newer);
-        __builtin_amdgcn_sched_barrier(0);
-        stage_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        // (no s_setprio here: raising the MFMA wave's priority measured ~1 % slower)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bv[j], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (!g1) wait_stages(newer);
-    }
-    if (!g1) stage_barrier();
-}
-
-}  // namespace pp16
-
-// 16x16 result layout: lane l holds token l % 16 and features 4 (l / 16) + r.
-// BUF: buffer loads (measured faster for the gate/up kernel; the down kernel
-// keeps global_load_lds, which measured faster there)
-template <int ACT, bool BUF>
-__global__ __launch_bounds__(512) void gateup_pp16(Bf16Args a, int n_ft_shard, int n_tt) {
-    using namespace pp16;
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
-    poison_lds(lds, sizeof(lds));
-    int ttile, flin;
-    raster(xcd_remap(blockIdx.x, gridDim.x), a.P * n_ft_shard, n_tt, ttile, flin);
-    const int s = flin / n_ft_shard;
-    const int ftile = flin - s * n_ft_shard;
-    const int64_t a_rs = (int64_t)(a.d >> 4) * 512;
-    const uint16_t* a_tile = a.packed + (int64_t)s * a.shard_elems + (int64_t)(ftile * (BM / 32)) * a_rs;
-    const int t0 = ttile * BN;
-    f32x4 acc[TM][TN];
-    pp16::mainloop<BUF>(lds, acc, a.d >> 5, a_rs, a.x, a.d, t0, a.T, a_tile, 0, 0);
-
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int wm = w / WN, wn = w % WN;
-    const int fsub = 4 * (lane >> 4);
-    if constexpr (ACT == 1) {
-        // wave rows: 16-row blocks 0, 1 are gate rows of 32-row block 2 wm,
-        // blocks 2, 3 the matching up rows
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int hcol = s * a.F + (ftile * (BM / 64) + wm) * 32 + i * 16 + fsub;
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int tok = t0 + (wn * TN + j) * 16 + (lane & 15);
-                if (tok < a.T) {
-                    const f32x4 g = acc[i][j], u = acc[i + 2][j];
-                    *reinterpret_cast<uint2*>(a.h + (int64_t)tok * a.f + hcol) =
-                        pack4_bf16(silu_f(g[0]) * u[0], silu_f(g[1]) * u[1], silu_f(g[2]) * u[2],
-                                   silu_f(g[3]) * u[3]);
-                }
-            }
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int hcol = s * a.F + ftile * BM + (wm * TM + i) * 16 + fsub;
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int tok = t0 + (wn * TN + j) * 16 + (lane & 15);
-                if (tok < a.T) {
-                    const f32x4 u = acc[i][j];
-                    *reinterpret_cast<uint2*>(a.h + (int64_t)tok * a.f + hcol) =
-                        pack4_bf16(gelu_tanh_f(u[0]), gelu_tanh_f(u[1]), gelu_tanh_f(u[2]), gelu_tanh_f(u[3]));
-                }
-            }
-        }
-    }
-}
-
-// split > 1: workgroup group g (of `split`) sums ring steps
-// [g * P / split, (g + 1) * P / split) into its own fp32 partial; records and
-// H columns are in ring order, so a group is a contiguous range of both.
-__global__ __launch_bounds__(512) void down_pp16(Bf16Args a, int n_ft, int n_tt, int split) {
-    using namespace pp16;
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
-    poison_lds(lds, sizeof(lds));
-    const int n_tiles = n_ft * n_tt;
-    const int lin = xcd_remap(blockIdx.x, gridDim.x);
-    const int g = lin / n_tiles;                        // ring-step group
-    int ttile, ftile;
-    raster(lin - g * n_tiles, n_ft, n_tt, ttile, ftile);
-    const int spp = a.F >> 5;
-    const int steps_per_group = a.P / split;
-    const int64_t a_rs = (int64_t)(a.F >> 4) * 512;
-    const uint16_t* a_ft = a.packed + a.down_off + (int64_t)(g * steps_per_group) * a.shard_elems +
-                           (int64_t)(ftile * (BM / 32)) * a_rs;
-    const uint16_t* h_g = a.h + (int64_t)(g * steps_per_group) * a.F;
-    float* y = split > 1 ? a.part + (int64_t)g * a.T * a.d : a.y;
-    const int t0 = ttile * BN;
-    f32x4 acc[TM][TN];
-    pp16::mainloop<false>(lds, acc, steps_per_group * spp, a_rs, h_g, a.f, t0, a.T, a_ft, a.shard_elems, spp);
-
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int wm = w / WN, wn = w % WN;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int n = ftile * BM + (wm * TM + i) * 16 + 4 * (lane >> 4);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int tok = t0 + (wn * TN + j) * 16 + (lane & 15);
-            if (tok < a.T) {
-                const f32x4 v = acc[i][j];
-                *reinterpret_cast<float4*>(y + (int64_t)tok * a.d + n) = make_float4(v[0], v[1], v[2], v[3]);
-            }
-        }
-    }
-}
-
-// ------------------------------------------------------------------ shape 6
-// The pipeline of w16.h with the forward's operands (PackedSrc).
-//
-// Measured (Llama-3-8B shape, same box): gate/up ~4 % and down ~8 % faster
-// than shape 5, so shape 6 is the automatic choice for both. Taking the
-// global-to-LDS loads out (a timing copy, not kept) makes either kernel ~25 %
-// faster: issuing them, not LDS reads or barriers, is what keeps the matrix
-// pipe below full rate, and how far apart they are issued matters (see
-// w16::step). Staging one or both operands through registers, and a
-// persistent grid that streams the next tile's first stages during the
-// epilogue, each measured slower.
+// ------------------------------------------------------------------ shape 0
+// The pipeline of w16.h with the forward's operands (PackedSrc): the gate/up
+// product on the split ring (whole 128-byte token rows per load), the down
+// product on the 5-stage ring (measured on one box, Llama shape: gate/up
+// 683 -> 667 us and 70B long 11.56 -> 10.79 ms on the split ring; the down
+// product 4-5 % slower there than on the 5-stage ring). Both measured faster
+// than every variant of the ping-pong shapes, of staging operands through
+// registers, and of a persistent grid that streams the next tile's first
+// stages during the epilogue.
 
 template <int ACT, bool BUF>
 __global__ __launch_bounds__(256) void gateup_w16(Bf16Args a, int n_ft_shard, int n_tt) {
     using namespace w16;
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
     poison_lds(lds, sizeof(lds));
     int ttile, flin;
     raster(xcd_remap(blockIdx.x, gridDim.x), a.P * n_ft_shard, n_tt, ttile, flin);
@@ -858,7 +455,7 @@ __global__ __launch_bounds__(256) void gateup_w16(Bf16Args a, int n_ft_shard, in
 
 __global__ __launch_bounds__(256) void down_w16(Bf16Args a, int n_ft, int n_tt, int split) {
     using namespace w16;
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[NS * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
     poison_lds(lds, sizeof(lds));
     const int n_tiles = n_ft * n_tt;
     const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -878,7 +475,7 @@ __global__ __launch_bounds__(256) void down_w16(Bf16Args a, int n_ft, int n_tt, 
     PackedSrc<false> src{a_ft, 0, 0, steps_per_group * spp, spp, a.shard_elems, a_rs, h_g, a.f, t0, a.T,
                          __builtin_amdgcn_readfirstlane(w), wm, wn, lane};
     f32x4 acc[TM][TN];
-    w16::mainloop(lds, acc, steps_per_group * spp, src);
+    w16::mainloop5(lds, acc, steps_per_group * spp, src);
 
     // Y rows through the LDS ring, half of each wave row's tokens at a time,
     // so that each store writes a whole 1 KiB row (from the MFMA layout a
@@ -914,16 +511,16 @@ __global__ __launch_bounds__(256) void reduce_partials(const float4* __restrict_
 }
 
 // ------------------------------------------------------------------ configs
-// cfg: 0 = 256 x 256 (8 waves as 4 x 2), 1 = 256 x 128 (8 waves),
-//      2 = 128 x 128 (4 waves as 2 x 2), 3 = 64 x 128 (4 waves as 1 x 4),
-//      4 = 256 x 256 with 4 waves (one per SIMD), 5 = 256 x 256 16x16x32
-//      ping-pong over global-to-LDS loads, 6 = 256 x 256 16x16x32 with 4
-//      waves of 128 x 128 over global-to-LDS loads
+// cfg: 0 = 256 x 256, 16x16x32 MFMAs, 4 waves of 128 x 128 over global-to-LDS
+//      loads (w16.h; the choice at large T), 1 = 256 x 128 (8 waves as 4 x 2,
+//      32x32x16, register-staged ping-pong), 2 = 128 x 128 (4 waves as 2 x 2),
+//      3 = 64 x 128 (4 waves as 1 x 4): the smaller tiles serve token counts
+//      and shard widths that 256 x 256 tiles would leave with too few
+//      workgroups, and shard widths that are not multiples of 256.
 struct CfgDesc { int bm, bn; const char* name; };
-constexpr int kNumCfgs = 7;
+constexpr int kNumCfgs = 4;
 static const CfgDesc kCfgs[kNumCfgs] = {
-    {256, 256, "256x256"}, {256, 128, "256x128"}, {128, 128, "128x128"}, {64, 128, "64x128"},
-    {256, 256, "256x256 4-wave"}, {256, 256, "256x256 16x16 ping-pong"}, {256, 256, "256x256 16x16 4-wave"}};
+    {256, 256, "256x256 16x16 4-wave"}, {256, 128, "256x128"}, {128, 128, "128x128"}, {64, 128, "64x128"}};
 
 const char* tiled_cfg_name(int cfg) { return (cfg >= 0 && cfg < kNumCfgs) ? kCfgs[cfg].name : "none"; }
 
@@ -941,9 +538,8 @@ bool down_cfg_fits(int cfg, int d, int F) {
 
 // Automatic choice: the first shape in the list that divides the shard's
 // packed width (gate/up) or d (down) and still gives at least one full wave
-// of workgroups on 256 CUs; otherwise the first one that divides. Shapes 0,
-// 4 and 5 stay reachable through tsp_mlp_set_tiles.
-static const int kAuto[4] = {6, 1, 2, 3};
+// of workgroups on 256 CUs; otherwise the first one that divides.
+static const int kAuto[4] = {0, 1, 2, 3};
 
 int choose_gateup_cfg(int T, int d, int F, int P, int swiglu) {
     const int64_t ngu = swiglu ? 2LL * F : (int64_t)F;
@@ -958,7 +554,7 @@ int choose_gateup_cfg(int T, int d, int F, int P, int swiglu) {
 }
 
 int choose_down_split(int T, int d, int P, int cfg) {
-    if ((cfg != 5 && cfg != 6) || d % 256) return 1;
+    if (cfg != 0 || d % 256) return 1;
     const int64_t tiles = (int64_t)(d / 256) * cdiv(T, 256);
     int best = 1;
     for (int s = 2; s <= P; ++s)                        // the largest divisor of P that keeps one round
@@ -970,7 +566,7 @@ int64_t down_split_bytes(int64_t T_max, int d, int P) {
     int64_t most = 0;
     for (int64_t t = 256; t < T_max + 256; t += 256) {
         const int64_t T = t < T_max ? t : T_max;
-        const int s = choose_down_split((int)T, d, P, 6);     // shapes 5 and 6 split alike
+        const int s = choose_down_split((int)T, d, P, 0);
         if (s > 1 && s * T * d * 4 > most) most = s * T * d * 4;
     }
     return most;
@@ -1011,31 +607,12 @@ static hipError_t down_go(const Bf16Args& a, hipStream_t st) {
 
 hipError_t launch_gateup_tiled(const Bf16Args& a, int cfg, hipStream_t st) {
     switch (cfg) {
-        case 0: return gateup_go<256, 256, 4, 2>(a, st);
-        case 1: return gateup_go<256, 128, 4, 2>(a, st);
-        case 2: return gateup_go<128, 128, 2, 2>(a, st);
-        case 3: return gateup_go<64, 128, 1, 4>(a, st);
-        case 4: return gateup_go<256, 256, 2, 2>(a, st);
-        case 5: {
+        case 0: {
             const int ngu = a.swiglu ? 2 * a.F : a.F;
             const int n_ft_shard = ngu / 256, n_tt = (int)cdiv(a.T, 256);
             const dim3 grid((unsigned)(a.P * n_ft_shard * n_tt));
             // buffer offsets are 32-bit: X (T x d bf16) and one stage's weight
             // slab (8 rows of 32 x d-element blocks) must each span < 2^31 bytes
-            const bool buf = (int64_t)a.T * a.d * 2 < (int64_t(1) << 31) && (int64_t)a.d * 512 < (int64_t(1) << 31);
-            if (a.swiglu) {
-                if (buf) hipLaunchKernelGGL((gateup_pp16<1, true>), grid, dim3(512), 0, st, a, n_ft_shard, n_tt);
-                else hipLaunchKernelGGL((gateup_pp16<1, false>), grid, dim3(512), 0, st, a, n_ft_shard, n_tt);
-            } else {
-                if (buf) hipLaunchKernelGGL((gateup_pp16<2, true>), grid, dim3(512), 0, st, a, n_ft_shard, n_tt);
-                else hipLaunchKernelGGL((gateup_pp16<2, false>), grid, dim3(512), 0, st, a, n_ft_shard, n_tt);
-            }
-            return hipGetLastError();
-        }
-        case 6: {
-            const int ngu = a.swiglu ? 2 * a.F : a.F;
-            const int n_ft_shard = ngu / 256, n_tt = (int)cdiv(a.T, 256);
-            const dim3 grid((unsigned)(a.P * n_ft_shard * n_tt));
             const bool buf = (int64_t)a.T * a.d * 2 < (int64_t(1) << 31) && (int64_t)a.d * 512 < (int64_t(1) << 31);
             if (a.swiglu) {
                 if (buf) hipLaunchKernelGGL((gateup_w16<1, true>), grid, dim3(256), 0, st, a, n_ft_shard, n_tt);
@@ -1046,30 +623,25 @@ hipError_t launch_gateup_tiled(const Bf16Args& a, int cfg, hipStream_t st) {
             }
             return hipGetLastError();
         }
+        case 1: return gateup_go<256, 128, 4, 2>(a, st);
+        case 2: return gateup_go<128, 128, 2, 2>(a, st);
+        case 3: return gateup_go<64, 128, 1, 4>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_down_tiled(const Bf16Args& a, int cfg, int split, hipStream_t st) {
-    if (split > 1 && ((cfg != 5 && cfg != 6) || a.P % split || !a.part)) return hipErrorInvalidValue;
+    if (split > 1 && (cfg != 0 || a.P % split || !a.part)) return hipErrorInvalidValue;
     switch (cfg) {
-        case 0: return down_go<256, 256, 4, 2>(a, st);
-        case 1: return down_go<256, 128, 4, 2>(a, st);
-        case 2: return down_go<128, 128, 2, 2>(a, st);
-        case 3: return down_go<64, 128, 1, 4>(a, st);
-        case 4: return down_go<256, 256, 2, 2>(a, st);
-        case 5: {
-            const int n_ft = a.d / 256, n_tt = (int)cdiv(a.T, 256);
-            hipLaunchKernelGGL(down_pp16, dim3((unsigned)(n_ft * n_tt * split)), dim3(512), 0, st, a, n_ft, n_tt,
-                               split);
-            return hipGetLastError();
-        }
-        case 6: {
+        case 0: {
             const int n_ft = a.d / 256, n_tt = (int)cdiv(a.T, 256);
             hipLaunchKernelGGL(down_w16, dim3((unsigned)(n_ft * n_tt * split)), dim3(256), 0, st, a, n_ft, n_tt,
                                split);
             return hipGetLastError();
         }
+        case 1: return down_go<256, 128, 4, 2>(a, st);
+        case 2: return down_go<128, 128, 2, 2>(a, st);
+        case 3: return down_go<64, 128, 1, 4>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -35,6 +35,11 @@ struct F32Args {
 hipError_t launch_pack_bf16(const void* wg, const void* wu, const void* wd, void* dst,
                             const int32_t* order, int64_t shard_elems, int64_t down_off, int d,
                             int f, int F, int P, int swiglu, hipStream_t st);
+// Inverse of launch_pack_bf16: the records back into row-major wg, wu (d x f)
+// and wd (f x d), bit for bit (wg unused for GeLU).
+hipError_t launch_unpack_bf16(const void* src, void* wg, void* wu, void* wd, const int32_t* order,
+                              int64_t shard_elems, int64_t down_off, int d, int f, int F, int P, int swiglu,
+                              hipStream_t st);
 hipError_t launch_pack_f32(const void* wg, const void* wu, const void* wd, void* dst,
                            const int32_t* order, int64_t shard_elems, int d, int f, int F, int P,
                            int swiglu, hipStream_t st);

@@ -85,6 +85,60 @@ __global__ void pack_down_bf16(const uint16_t* __restrict__ wd, uint16_t* __rest
     }
 }
 
+// The inverse of the two kernels above, for the backward: each 16-byte chunk
+// of a record goes back to the 8 rows of its column it came from.
+__global__ void unpack_gateup_bf16(const uint16_t* __restrict__ src, uint16_t* __restrict__ wg,
+                                   uint16_t* __restrict__ wu, const int32_t* __restrict__ order,
+                                   int64_t shard_elems, int d, int f, int F, int swiglu,
+                                   int64_t chunks_per_shard) {
+    const int rec = blockIdx.y;
+    const int s = order[rec];
+    const int kblocks = d >> 4;
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks_per_shard;
+         c += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t block = c >> 6;
+        const int lane = (int)(c & 63);
+        const int64_t nb = block / kblocks;
+        const int kb = (int)(block - nb * kblocks);
+        const int64_t j = nb * 32 + (lane & 31);
+        const int k0 = kb * 16 + (lane >> 5) * 8;
+        uint16_t* dst;
+        int64_t col;
+        if (swiglu) {
+            dst = ((j & 63) < 32) ? wg : wu;
+            col = (int64_t)s * F + (j >> 6) * 32 + (j & 31);
+        } else {
+            dst = wu;
+            col = (int64_t)s * F + j;
+        }
+        const uint4 o = *reinterpret_cast<const uint4*>(src + (int64_t)rec * shard_elems + c * 8);
+        const uint32_t w4[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[(int64_t)(k0 + e) * f + col] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+    }
+}
+
+__global__ void unpack_down_bf16(const uint16_t* __restrict__ src, uint16_t* __restrict__ wd,
+                                 const int32_t* __restrict__ order, int64_t shard_elems,
+                                 int64_t down_off, int d, int F, int64_t chunks_per_shard) {
+    const int rec = blockIdx.y;
+    const int s = order[rec];
+    const int kblocks = F >> 4;
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks_per_shard;
+         c += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t block = c >> 6;
+        const int lane = (int)(c & 63);
+        const int64_t nb = block / kblocks;
+        const int kb = (int)(block - nb * kblocks);
+        const int64_t n = nb * 32 + (lane & 31);
+        const int64_t r0 = (int64_t)s * F + kb * 16 + (lane >> 5) * 8;
+        const uint4 o = *reinterpret_cast<const uint4*>(src + (int64_t)rec * shard_elems + down_off + c * 8);
+        const uint32_t w4[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wd[(r0 + e) * d + n] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+    }
+}
+
 // fp32 records keep the natural row-major orientation, per shard:
 //   [gate cols d x F][up cols d x F][down rows F x d]  (GeLU: no gate part).
 __global__ void pack_f32(const float* __restrict__ wg, const float* __restrict__ wu,
@@ -127,6 +181,23 @@ hipError_t launch_pack_bf16(const void* wg, const void* wu, const void* wd, void
     dim3 g2((unsigned)std::min<int64_t>((dn_chunks + 255) / 256, 4096), P);
     hipLaunchKernelGGL(pack_down_bf16, g2, blk, 0, st, (const uint16_t*)wd, (uint16_t*)dst, order,
                        shard_elems, down_off, d, F, dn_chunks);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack_bf16(const void* src, void* wg, void* wu, void* wd, const int32_t* order,
+                              int64_t shard_elems, int64_t down_off, int d, int f, int F, int P, int swiglu,
+                              hipStream_t st) {
+    const int64_t ngu = swiglu ? 2LL * F : (int64_t)F;
+    const int64_t gu_chunks = ngu * d / 8, dn_chunks = (int64_t)d * F / 8;
+    dim3 blk(256);
+    dim3 g1((unsigned)std::min<int64_t>((gu_chunks + 255) / 256, 4096), P);
+    hipLaunchKernelGGL(unpack_gateup_bf16, g1, blk, 0, st, (const uint16_t*)src, (uint16_t*)wg, (uint16_t*)wu,
+                       order, shard_elems, d, f, F, swiglu, gu_chunks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 g2((unsigned)std::min<int64_t>((dn_chunks + 255) / 256, 4096), P);
+    hipLaunchKernelGGL(unpack_down_bf16, g2, blk, 0, st, (const uint16_t*)src, (uint16_t*)wd, order, shard_elems,
+                       down_off, d, F, dn_chunks);
     return hipGetLastError();
 }
 

@@ -1,11 +1,22 @@
-// Shape-6 MFMA pipeline (gfx950), shared by the forward kernels and the
-// backward's matrix products.
+// The 256 x 256 MFMA pipeline (gfx950), shared by the forward kernels, the
+// attention projection and the backward's matrix products.
 //
 // A 256 x 256 output tile per workgroup, 4 waves (one per SIMD) as 2 x 2, each
 // wave a 128 x 128 piece held in 64 16x16 fp32 accumulators (all 256
-// accumulation registers), v_mfma_f32_16x16x32_bf16. Operands stream through
-// a 5-stage LDS ring of 32-deep reduction stages (5 x 32 KiB = all 160 KiB)
-// filled by global-to-LDS loads; a wave reads 16 fragments per 64 MFMAs.
+// accumulation registers), v_mfma_f32_16x16x32_bf16, 32 reduction indices per
+// step; a wave reads 16 fragments per 64 MFMAs. Operands reach LDS by
+// global-to-LDS loads, in one of two rings over the 160 KiB:
+//
+// * the split ring (mainloop): the A operand through 4 stages 32 deep, the B
+//   operand (token rows) through 3 super-stages 64 deep, so that every B load
+//   instruction reads 8 whole 128-byte rows. With 64-byte row pieces each
+//   instruction makes 16 cache-line requests instead of 8, and the texture
+//   address unit spent a quarter of the gate/up kernel's cycles stalled on the
+//   L1 (TA_ADDR_STALLED_BY_TC_CYCLES 0.31 per CU-cycle; 0.04 here). A load has
+//   two steps to land.
+// * the 5-stage ring (mainloop5): both operands in 32-deep stages (B in 64-byte
+//   row pieces); a load has three steps to land. The down product, whose
+//   operands stream from beyond the L2, runs faster on it.
 //
 // The first reduction step starts every accumulator from the constant 0
 // (MFMA source C = 0) instead of adding to zero-initialised registers: with
@@ -13,14 +24,9 @@
 // loop (with zero-initialised registers it copies accumulators between
 // registers on every trip).
 //
-// An operand source (Src) supplies one stage's loads for this wave, the
-// fragment reads, and the walk over the reduction dimension:
-//   void issue(int g, uint16_t* lds_stage)   load g of LOADS for the current stage
-//   void advance()                           next stage (clamped to the last one)
-//   void read(int q, const uint16_t* lds_stage, bf16x8 (&af)[TM], bf16x8 (&bv)[TN])
 // PackedSrc takes the A operand from packed 32 x 16 fragment blocks (the
 // forward's weight records); RowSrc takes it from a row-major matrix with
-// the reduction index contiguous, like the B operand (the backward).
+// the reduction index contiguous (the backward). B is always row-major.
 #pragma once
 
 #include "common.h"
@@ -43,13 +49,24 @@ namespace w16 {
 
 constexpr int BM = 256, BN = 256, NW = 4, WN = 2;
 constexpr int TM = 8, TN = 8;                           // 16-row / 16-token MFMA blocks per wave
-constexpr int A_BLK = BM / 16, B_BLK = BN / 16;         // 1 KiB blocks per 32-wide stage
-constexpr int LA = A_BLK / NW, LB = B_BLK / NW;         // blocks each wave loads per stage
+// A operand: a ring of NA stages, 32 reduction indices each, sixteen 1 KiB
+// blocks per stage (A_BLK), each wave loading LA of them per step.
+constexpr int A_BLK = BM / 16;
+constexpr int LA = A_BLK / NW;
+constexpr int A_STAGE = A_BLK * 512;                    // elements
+constexpr int NA = 4;
+// B operand (token rows): a ring of NB super-stages of 64 reduction indices,
+// so that every load instruction fetches 8 whole 128-byte rows (one full
+// cache line per row). A super-stage is loaded in two halves of 128 rows,
+// one half per step, each wave loading LB pieces of 8 rows per half.
+constexpr int B_SUPER = BN * 64;                        // elements
+constexpr int NB = 3;
+constexpr int LB = BN / 2 / 8 / NW;
 constexpr int LOADS = LA + LB;
-constexpr int STAGE = (A_BLK + B_BLK) * 512;
-constexpr int NS = 5;                                   // 5 x 32 KiB = all 160 KiB of LDS
-static_assert(NS * STAGE * 2 <= 160 * 1024, "LDS");
-static_assert((NS - 1) * LOADS <= 63, "vmcnt range");
+constexpr int B_OFF = NA * A_STAGE;                     // element offset of the B ring
+constexpr int LDS_ELEMS = NA * A_STAGE + NB * B_SUPER;  // 64 + 96 KiB = all 160 KiB of LDS
+static_assert(LDS_ELEMS * 2 <= 160 * 1024, "LDS");
+static_assert(LOADS == 8, "schedule");
 
 #define TSP_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
@@ -81,6 +98,50 @@ __device__ __forceinline__ bf16x8 read_rows(const uint16_t* region, int blk, int
     return reinterpret_cast<const bf16x8*>(region)[blk * 64 + b_slot(r, c)];
 }
 
+// B super-stage layout: row r's 16-byte chunk c (c = 0..7, reduction indices
+// 8 c .. 8 c + 7 of the 64) sits in slot 8 r + (c ^ (r % 8)). A fragment
+// read (lane l: row l % 16 of a 16-row block, chunk 4 h + l / 16 for the
+// step's half h) then puts eight consecutive lanes on eight different 16-byte
+// bank groups.
+__device__ __forceinline__ int b64_slot(int r, int c) { return 8 * r + (c ^ (r & 7)); }
+
+// 8 rows x 128 bytes into one 1 KiB piece of a B super-stage: lane l loads
+// row row0 + l / 8 (clamped to last_row; row0 % 8 == 0) and the 16 bytes that
+// land in slot l % 8 of that row, i.e. chunk (l % 8) ^ (l / 8). Every lane
+// group of 8 reads one whole 128-byte row.
+template <bool BUF>
+__device__ __forceinline__ void load_rows128(uint16_t* lds_piece, const uint16_t* __restrict__ base, int ld,
+                                             int row0, int last_row, int lane) {
+    const int rr = lane >> 3;
+    const int c = (lane & 7) ^ rr;                      // slot = lane = b64_slot(rr, c) - 8 rr + 8 rr
+    TSP_LDS void* dst = (TSP_LDS void*)lds_piece;
+    const int row = min(row0 + rr, last_row);
+    const int64_t off = (int64_t)row * ld + c * 8;
+    if constexpr (BUF) {
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, kRawBufferWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (int)(off * 2), 0, 0, 0);
+    } else {
+        __builtin_amdgcn_global_load_lds(base + off, dst, 16, 0, 0);
+    }
+}
+
+// B fragment of 16-row block blk for the step's half h of a super-stage.
+__device__ __forceinline__ bf16x8 read_rows128(const uint16_t* super, int blk, int h, int lane) {
+    const int r = blk * 16 + (lane & 15), c = 4 * h + (lane >> 4);
+    return reinterpret_cast<const bf16x8*>(super)[b64_slot(r, c)];
+}
+
+// An operand source supplies, for this wave:
+//   issue_a(g, lds_stage)       A load g (< LA) of the current A stage
+//   advance_a()                 next A stage (clamped to the last one)
+//   issue_b(g, lds_super, h)    B load g (< LB) of half h of the current super-stage
+//   advance_b()                 next super-stage (clamped to the last one)
+//   read_a(q, lds_stage, af)    A fragment q (< TM)
+// The B fragments are read by the pipeline itself (read_rows128): B is always
+// a row-major token-like operand, rows b_row0 + ..., with the reduction index
+// contiguous.
+//
 // Forward operands: A = packed weight records (32 x 16 fragment blocks, a
 // stage's 256 rows are 8 blocks of 32 rows, each two 1 KiB blocks deep), B =
 // token rows (T x ldb row-major). spp > 0 (down product): the reduction walks
@@ -88,61 +149,68 @@ __device__ __forceinline__ bf16x8 read_rows(const uint16_t* region, int blk, int
 template <bool BUF>
 struct PackedSrc {
     const uint16_t* a;                                  // A slab of the current stage
-    int tl, ls;                                         // stage index, step inside the record
+    int tl, ls;                                         // A stage index, step inside the record
     int ksteps, spp;
     int64_t a_rec, a_rs;                                // record stride, 32-row block stride (elements)
     const uint16_t* b_src;
     int ldb, t0, T, w, wm, wn, lane;
+    int sb = 0;                                         // B super-stage index
 
-    __device__ void issue(int g, uint16_t* lds_stage) {
-        if (g < LA) {
-            const int b = g * NW + w;
-            TSP_LDS void* dst = (TSP_LDS void*)(lds_stage + b * 512);
-            const int64_t off = (b >> 1) * a_rs + (b & 1) * 512 + lane * 8;
-            if constexpr (BUF) {
-                const __amdgpu_buffer_rsrc_t rs =
-                    __builtin_amdgcn_make_buffer_rsrc((void*)a, (short)0, 0x7fffffff, kRawBufferWord3);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (int)(off * 2), 0, 0, 0);
-            } else {
-                __builtin_amdgcn_global_load_lds(a + off, dst, 16, 0, 0);
-            }
+    __device__ void issue_a(int g, uint16_t* lds_stage) {
+        const int b = g * NW + w;
+        TSP_LDS void* dst = (TSP_LDS void*)(lds_stage + b * 512);
+        const int64_t off = (b >> 1) * a_rs + (b & 1) * 512 + lane * 8;
+        if constexpr (BUF) {
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc((void*)a, (short)0, 0x7fffffff, kRawBufferWord3);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (int)(off * 2), 0, 0, 0);
         } else {
-            const int bb = (g - LA) * NW + w;
-            load_rows<BUF>(lds_stage + (A_BLK + bb) * 512, b_src + (int64_t)tl * 32, ldb, t0 + bb * 16, T - 1, lane);
+            __builtin_amdgcn_global_load_lds(a + off, dst, 16, 0, 0);
         }
     }
-    __device__ void advance() {
+    __device__ void advance_a() {
         const bool adv = tl + 1 < ksteps;
         const bool wrap = spp > 0 && ls + 1 == spp;
         a += adv ? (wrap ? a_rec - (int64_t)(spp - 1) * 1024 : (int64_t)1024) : (int64_t)0;
         ls = adv ? (wrap ? 0 : ls + 1) : ls;
         tl += adv ? 1 : 0;
     }
+    __device__ void issue_b(int g, uint16_t* lds_super, int h) {
+        const int r0 = h * (BN / 2) + (g * NW + w) * 8;
+        load_rows128<BUF>(lds_super + r0 * 64, b_src + (int64_t)sb * 64, ldb, t0 + r0, T - 1, lane);
+    }
+    __device__ void advance_b() { sb += 2 * (sb + 1) < ksteps ? 1 : 0; }
+    // 32-deep B stages of the 5-stage ring (mainloop5): 16-row x 64-byte pieces
+    // at the A stage's reduction offset (the two operands advance together
+    // there, advance_a moves both)
+    __device__ void issue_b32(int g, uint16_t* lds_blocks) {
+        const int bb = g * NW + w;
+        load_rows<BUF>(lds_blocks + bb * 512, b_src + (int64_t)tl * 32, ldb, t0 + bb * 16, T - 1, lane);
+    }
     // A fragment q: 16-row block ib = rows 16 (ib % 2) + l % 16 of 32-row block
     // ib / 2, reduction indices 8 (l / 16) .. + 7 (two 1 KiB blocks deep).
-    __device__ void read(int q, const uint16_t* lds_stage, bf16x8 (&af)[TM], bf16x8 (&bv)[TN]) const {
-        if (q < TM) {
-            const int r = lane & 15, c = lane >> 4;
-            const bf16x8* as = reinterpret_cast<const bf16x8*>(lds_stage);
-            const int ib = wm * TM + q;
-            af[q] = as[((ib >> 1) * 2 + (c >> 1)) * 64 + (c & 1) * 32 + (ib & 1) * 16 + r];
-        } else {
-            bv[q - TM] = read_rows(lds_stage + A_BLK * 512, wn * TN + q - TM, lane);
-        }
+    __device__ void read_a(int q, const uint16_t* lds_stage, bf16x8 (&af)[TM]) const {
+        const int r = lane & 15, c = lane >> 4;
+        const bf16x8* as = reinterpret_cast<const bf16x8*>(lds_stage);
+        const int ib = wm * TM + q;
+        af[q] = as[((ib >> 1) * 2 + (c >> 1)) * 64 + (c & 1) * 32 + (ib & 1) * 16 + r];
     }
 };
 
 // Backward operands: C[n][m] = sum_k A[m][k] B[n][k] with A (M x K, lda) and
-// B (N x K, ldb) row-major, both loaded like the forward's token operand. The
-// reduction runs over nseg segments of spp steps; segment j uses A and B at
-// a_base[j % kinds] + (order ? order[j / kinds] : j / kinds) * a_seg and
-// b_base[j % kinds] + (j / kinds) * b_seg (elements along the rows), which
-// walks (gate, up) column blocks of the weights in ring order for dX.
+// B (N x K, ldb) row-major. The reduction runs over nseg segments of spp steps;
+// segment j uses A and B at a_base[j % kinds] + (order ? order[j / kinds] :
+// j / kinds) * a_seg and b_base[j % kinds] + (j / kinds) * b_seg (elements
+// along the rows), which walks (gate, up) column blocks of the weights in
+// ring order for dX. A is loaded in 64-byte row pieces into the A ring, B in
+// whole 128-byte rows into the B ring; the two walk the segments with cursors
+// of their own (B runs ahead of A). spp is even.
 template <bool BUF>
 struct RowSrc {
     const uint16_t* a;                                  // A at the current stage's reduction offset
-    const uint16_t* b;
-    int ls, j;                                          // step inside the segment, segment
+    const uint16_t* b;                                  // B at the current super-stage's offset
+    int ls, j;                                          // A: step inside the segment, segment
+    int lsb, jb;                                        // B: super-stage inside the segment, segment
     int spp, nseg, kinds;
     const uint16_t *a_base0, *a_base1;                  // segment kinds 0 and 1 (no indexed arrays:
     const uint16_t *b_base0, *b_base1;                  // a runtime index would put them in scratch)
@@ -150,62 +218,208 @@ struct RowSrc {
     const int32_t* order;
     int lda, ldb, m0, n0, last_m, last_n, w, wm, wn, lane;
 
-    __device__ void seek(int seg) {
+    __device__ void seek_a(int seg) {
         const int kind = seg % kinds, k = seg / kinds;
         // wave-uniform (the buffer resource built from it must live in SGPRs)
         const int s = order ? __builtin_amdgcn_readfirstlane(order[k]) : k;
         a = (kind ? a_base1 : a_base0) + (int64_t)s * a_seg;
+    }
+    __device__ void seek_b(int seg) {
+        const int kind = seg % kinds, k = seg / kinds;
         b = (kind ? b_base1 : b_base0) + (int64_t)k * b_seg;
     }
-    __device__ void issue(int g, uint16_t* lds_stage) {
-        if (g < LA) {
-            const int blk = g * NW + w;
-            load_rows<BUF>(lds_stage + blk * 512, a, lda, m0 + blk * 16, last_m, lane);
-        } else {
-            const int bb = (g - LA) * NW + w;
-            load_rows<BUF>(lds_stage + (A_BLK + bb) * 512, b, ldb, n0 + bb * 16, last_n, lane);
-        }
+    __device__ void issue_a(int g, uint16_t* lds_stage) {
+        const int blk = g * NW + w;
+        load_rows<BUF>(lds_stage + blk * 512, a, lda, m0 + blk * 16, last_m, lane);
     }
-    __device__ void advance() {
+    __device__ void advance_a() {
         if (ls + 1 < spp) {
             ++ls;
             a += 32;
-            b += 32;
         } else if (j + 1 < nseg) {
             ls = 0;
-            seek(++j);
+            seek_a(++j);
         }
     }
-    __device__ void read(int q, const uint16_t* lds_stage, bf16x8 (&af)[TM], bf16x8 (&bv)[TN]) const {
-        if (q < TM) af[q] = read_rows(lds_stage, wm * TM + q, lane);
-        else bv[q - TM] = read_rows(lds_stage + A_BLK * 512, wn * TN + q - TM, lane);
+    __device__ void issue_b(int g, uint16_t* lds_super, int h) {
+        const int r0 = h * (BN / 2) + (g * NW + w) * 8;
+        load_rows128<BUF>(lds_super + r0 * 64, b, ldb, n0 + r0, last_n, lane);
+    }
+    __device__ void advance_b() {
+        if (lsb + 2 < spp) {
+            lsb += 2;
+            b += 64;
+        } else if (jb + 1 < nseg) {
+            lsb = 0;
+            seek_b(++jb);
+        }
+    }
+    __device__ void read_a(int q, const uint16_t* lds_stage, bf16x8 (&af)[TM]) const {
+        af[q] = read_rows(lds_stage, wm * TM + q, lane);
     }
 };
 
-__device__ __forceinline__ int next_buf(int off) { return off == (NS - 1) * STAGE ? 0 : off + STAGE; }
+// Ring bookkeeping: byte-free element offsets of the stage/super-stage that
+// step t loads into and the one whose fragments it reads.
+struct Ring {
+    int a_ld = 0, a_rd = A_STAGE;                       // A buffers: loads of stage t + 4, reads of t + 1
+    int b_ld = 2 * B_SUPER, b_rd = 0;                   // B buffers: loads of half t + 5, reads of t + 1
+};
+__device__ __forceinline__ int next_a(int off) { return off == (NA - 1) * A_STAGE ? 0 : off + A_STAGE; }
+__device__ __forceinline__ int next_b(int off) { return off == (NB - 1) * B_SUPER ? 0 : off + B_SUPER; }
 
-// Step t. The barrier makes every wave's share of stage t + 1 visible and
-// ends every wave's fragment reads of stage t (issued in step t - 1), so
-// stage t's buffer takes the loads of stage t + NS. The wave then reads stage
-// t + 1's fragments into the other register set while its MFMAs run on stage
-// t's, and before the next barrier waits for those reads and for its own
-// loads of stage t + 2. Every step issues one stage (past the end, the last
-// stage again, into a buffer nobody reads), so that wait is always "at most 3
-// stages newer". FIRST: the accumulators start from 0. LAST: MFMAs only.
+// Step t, H = (t + 1) % 2. The barrier makes every wave's share of step t + 1's
+// data visible and ends every wave's fragment reads of step t (issued in step
+// t - 1). The wave then loads A stage t + 4 into the A buffer step t read and
+// half H of B super-stage (t + 5) / 2 (half t + 5 of the B stream) into the B
+// buffer that super-stage (t + 5) / 2 - 3 held, whose last step (t - 1 or t)
+// has been read; it reads step t + 1's fragments into the other register set
+// while its MFMAs run on step t's, and before the next barrier waits for those
+// reads and for every load it issued up to step t - 1 (step t + 2's data: A
+// stage t + 2 was issued in step t - 2, the two halves of its B super-stage in
+// steps t - 4 .. t - 2). Every step issues its loads (past the end, the last
+// stage again, into a buffer nobody reads), so that wait is always "at most
+// two steps' loads outstanding". FIRST: the accumulators start from 0. LAST:
+// MFMAs only.
 //
 // With one wave per SIMD nothing else feeds the matrix pipe while this wave
 // issues other work, so scheduling fences fix the order: three MFMAs right
 // after the barrier, then eight groups of one load, two fragment reads and
 // seven MFMAs (a load right after another costs the matrix pipe far more
-// than one that follows a few MFMAs: 3-5 % of the kernel time here), and the
-// scalar bookkeeping for the next step spread over the last five MFMAs.
-template <bool FIRST, bool LAST, class Src>
-__device__ __forceinline__ void step(int& ld_ref, int& rd_ref, Src& src, uint16_t* lds, f32x4 (&acc)[TM][TN],
+// than one that follows a few MFMAs), and the scalar bookkeeping for the next
+// step spread over the last five MFMAs.
+template <bool FIRST, bool LAST, int H, class Src>
+__device__ __forceinline__ void step(Ring& rg, Src& src, uint16_t* lds, f32x4 (&acc)[TM][TN],
                                      const bf16x8 (&ca)[TM], const bf16x8 (&cb)[TN], bf16x8 (&na)[TM],
                                      bf16x8 (&nb)[TN]) {
     constexpr int LEAD = 3, GROUP = 7;
     constexpr int TAIL = TM * TN - LEAD - LOADS * GROUP;
-    static_assert(LOADS == 8 && TM + TN == 2 * LOADS && TAIL == 5, "schedule");
+    static_assert(TM + TN == 2 * LOADS && TAIL == 5, "schedule");
+    auto mf = [&](int m) {
+        const int i = m / TN, j = m % TN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], FIRST ? f32x4{0.f, 0.f, 0.f, 0.f}
+                                                                                : acc[i][j], 0, 0, 0);
+    };
+    if constexpr (LAST) {
+#pragma unroll
+        for (int m = 0; m < TM * TN; ++m) mf(m);
+        // the epilogue starts after every MFMA: MFMAs sunk into it keep the
+        // fragment registers alive there and made the compiler spill
+        __builtin_amdgcn_sched_barrier(0);
+        return;
+    }
+    const int a_ld = rg.a_ld, a_rd = rg.a_rd, b_ld = rg.b_ld, b_rd = rg.b_rd;
+    stage_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < LEAD; ++m) mf(m);
+    __builtin_amdgcn_sched_barrier(0);
+    const int lane = src.lane;
+#pragma unroll
+    for (int g = 0; g < LOADS; ++g) {
+        const int m0 = LEAD + GROUP * g;
+        if (g < LA) src.issue_a(g, lds + a_ld);
+        else src.issue_b(g - LA, lds + B_OFF + b_ld, H);
+        mf(m0);
+        mf(m0 + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (g < TM / 2) src.read_a(2 * g, lds + a_rd, na);
+        else nb[2 * g - TM] = read_rows128(lds + B_OFF + b_rd, src.wn * TN + 2 * g - TM, H, lane);
+        mf(m0 + 2);
+        mf(m0 + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        if (g < TM / 2) src.read_a(2 * g + 1, lds + a_rd, na);
+        else nb[2 * g + 1 - TM] = read_rows128(lds + B_OFF + b_rd, src.wn * TN + 2 * g + 1 - TM, H, lane);
+        mf(m0 + 4);
+        mf(m0 + 5);
+        mf(m0 + 6);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    src.advance_a();
+    rg.a_ld = a_rd;
+    rg.a_rd = next_a(a_rd);
+    if constexpr (H == 1) {                             // the next loads go to a new super-stage
+        src.advance_b();
+        rg.b_ld = next_b(b_ld);
+    }
+    if constexpr (H == 1) rg.b_rd = next_b(b_rd);       // the next step reads a new super-stage
+#pragma unroll
+    for (int m = TM * TN - TAIL; m < TM * TN; ++m) mf(m);
+#pragma unroll
+    for (int k = 0; k < TAIL; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x006, 4, 0);   // VALU / SALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    TSP_VMCNT(2 * LOADS);                               // own loads up to step t - 1 landed
+    lgkm_zero();                                        // step t + 1's fragments in registers
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The reduction over ksteps steps (even, >= 2) of 32 indices on the split
+// ring. src is positioned at step 0 for both operands. The prologue issues B
+// half 0, then (A stage s, B half s + 1) for s = 0..3, exactly as steps
+// -5..-1 would, and reads step 0's fragments. (Issuing a whole B super-stage
+// every other step instead, which gives it 3 steps to land, measured slower
+// for both products.)
+template <class Src>
+__device__ __forceinline__ void mainloop(uint16_t* lds, f32x4 (&acc)[TM][TN], int ksteps, Src& src) {
+    bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
+    const int lane = src.lane;
+#pragma unroll
+    for (int g = 0; g < LB; ++g) src.issue_b(g, lds + B_OFF, 0);
+#pragma unroll
+    for (int s = 0; s < NA; ++s) {
+        const int u = s + 1;                            // B half u: super-stage u / 2, half u % 2
+#pragma unroll
+        for (int g = 0; g < LA; ++g) src.issue_a(g, lds + s * A_STAGE);
+        src.advance_a();
+#pragma unroll
+        for (int g = 0; g < LB; ++g) src.issue_b(g, lds + B_OFF + (u >> 1) * B_SUPER, u & 1);
+        if (u & 1) src.advance_b();
+    }
+    TSP_VMCNT(3 * LOADS);                               // A stage 0 and B super-stage 0 landed
+    stage_barrier();
+#pragma unroll
+    for (int q = 0; q < TM; ++q) src.read_a(q, lds, a0);
+#pragma unroll
+    for (int q = 0; q < TN; ++q) b0[q] = read_rows128(lds + B_OFF, src.wn * TN + q, 0, lane);
+    TSP_VMCNT(2 * LOADS + LB);                          // A stage 1 landed too
+    lgkm_zero();
+    __builtin_amdgcn_sched_barrier(0);
+
+    Ring rg;
+    step<true, false, 1>(rg, src, lds, acc, a0, b0, a1, b1);
+    for (int t = 1; t + 2 < ksteps; t += 2) {
+        step<false, false, 0>(rg, src, lds, acc, a1, b1, a0, b0);
+        step<false, false, 1>(rg, src, lds, acc, a0, b0, a1, b1);
+    }
+    step<false, true, 0>(rg, src, lds, acc, a1, b1, a0, b0);
+    TSP_VMCNT(0);                                       // no load into LDS outlives the workgroup
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// ---- the 5-stage ring -------------------------------------------------------
+// Both operands in 32-deep stages of 32 KiB ([A 16 KiB][B 16 KiB], B as
+// sixteen 16-row x 64-byte blocks), five stages in the 160 KiB: step t loads
+// stage t + 5 into the buffer stage t held, and before the next barrier waits
+// only for stage t + 2, issued in step t - 3, so a load has three steps to land
+// (two in the split ring). The price is the B loads' 64-byte row pieces: 16
+// cache-line requests per instruction instead of 8. The down product, whose
+// operands (H and the down weights) stream from beyond the L2, runs faster on
+// this ring; the gate/up product on the split one (measured on one box).
+constexpr int R5_STAGE = 2 * A_STAGE;
+constexpr int NS5 = 5;
+static_assert(NS5 * R5_STAGE <= LDS_ELEMS, "LDS");
+
+__device__ __forceinline__ int next5(int off) { return off == (NS5 - 1) * R5_STAGE ? 0 : off + R5_STAGE; }
+
+template <bool FIRST, bool LAST, class Src>
+__device__ __forceinline__ void step5(int& ld_ref, int& rd_ref, Src& src, uint16_t* lds, f32x4 (&acc)[TM][TN],
+                                      const bf16x8 (&ca)[TM], const bf16x8 (&cb)[TN], bf16x8 (&na)[TM],
+                                      bf16x8 (&nb)[TN]) {
+    constexpr int LEAD = 3, GROUP = 7;
+    constexpr int TAIL = TM * TN - LEAD - LOADS * GROUP;
     auto mf = [&](int m) {
         const int i = m / TN, j = m % TN;
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[i], cb[j], FIRST ? f32x4{0.f, 0.f, 0.f, 0.f}
@@ -222,26 +436,30 @@ __device__ __forceinline__ void step(int& ld_ref, int& rd_ref, Src& src, uint16_
 #pragma unroll
     for (int m = 0; m < LEAD; ++m) mf(m);
     __builtin_amdgcn_sched_barrier(0);
+    const int lane = src.lane;
 #pragma unroll
     for (int g = 0; g < LOADS; ++g) {
         const int m0 = LEAD + GROUP * g;
-        src.issue(g, lds + ld_off);
+        if (g < LA) src.issue_a(g, lds + ld_off);
+        else src.issue_b32(g - LA, lds + ld_off + A_STAGE);
         mf(m0);
         mf(m0 + 1);
         __builtin_amdgcn_sched_barrier(0);
-        src.read(2 * g, lds + rd_off, na, nb);
+        if (g < TM / 2) src.read_a(2 * g, lds + rd_off, na);
+        else nb[2 * g - TM] = read_rows(lds + rd_off + A_STAGE, src.wn * TN + 2 * g - TM, lane);
         mf(m0 + 2);
         mf(m0 + 3);
         __builtin_amdgcn_sched_barrier(0);
-        src.read(2 * g + 1, lds + rd_off, na, nb);
+        if (g < TM / 2) src.read_a(2 * g + 1, lds + rd_off, na);
+        else nb[2 * g + 1 - TM] = read_rows(lds + rd_off + A_STAGE, src.wn * TN + 2 * g + 1 - TM, lane);
         mf(m0 + 4);
         mf(m0 + 5);
         mf(m0 + 6);
         __builtin_amdgcn_sched_barrier(0);
     }
-    src.advance();
+    src.advance_a();
     ld_ref = rd_off;
-    rd_ref = next_buf(rd_off);
+    rd_ref = next5(rd_off);
 #pragma unroll
     for (int m = TM * TN - TAIL; m < TM * TN; ++m) mf(m);
 #pragma unroll
@@ -255,45 +473,38 @@ __device__ __forceinline__ void step(int& ld_ref, int& rd_ref, Src& src, uint16_
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// One stream of stages through the LDS ring. start() issues the first NS
-// stages and reads stage 0's fragments; tile() runs one tile's ksteps stages
-// (even, >= 2) from the stream, leaving the next tile's stage-0 fragments in
-// (a0, b0) unless END; finish() waits for every load into LDS. A workgroup
-// that runs several tiles back to back (a source whose advance() walks on to
-// the next tile) thus issues the next tile's first loads during this tile's
-// last steps, and they land while it writes its results.
+// The reduction over ksteps stages (even, >= 2) on the 5-stage ring; src is
+// positioned at stage 0 for both operands (issue_a / issue_b32).
 template <class Src>
-struct Stream {
+__device__ __forceinline__ void mainloop5(uint16_t* lds, f32x4 (&acc)[TM][TN], int ksteps, Src& src) {
     bf16x8 a0[TM], b0[TN], a1[TM], b1[TN];
-    int ld = 0, rd = STAGE;                             // buffers of stages t and t + 1
-
-    __device__ __forceinline__ void start(uint16_t* lds, Src& src) {
-        for (int t = 0; t < NS; ++t) {
+    const int lane = src.lane;
 #pragma unroll
-            for (int g = 0; g < LOADS; ++g) src.issue(g, lds + t * STAGE);
-            src.advance();
-        }
-        TSP_VMCNT((NS - 1) * LOADS);                    // own loads of stage 0 landed
-        stage_barrier();
+    for (int t = 0; t < NS5; ++t) {
 #pragma unroll
-        for (int q = 0; q < TM + TN; ++q) src.read(q, lds, a0, b0);
-        TSP_VMCNT((NS - 2) * LOADS);                    // own loads of stage 1 landed
-        lgkm_zero();
-        __builtin_amdgcn_sched_barrier(0);
+        for (int g = 0; g < LA; ++g) src.issue_a(g, lds + t * R5_STAGE);
+#pragma unroll
+        for (int g = 0; g < LOADS - LA; ++g) src.issue_b32(g, lds + t * R5_STAGE + A_STAGE);
+        src.advance_a();
     }
-    template <bool END>
-    __device__ __forceinline__ void tile(uint16_t* lds, f32x4 (&acc)[TM][TN], int ksteps, Src& src) {
-        step<true, false>(ld, rd, src, lds, acc, a0, b0, a1, b1);
-        for (int t = 1; t + 2 < ksteps; t += 2) {
-            step<false, false>(ld, rd, src, lds, acc, a1, b1, a0, b0);
-            step<false, false>(ld, rd, src, lds, acc, a0, b0, a1, b1);
-        }
-        step<false, END>(ld, rd, src, lds, acc, a1, b1, a0, b0);
+    TSP_VMCNT((NS5 - 1) * LOADS);                       // own loads of stage 0 landed
+    stage_barrier();
+#pragma unroll
+    for (int q = 0; q < TM; ++q) src.read_a(q, lds, a0);
+#pragma unroll
+    for (int q = 0; q < TN; ++q) b0[q] = read_rows(lds + A_STAGE, src.wn * TN + q, lane);
+    TSP_VMCNT((NS5 - 2) * LOADS);                       // own loads of stage 1 landed
+    lgkm_zero();
+    __builtin_amdgcn_sched_barrier(0);
+    int ld = 0, rd = R5_STAGE;                          // buffers of stages t and t + 1
+    step5<true, false>(ld, rd, src, lds, acc, a0, b0, a1, b1);
+    for (int t = 1; t + 2 < ksteps; t += 2) {
+        step5<false, false>(ld, rd, src, lds, acc, a1, b1, a0, b0);
+        step5<false, false>(ld, rd, src, lds, acc, a0, b0, a1, b1);
     }
-    __device__ __forceinline__ void finish() {
-        TSP_VMCNT(0);                                   // no load into LDS outlives the workgroup
-    }
-};
+    step5<false, true>(ld, rd, src, lds, acc, a1, b1, a0, b0);
+    TSP_VMCNT(0);                                       // no load into LDS outlives the workgroup
+}
 
 // A workgroup's bf16 result rows staged in the LDS ring once the reduction is
 // done, so that the global stores write whole rows: straight from the MFMA
@@ -310,7 +521,7 @@ struct StagedRows16 {
     static_assert(ROWS == 256 || ROWS == 128, "ROWS");
     static constexpr int PITCH = COLS + 8;
     static constexpr int ELEMS = ROWS * PITCH;          // LDS elements one staged tile takes
-    static_assert(ELEMS * 2 <= NS * STAGE * 2, "LDS");
+    static_assert(ELEMS * 2 <= LDS_ELEMS * 2, "LDS");
     uint16_t* lds;
     __device__ __forceinline__ void put4(int r, int c, uint2 v) {
         *reinterpret_cast<uint2*>(lds + r * PITCH + c) = v;
@@ -338,7 +549,7 @@ struct StagedRows16 {
 struct StagedRowsF32 {
     static constexpr int COLS = 256, ROWS = 128, PITCH = COLS + 4;
     static constexpr int ELEMS = ROWS * PITCH;          // floats
-    static_assert(ELEMS * 4 <= NS * STAGE * 2, "LDS");
+    static_assert(ELEMS * 4 <= LDS_ELEMS * 2, "LDS");
     float* lds;
     __device__ __forceinline__ void put4(int r, int c, f32x4 v) {
         *reinterpret_cast<f32x4*>(lds + r * PITCH + c) = v;
@@ -356,14 +567,6 @@ struct StagedRowsF32 {
     }
 };
 
-// The reduction over ksteps stages (even, >= 2). src is positioned at stage 0.
-template <class Src>
-__device__ __forceinline__ void mainloop(uint16_t* lds, f32x4 (&acc)[TM][TN], int ksteps, Src& src) {
-    Stream<Src> st;
-    st.start(lds, src);
-    st.template tile<true>(lds, acc, ksteps, src);
-    st.finish();
-}
 #undef TSP_VMCNT
 
 }  // namespace w16

@@ -24,7 +24,7 @@ def test_bench_emits_the_contract_line(wl):
         pytest.skip("no GPU")
     print(f"[gpu] bench {wl}", flush=True)
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", wl, "--steps", "2",
-                        "--warmup", "1", "--no-cpu-baseline", "--no-ceilings"],
+                        "--warmup", "1", "--no-cpu-baseline", "--no-ceilings", "--also", ""],
                        capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
@@ -38,6 +38,32 @@ def test_bench_emits_the_contract_line(wl):
     for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert k in roof, k
     assert 0 < roof["frac"] < 1
+
+
+@pytest.mark.gpu
+def test_bench_default_line_carries_the_whole_metric():
+    """The default run: the Llama-shaped headline, then the 70B long-context
+    (TFLOP/s) and decode (GB/s) workloads in the same process, each with its
+    per-step median and minimum and its own roofline."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print("[gpu] bench default line", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3", "--warmup", "1",
+                        "--no-cpu-baseline", "--no-ceilings"], capture_output=True, text=True, timeout=900)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    assert d["config"]["workload"].startswith("llama3-8b") and d["unit"] == "TFLOP/s"
+    assert d["min_ms"] <= d["median_ms"] <= d["max_ms"]
+    also = {a["config"]["workload"]: a for a in d["also"]}
+    long70, dec70 = (also[k] for k in ("70b-long-swiglu-bf16-T16384-d8192-f28672-P8",
+                                       "70b-decode-swiglu-bf16-T16-d8192-f28672-P8"))
+    assert long70["unit"] == "TFLOP/s" and long70["roofline"]["bound"] == "mfma"
+    assert dec70["unit"] == "GB/s" and dec70["roofline"]["bound"] == "hbm"
+    for a in (long70, dec70):
+        assert a["value"] > 0 and 0 < a["roofline"]["frac"] < 1 and a["min_ms"] <= a["median_ms"]
 
 
 @pytest.mark.gpu

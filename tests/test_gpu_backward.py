@@ -53,12 +53,19 @@ def run_bwd(w: Workload, inp, dy, order=None, T_max=None, reuse=None):
     wu, wd = inp.w_up.to(dev), inp.w_down.to(dev)
     mlp = reuse or TspMLP(wg, wu, wd, w.P, order=w.order() if order is None else order, act=w.act,
                           T_max=T_max or inp.x.shape[0])
-    g = mlp.backward(inp.x.to(dev).contiguous(), dy.to(dev).contiguous(), wg, wu, wd)
+    # the handle owns its weights: the caller's copies are wiped before the
+    # backward, which must not read them
+    for t in (wg, wu, wd):
+        if t is not None:
+            t.fill_(float("nan"))
+    g = mlp.backward(inp.x.to(dev).contiguous(), dy.to(dev).contiguous())
     torch.cuda.synchronize()
     return {k: None if v is None else v.cpu().double().numpy() for k, v in g.items()}, mlp
 
 
 def check(name, got, ref, el2=EL2, emax=EMAX):
+    """Every gradient's errors are printed before any is asserted."""
+    errs = {}
     for k in KEYS:
         if ref[k] is None:
             assert got[k] is None, (name, k)
@@ -67,6 +74,8 @@ def check(name, got, ref, el2=EL2, emax=EMAX):
         e2 = float(np.linalg.norm(d) / np.linalg.norm(ref[k]))
         em = float(np.max(np.abs(d)) / np.max(np.abs(ref[k])))
         say(f"[gpu]   {name} {k}: e_L2 {e2:.2e} e_max {em:.2e}")
+        errs[k] = (e2, em)
+    for k, (e2, em) in errs.items():
         assert np.all(np.isfinite(got[k])), (name, k)
         assert e2 <= el2, f"{name} {k}: e_L2 {e2:.3e}"
         if emax is not None:
@@ -165,21 +174,27 @@ def test_backward_unsupported_and_invalid():
     with pytest.raises(TspError) as e:
         run_bwd(wf, inpf, dyf)
     assert e.value.status == TSP_ERR_UNSUPPORTED
-    # GeLU handle given a gate matrix; T above T_max
+    # GeLU handle given a gate gradient (C ABI); T above T_max
+    from sharded_transformer_mlp_amd.binding import lib
     wg = Workload("u", T=32, d=256, f=1024, P=2, act="gelu_tanh", dtype="bf16", seed=70)
     inpg, dyg = make_inputs(wg), make_output_grad(wg)
     mlp = TspMLP(None, inpg.w_up.to(dev), inpg.w_down.to(dev), wg.P, act=wg.act, T_max=32)
     x, d_y = inpg.x.to(dev), dyg.to(dev)
-    with pytest.raises(TspError) as e:
-        mlp.backward(x, d_y, inpg.w_up.to(dev), inpg.w_up.to(dev), inpg.w_down.to(dev))
-    assert e.value.status == TSP_ERR_INVALID_ARG
+    dX = torch.empty(32, 256, dtype=torch.float32, device=dev)
+    dW = [torch.empty(256, 1024, dtype=torch.float32, device=dev) for _ in range(2)]
+    dWd = torch.empty(1024, 256, dtype=torch.float32, device=dev)
+    st = lib().tsp_mlp_backward(mlp.handle, 32, x.data_ptr(), d_y.data_ptr(), dX.data_ptr(), dW[0].data_ptr(),
+                                dW[1].data_ptr(), dWd.data_ptr(), None)
+    assert st == TSP_ERR_INVALID_ARG
+    st = lib().tsp_mlp_backward(mlp.handle, 32, x.data_ptr(), d_y.data_ptr(), dX.data_ptr(), None,
+                                dW[1].data_ptr(), dW[1].data_ptr(), None)       # dW_down on dW_up
+    assert st == TSP_ERR_INVALID_ARG
     big = make_inputs(wg.with_(T=33))
     with pytest.raises(TspError) as e:
-        mlp.backward(big.x.to(dev), make_output_grad(wg.with_(T=33)).to(dev), None, inpg.w_up.to(dev),
-                     inpg.w_down.to(dev))
+        mlp.backward(big.x.to(dev), make_output_grad(wg.with_(T=33)).to(dev))
     assert e.value.status == TSP_ERR_INVALID_ARG
     # the handle still works afterwards
-    g = mlp.backward(x, d_y, None, inpg.w_up.to(dev), inpg.w_down.to(dev))
+    g = mlp.backward(x, d_y)
     torch.cuda.synchronize()
     assert torch.isfinite(g["dX"]).all()
     mlp.close()

@@ -52,7 +52,7 @@ def test_forward_rejects_bad_arguments(small):
     big = torch.empty(w.T * w.d * 4, dtype=torch.uint8, device=dev)
     assert lib.tsp_mlp_forward(h, 8, big.data_ptr(), big.data_ptr() + 256, None) == INV  # Y overlaps X
     assert b"overlaps" in lib.tsp_last_error()
-    assert lib.tsp_mlp_set_tiles(h, 7, -1) == UNSUP
+    assert lib.tsp_mlp_set_tiles(h, 4, -1) == UNSUP
     assert lib.tsp_mlp_set_tiles(h, -2, -1) == INV
     assert lib.tsp_mlp_set_path(h, 9) == INV
     torch.cuda.synchronize()
@@ -69,7 +69,7 @@ def test_fp32_handle_rejects_bf16_only_settings():
     mlp = B.TspMLP(inp.w_gate.to(dev), inp.w_up.to(dev), inp.w_down.to(dev), w.P, act=w.act, T_max=w.T)
     lib = B.lib()
     say("[gpu] fp32 handle: bf16-only settings")
-    assert lib.tsp_mlp_set_tiles(mlp.handle, 5, 5) == UNSUP
+    assert lib.tsp_mlp_set_tiles(mlp.handle, 0, 0) == UNSUP
     mlp.set_path("skinny")
     with pytest.raises(B.TspError) as e:
         mlp.forward(inp.x.to(dev))

@@ -36,18 +36,14 @@ def poison_library():
 
 
 CASES = [
-    ("tiled shape 5 + split", Workload("a", T=300, d=512, f=2048, P=4, act="swiglu", dtype="bf16", seed=11, r0=1),
-     "tiled", (5, 5)),
+    ("tiled shape 0 + split", Workload("a", T=300, d=512, f=2048, P=4, act="swiglu", dtype="bf16", seed=11, r0=1),
+     "tiled", (0, 0)),
     ("tiled auto shapes + split", Workload("a", T=300, d=512, f=2048, P=4, act="swiglu", dtype="bf16", seed=11,
                                            r0=1), "tiled", None),
-    ("tiled shape 5, 4 tiles", Workload("b", T=513, d=1024, f=4096, P=2, act="swiglu", dtype="bf16", seed=12),
-     "tiled", (5, 5)),
-    ("tiled shape 6 + split", Workload("a", T=300, d=512, f=2048, P=4, act="swiglu", dtype="bf16", seed=11, r0=1),
-     "tiled", (6, 6)),
-    ("tiled shape 6, 4 tiles", Workload("b", T=513, d=1024, f=4096, P=2, act="swiglu", dtype="bf16", seed=12),
-     "tiled", (6, 6)),
-    ("tiled shape 0", Workload("c", T=290, d=512, f=2048, P=2, act="swiglu", dtype="bf16", seed=21), "tiled", (0, 0)),
-    ("tiled shape 4", Workload("c", T=290, d=512, f=2048, P=2, act="swiglu", dtype="bf16", seed=21), "tiled", (4, 4)),
+    ("tiled shape 0, 4 tiles", Workload("b", T=513, d=1024, f=4096, P=2, act="swiglu", dtype="bf16", seed=12),
+     "tiled", (0, 0)),
+    ("tiled shape 1", Workload("c", T=290, d=512, f=2048, P=2, act="swiglu", dtype="bf16", seed=21), "tiled", (1, 1)),
+    ("tiled shape 2", Workload("c", T=290, d=512, f=2048, P=2, act="swiglu", dtype="bf16", seed=21), "tiled", (2, 2)),
     ("tiled gelu shape 1/3", Workload("g", T=200, d=256, f=1024, P=2, act="gelu_tanh", dtype="bf16", seed=12),
      "tiled", (1, 3)),
     ("skinny", Workload("k", T=17, d=1024, f=2048, P=4, act="swiglu", dtype="bf16", seed=31, r0=2), "skinny", None),
@@ -99,7 +95,7 @@ def test_backward_with_poisoned_lds(name, w):
     wg = None if inp.w_gate is None else inp.w_gate.to(dev)
     wu, wd = inp.w_up.to(dev), inp.w_down.to(dev)
     mlp = binding.TspMLP(wg, wu, wd, w.P, order=w.order(), act=w.act, T_max=w.T)
-    g = mlp.backward(inp.x.to(dev), dy.to(dev), wg, wu, wd)
+    g = mlp.backward(inp.x.to(dev), dy.to(dev))
     torch.cuda.synchronize()
     mlp.close()
     f = lambda t: None if t is None else t.float().numpy()
@@ -144,4 +140,4 @@ def test_attention_with_poisoned_lds(name, kw):
     f = lambda t: t.float().numpy()
     ref = ao.tsp_attention(f(inp.x_all), f(inp.w_q), f(inp.w_k), f(inp.w_v), f(inp.w_o), w.H, w.Hkv, w.P, w.rank,
                            order=w.order(), causal=w.causal)
-    assert np.linalg.norm(y - ref) / np.linalg.norm(ref) <= 8e-3, name
+    assert np.linalg.norm(y - ref) / np.linalg.norm(ref) <= 3e-3, name

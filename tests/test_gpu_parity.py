@@ -119,10 +119,8 @@ TIGHT = {
     "tiled-gelu": (Workload("g", T=200, d=256, f=1024, P=2, act="gelu_tanh", dtype="bf16", seed=12), "auto", None),
     "tiled-swiglu-shape0": (Workload("t", T=290, d=512, f=2048, P=2, act="swiglu", dtype="bf16", seed=21, r0=1),
                             "tiled", (0, 0)),
-    "tiled-swiglu-shape4": (Workload("t", T=290, d=512, f=2048, P=2, act="swiglu", dtype="bf16", seed=21, r0=1),
-                            "tiled", (4, 4)),
-    "tiled-swiglu-shape6": (Workload("t", T=290, d=512, f=2048, P=2, act="swiglu", dtype="bf16", seed=21, r0=1),
-                            "tiled", (6, 6)),
+    "tiled-swiglu-shape1": (Workload("t", T=290, d=512, f=2048, P=2, act="swiglu", dtype="bf16", seed=21, r0=1),
+                            "tiled", (1, 1)),
     "skinny-swiglu": (Workload("k", T=17, d=1024, f=2048, P=4, act="swiglu", dtype="bf16", seed=31, r0=2),
                       "skinny", None),
     "skinny-gelu": (Workload("k", T=32, d=1024, f=2048, P=4, act="gelu_tanh", dtype="bf16", seed=31),
@@ -146,8 +144,7 @@ def test_tight_parity_with_bf16_hidden(name):
     assert el2 <= BF16_ROUNDED_H_EL2, f"{name}: e_L2 {el2:.3e} against the bf16-H oracle"
 
 
-@pytest.mark.parametrize("gcfg,dcfg", [(0, 0), (1, 1), (2, 2), (3, 3), (4, 4), (5, 5), (6, 6), (0, 3), (3, 0), (4, 0),
-                                       (5, 1), (6, 5), (5, 6)])
+@pytest.mark.parametrize("gcfg,dcfg", [(0, 0), (1, 1), (2, 2), (3, 3), (0, 3), (3, 0), (0, 1), (1, 0), (2, 0)])
 def test_every_tile_shape(gcfg, dcfg):
     w = Workload("t", T=290, d=512, f=2048, P=2, act="swiglu", dtype="bf16", seed=21, r0=1)
     say(f"[gpu] tile shapes gateup={gcfg} down={dcfg}")
@@ -156,7 +153,7 @@ def test_every_tile_shape(gcfg, dcfg):
     check(w, y, ref(w, inp), f"tiles {gcfg}/{dcfg}")
 
 
-@pytest.mark.parametrize("gcfg", [0, 1, 2, 4, 5, 6])
+@pytest.mark.parametrize("gcfg", [0, 1, 2])
 def test_every_tile_shape_gelu(gcfg):
     w = Workload("t", T=130, d=256, f=1024, P=2, act="gelu_tanh", dtype="bf16", seed=22)
     say(f"[gpu] gelu tile shape {gcfg}")
@@ -216,26 +213,8 @@ def test_down_ring_group_split(T, d, f, P, r0):
     check(w, y, ref(w, inp), "split")
     y2, _ = run_gpu(w, inp, reuse=mlp)
     assert np.array_equal(y, y2)
-    y3, _ = run_gpu(w, inp, path="tiled", tiles=(5, 1))
+    y3, _ = run_gpu(w, inp, path="tiled", tiles=(0, 1))
     check(w, y3, ref(w, inp), "unsplit")
-    y4, _ = run_gpu(w, inp, path="tiled", tiles=(6, 6))     # the 4-wave shape splits the same way
-    check(w, y4, ref(w, inp), "split, shape 6")
-
-
-@pytest.mark.parametrize("T,d,f,P,act", [(290, 512, 2048, 2, "swiglu"), (700, 1024, 4096, 4, "swiglu"),
-                                         (130, 256, 1024, 2, "gelu_tanh"), (300, 512, 4096, 8, "swiglu")])
-def test_shape6_matches_shape5_bitwise(T, d, f, P, act):
-    """Shapes 5 and 6 cut the same 256 x 256 tiles and feed each output the
-    same 16x16x32 MFMAs over the same 32-wide reduction steps in the same
-    order (shape 6 starts from the constant 0, shape 5 from registers holding
-    0), so their results are identical bit for bit."""
-    w = Workload("b", T=T, d=d, f=f, P=P, act=act, dtype="bf16", seed=52, r0=1)
-    say(f"[gpu] shape 6 vs 5 T={T} d={d} f={f} P={P} {act}")
-    inp = make_inputs(w)
-    y5, mlp = run_gpu(w, inp, path="tiled", tiles=(5, 5))
-    y6, _ = run_gpu(w, inp, path="tiled", tiles=(6, 6))
-    check(w, y6, ref(w, inp), "shape 6")
-    assert np.array_equal(y5, y6)
 
 
 def test_ring_orders():
@@ -399,7 +378,7 @@ def test_full_decode70b():
 
 
 def test_full_long70b():
-    _full("70b-long-swiglu-bf16-T16384-d8192-f28672-P8", 200)   # includes all 164 outlier rows
+    _full("70b-long-swiglu-bf16-T16384-d8192-f28672-P8", 512)   # all 164 outlier rows + 348 random rows
 
 
 def test_ceiling_probes_are_plausible():
