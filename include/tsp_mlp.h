@@ -122,6 +122,26 @@ tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y,
                              hipStream_t stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward as tsp_mlp_forward, the same kernels and the same results, with its
+ * workspace (hidden activations, down-split partials) in a static device
+ * array of TSP_STATIC_SCRATCH_BYTES bytes per GPU instead of the handle's
+ * workspace. It allocates nothing and records no timing events. T is bounded
+ * by that array, not by T_max: a T whose workspace exceeds it returns
+ * TSP_ERR_UNSUPPORTED before any launch (e.g. up to ~2300 tokens at
+ * f = 14336 bf16, every T <= 48 of the weight-streaming path). Every call on
+ * one GPU shares that GPU's array, which keeps the last call's contents:
+ * calls that overlap in time on one GPU (on different streams or host
+ * threads) race. The array is set up on the first call on each device and
+ * held until the process ends. Arguments and errors otherwise as
+ * tsp_mlp_forward.
+ */
+#define TSP_STATIC_SCRATCH_BYTES (64LL << 20)
+tsp_status_t tsp_mlp_forward_static(tsp_mlp_t h, int64_t T, const void* X, float* Y,
+                                    hipStream_t stream);
+
+/*
  * Backward of the block for an output gradient dY: the gradients of the
  * forward ("Folding Tensor and Sequence Parallelism ...", Abstract: the method
  * is for training; "Tensor Parallelism: Splitting the Math", the paragraph

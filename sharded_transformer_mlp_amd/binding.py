@@ -24,6 +24,7 @@ SIGNATURES = {
     "tsp_mlp_create": (_i32, [ctypes.POINTER(_vp), _i64, _i64, _i64, _i32, _i32, _i32,
                               ctypes.POINTER(_i32), _vp, _vp, _vp, _vp]),
     "tsp_mlp_forward": (_i32, [_vp, _i64, _vp, _vp, _vp]),
+    "tsp_mlp_forward_static": (_i32, [_vp, _i64, _vp, _vp, _vp]),
     "tsp_mlp_backward": (_i32, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "tsp_mlp_destroy": (_i32, [_vp]),
     "tsp_mlp_set_path": (_i32, [_vp, _i32]),

@@ -9,6 +9,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -402,7 +403,57 @@ tsp_status_t tsp_mlp_forward(tsp_mlp_t h, int64_t T, const void* X, float* Y, hi
 
 }  // extern "C"
 
+namespace {
+
+// ---- the allocation-free forward ----------------------------------------
+// Its workspace is this file-scope device array. In host code `scratch` is a
+// host-side stand-in, not a device address: host code uses the address that
+// hipGetSymbolAddress returns for the current device, kept per device.
+constexpr int64_t kStaticScratchBytes = TSP_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on device dev (current), looked up once.
+tsp_status_t scratch_address(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxDevices) return fail(TSP_ERR_UNSUPPORTED, "device %d beyond the scratch table", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return hip_fail(e == hipSuccess ? hipErrorInvalidSymbol : e, "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return TSP_OK;
+}
+
+}  // namespace
+
 extern "C" {
+
+tsp_status_t tsp_mlp_forward_static(tsp_mlp_t h, int64_t T, const void* X, float* Y, hipStream_t stream) {
+    if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
+    if (T < 0) return fail(TSP_ERR_INVALID_ARG, "T=%lld is negative", (long long)T);
+    if (T == 0) return TSP_OK;
+    if (T > kMaxDim) return fail(TSP_ERR_INVALID_ARG, "T=%lld out of range", (long long)T);
+    FwdPlan pl;
+    tsp_status_t s = plan_forward(h, T, pl);
+    if (s != TSP_OK) return s;
+    if (pl.total > kStaticScratchBytes)
+        return fail(TSP_ERR_UNSUPPORTED, "T=%lld needs %lld bytes of workspace; the static scratch holds %lld",
+                    (long long)T, (long long)pl.total, (long long)kStaticScratchBytes);
+    s = check_forward_args(h, T, X, Y);
+    if (s != TSP_OK) return s;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return fail(TSP_ERR_HIP, "cannot select the handle's device");
+    void* work = nullptr;
+    s = scratch_address(h->device, &work);
+    if (s != TSP_OK) return s;
+    return run_forward(h, T, X, Y, stream ? stream : h->stream, pl, work, false);
+}
 
 namespace {
 
