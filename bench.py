@@ -418,6 +418,7 @@ def measure_mlp(w, args, backward: bool = False, with_cpu: bool = False):
     kt = mlp.read_timing()
     kernels = {k: v[0] / max(v[1], 1) for k, v in kt.items()}
     log(f"ms/step {ms:.4f}; kernels {kernels}")
+    log("per-step ms: " + " ".join(f"{p:.3f}" for p in per))
 
     decode = is_decode(w) and not backward
     if backward:
