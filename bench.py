@@ -13,8 +13,8 @@ block (T=4096 tokens, d=4096, f=14336, P=8 shards, ring start 3), reported in
 TFLOP/s; ``--workload decode70b`` runs the T=16 weight-streaming workload,
 reported in GB/s. The ``roofline`` object is for the dominant kernel, timed
 with HIP events recorded by the library on the stream the kernel runs on,
-over a second region of as many steps right after the (event-free) timed
-region.
+over a region of as many steps run just before the warmup and the
+(event-free) timed region.
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 workload on this host's cores. ``--pass backward`` times the backward instead
 (one step = the gradients for a seeded output gradient; TFLOP/s over the
@@ -272,19 +272,8 @@ def bench_attention(args):
     def step():
         attn.forward(x, w.rank, y)
 
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    log(f"timing {args.steps} steps")
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    # kernel-timing pass first (see measure_mlp), then warmup and timed steps
+    log(f"kernel-timing pass, {args.steps} steps")
     attn.read_timing()
     attn.set_timing(True)
     for _ in range(args.steps):
@@ -292,7 +281,10 @@ def bench_attention(args):
     torch.cuda.synchronize()
     attn.set_timing(False)
     kernels = {k: v[0] / max(v[1], 1) for k, v in attn.read_timing().items()}
+    log(f"warmup {args.warmup}, timing {args.steps} steps")
+    ms, per = time_steps(step, args.steps, args.warmup)
     log(f"ms/step {ms:.4f}; kernels {kernels}")
+    log("per-step ms: " + " ".join(f"{p:.3f}" for p in per))
     total = ao.attention_flops(w.T, w.d, w.H, w.Hkv, w.dh, w.P, w.rank, w.causal)
     value = total / (ms * 1e-3) / 1e12
     dom = max(kernels, key=lambda k: kernels[k])
@@ -311,7 +303,7 @@ def bench_attention(args):
                    "P": w.P, "rank": w.rank, "causal": w.causal, "order": w.order(),
                    "parallelism": "one TSP rank (head-group loop on one GPU; other ranks' keys/values "
                                   "projected before timing)"},
-        "pct_of_peak": value / PEAK_BF16_TFLOPS * 100.0,
+        "pct_of_peak": value / PEAK_BF16_TFLOPS * 100.0, **step_stats(per),
         "kernels_ms": kernels, "pack_ms": pack_ms, "roofline": roof, "cpu_baseline": None, "pass": "attention",
         "env": {"gpu": torch.cuda.get_device_name(0), "torch": torch.__version__, "hip": torch.version.hip},
     }
@@ -404,11 +396,13 @@ def measure_mlp(w, args, backward: bool = False, with_cpu: bool = False):
         def step():
             mlp.forward(x, y)
 
-    log(f"warmup {args.warmup}, timing {args.steps} steps")
-    ms, per = time_steps(step, args.steps, args.warmup)
-    # Kernel region: the same number of passes again, with the library
-    # recording HIP events around every kernel on the stream it runs on. The
-    # events cost ~15 us per step, so they stay out of the timed region above.
+    # Kernel region first: as many passes as the timed region, with the
+    # library recording HIP events around every kernel on the stream it runs
+    # on (the events cost ~15 us per step, so they stay out of the timed
+    # region). Running it before the timed region also brings the GPU's clock
+    # out of idle: per-step events show the first ~15 ms of work after idle
+    # running up to 20 % slower, which 5 warmup steps of this block do not cover.
+    log(f"kernel-timing pass, {args.steps} steps")
     mlp.read_timing()
     mlp.set_timing(True)
     for _ in range(args.steps):
@@ -417,6 +411,8 @@ def measure_mlp(w, args, backward: bool = False, with_cpu: bool = False):
     mlp.set_timing(False)
     kt = mlp.read_timing()
     kernels = {k: v[0] / max(v[1], 1) for k, v in kt.items()}
+    log(f"warmup {args.warmup}, timing {args.steps} steps")
+    ms, per = time_steps(step, args.steps, args.warmup)
     log(f"ms/step {ms:.4f}; kernels {kernels}")
     log("per-step ms: " + " ".join(f"{p:.3f}" for p in per))
 
