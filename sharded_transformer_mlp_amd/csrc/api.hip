@@ -247,7 +247,7 @@ tsp_status_t tsp_mlp_create(tsp_mlp_t* out, int64_t T_max, int64_t d, int64_t f,
     // f / 16 fragment blocks of 1 KiB per 32-token block; the larger of the
     // two), then for bf16 the fp32 partials of a ring-group split of the down
     // product (at most 64 MiB, see down_split_bytes)
-    h->work_bytes = T_max * f * es;
+    h->work_bytes = (T_max + 15) / 16 * 16 * f * es;     // whole 16-token blocks of H
     if (dtype == TSP_DTYPE_BF16) {
         const int64_t ntb = ((T_max < tsp::SKINNY_T_MAX ? T_max : tsp::SKINNY_T_MAX) + 31) / 32;
         if (ntb * 32 * f * 2 > h->work_bytes) h->work_bytes = ntb * 32 * f * 2;
@@ -289,7 +289,7 @@ namespace {
 // forward will take.
 struct FwdPlan {
     bool skinny = false;
-    int cg = -1, cd = -1, split = 1;
+    int cg = -1, cd = -1, split = 1, nbt = 0;
     int64_t h_bytes = 0, part_off = 0, total = 0;
 };
 
@@ -313,7 +313,10 @@ tsp_status_t plan_forward(const tsp_mlp* h, int64_t T, FwdPlan& pl) {
             pl.split = tsp::choose_down_split((int)T, (int)d, h->P, pl.cd);
             const int64_t n_tok_tiles = (T + 63) / 64;
             if (n_tok_tiles * (2 * f / 64 + d / 64) > INT32_MAX / 2) return fail(TSP_ERR_UNSUPPORTED, "grid too large");
-            pl.h_bytes = T * f * 2;
+            // blocked H (both products on the 256 x 256 kernels) fills whole
+            // 16-token blocks
+            pl.nbt = (pl.cg == 0 && pl.cd == 0) ? (int)((T + 15) / 16) : 0;
+            pl.h_bytes = (T + 15) / 16 * 16 * f * 2;
         }
     } else {
         if (h->path == TSP_PATH_SKINNY) return fail(TSP_ERR_UNSUPPORTED, "skinny path is bf16 only");
@@ -355,6 +358,7 @@ tsp_status_t run_forward(tsp_mlp* h, int64_t T, const void* X, float* Y, hipStre
         a.down_off = h->down_off;
         a.T = (int)T; a.d = (int)h->d; a.f = (int)h->f; a.F = (int)h->F; a.P = h->P;
         a.swiglu = swiglu ? 1 : 0;
+        a.nbt = pl.nbt;
         if (pl.skinny) {
             s = timed_launch(h, "skinny_gateup", st, [&] { return tsp::launch_gateup_skinny(a, st); });
             if (s != TSP_OK) return s;

@@ -391,7 +391,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
 // registers, and of a persistent grid that streams the next tile's first
 // stages during the epilogue.
 
-template <int ACT, bool BUF>
+template <int ACT, bool BUF, bool BLK>
 __global__ __launch_bounds__(256) void gateup_w16(Bf16Args a, int n_ft_shard, int n_tt) {
     using namespace w16;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
@@ -434,7 +434,8 @@ __global__ __launch_bounds__(256) void gateup_w16(Bf16Args a, int n_ft_shard, in
             }
         lgkm_zero();
         stage_barrier();
-        stg.flush(a.h, a.f, t0, a.T, (int64_t)s * a.F + ftile * (BM / 2), w, lane);
+        if constexpr (BLK) stg.flush_blocks(a.h, a.nbt, t0, ((int64_t)s * a.F + ftile * (BM / 2)) >> 5, w, lane);
+        else stg.flush(a.h, a.f, t0, a.T, (int64_t)s * a.F + ftile * (BM / 2), w, lane);
     } else {
         StagedRows16<BM> stg{lds};
 #pragma unroll
@@ -449,10 +450,12 @@ __global__ __launch_bounds__(256) void gateup_w16(Bf16Args a, int n_ft_shard, in
         }
         lgkm_zero();
         stage_barrier();
-        stg.flush(a.h, a.f, t0, a.T, (int64_t)s * a.F + ftile * BM, w, lane);
+        if constexpr (BLK) stg.flush_blocks(a.h, a.nbt, t0, ((int64_t)s * a.F + ftile * BM) >> 5, w, lane);
+        else stg.flush(a.h, a.f, t0, a.T, (int64_t)s * a.F + ftile * BM, w, lane);
     }
 }
 
+template <bool BLK>
 __global__ __launch_bounds__(256) void down_w16(Bf16Args a, int n_ft, int n_tt, int split) {
     using namespace w16;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
@@ -467,13 +470,16 @@ __global__ __launch_bounds__(256) void down_w16(Bf16Args a, int n_ft, int n_tt, 
     const int64_t a_rs = (int64_t)(a.F >> 4) * 512;
     const uint16_t* a_ft = a.packed + a.down_off + (int64_t)(g * steps_per_group) * a.shard_elems +
                            (int64_t)(ftile * (BM / 32)) * a_rs;
-    const uint16_t* h_g = a.h + (int64_t)(g * steps_per_group) * a.F;
+    // the group's first hidden column: row-major, or its column block (BLK)
+    const uint16_t* h_g = BLK ? a.h + (int64_t)(g * steps_per_group) * spp * a.nbt * 512
+                              : a.h + (int64_t)(g * steps_per_group) * a.F;
     float* y = split > 1 ? a.part + (int64_t)g * a.T * a.d : a.y;
     const int t0 = ttile * BN;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w / WN, wn = w % WN;
-    PackedSrc<false> src{a_ft, 0, 0, steps_per_group * spp, spp, a.shard_elems, a_rs, h_g, a.f, t0, a.T,
-                         __builtin_amdgcn_readfirstlane(w), wm, wn, lane};
+    PackedSrc<false, BLK> src{a_ft, 0, 0, steps_per_group * spp, spp, a.shard_elems, a_rs, h_g, a.f, t0, a.T,
+                              __builtin_amdgcn_readfirstlane(w), wm, wn, lane};
+    src.nbt = a.nbt;
     f32x4 acc[TM][TN];
     w16::mainloop5(lds, acc, steps_per_group * spp, src);
 
@@ -614,18 +620,21 @@ hipError_t launch_gateup_tiled(const Bf16Args& a, int cfg, hipStream_t st) {
             // buffer offsets are 32-bit: X (T x d bf16) and one stage's weight
             // slab (8 rows of 32 x d-element blocks) must each span < 2^31 bytes
             const bool buf = (int64_t)a.T * a.d * 2 < (int64_t(1) << 31) && (int64_t)a.d * 512 < (int64_t(1) << 31);
+            const bool blk = a.nbt > 0;
+#define TSP_GU(ACT, BUF, BLK) hipLaunchKernelGGL((gateup_w16<ACT, BUF, BLK>), grid, dim3(256), 0, st, a, n_ft_shard, n_tt)
             if (a.swiglu) {
-                if (buf) hipLaunchKernelGGL((gateup_w16<1, true>), grid, dim3(256), 0, st, a, n_ft_shard, n_tt);
-                else hipLaunchKernelGGL((gateup_w16<1, false>), grid, dim3(256), 0, st, a, n_ft_shard, n_tt);
+                if (buf) { if (blk) TSP_GU(1, true, true); else TSP_GU(1, true, false); }
+                else { if (blk) TSP_GU(1, false, true); else TSP_GU(1, false, false); }
             } else {
-                if (buf) hipLaunchKernelGGL((gateup_w16<2, true>), grid, dim3(256), 0, st, a, n_ft_shard, n_tt);
-                else hipLaunchKernelGGL((gateup_w16<2, false>), grid, dim3(256), 0, st, a, n_ft_shard, n_tt);
+                if (buf) { if (blk) TSP_GU(2, true, true); else TSP_GU(2, true, false); }
+                else { if (blk) TSP_GU(2, false, true); else TSP_GU(2, false, false); }
             }
+#undef TSP_GU
             return hipGetLastError();
         }
-        case 1: return gateup_go<256, 128, 4, 2>(a, st);
-        case 2: return gateup_go<128, 128, 2, 2>(a, st);
-        case 3: return gateup_go<64, 128, 1, 4>(a, st);
+        case 1: if (a.nbt) return hipErrorInvalidValue; return gateup_go<256, 128, 4, 2>(a, st);
+        case 2: if (a.nbt) return hipErrorInvalidValue; return gateup_go<128, 128, 2, 2>(a, st);
+        case 3: if (a.nbt) return hipErrorInvalidValue; return gateup_go<64, 128, 1, 4>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -635,13 +644,14 @@ hipError_t launch_down_tiled(const Bf16Args& a, int cfg, int split, hipStream_t 
     switch (cfg) {
         case 0: {
             const int n_ft = a.d / 256, n_tt = (int)cdiv(a.T, 256);
-            hipLaunchKernelGGL(down_w16, dim3((unsigned)(n_ft * n_tt * split)), dim3(256), 0, st, a, n_ft, n_tt,
-                               split);
+            const dim3 grid((unsigned)(n_ft * n_tt * split));
+            if (a.nbt) hipLaunchKernelGGL(down_w16<true>, grid, dim3(256), 0, st, a, n_ft, n_tt, split);
+            else hipLaunchKernelGGL(down_w16<false>, grid, dim3(256), 0, st, a, n_ft, n_tt, split);
             return hipGetLastError();
         }
-        case 1: return down_go<256, 128, 4, 2>(a, st);
-        case 2: return down_go<128, 128, 2, 2>(a, st);
-        case 3: return down_go<64, 128, 1, 4>(a, st);
+        case 1: if (a.nbt) return hipErrorInvalidValue; return down_go<256, 128, 4, 2>(a, st);
+        case 2: if (a.nbt) return hipErrorInvalidValue; return down_go<128, 128, 2, 2>(a, st);
+        case 3: if (a.nbt) return hipErrorInvalidValue; return down_go<64, 128, 1, 4>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

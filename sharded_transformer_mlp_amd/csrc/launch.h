@@ -19,6 +19,11 @@ struct Bf16Args {
     int64_t down_off;         // offset of the down part inside a record
     int T, d, f, F, P;
     int swiglu;
+    // H in 16-token x 32-column blocks (1 KiB, row-major inside), block
+    // (column block kb, token block tb) at (kb * nbt + tb) * 512 elements, with
+    // nbt = ceil(T / 16); 0 = H row-major T x f. Only the 256 x 256 kernels
+    // (tile shape 0 for both products) take the blocked layout.
+    int nbt = 0;
 };
 
 struct F32Args {

@@ -146,7 +146,7 @@ __device__ __forceinline__ bf16x8 read_rows128(const uint16_t* super, int blk, i
 // stage's 256 rows are 8 blocks of 32 rows, each two 1 KiB blocks deep), B =
 // token rows (T x ldb row-major). spp > 0 (down product): the reduction walks
 // shard records, spp steps each, a_rec elements apart.
-template <bool BUF>
+template <bool BUF, bool BLK = false>
 struct PackedSrc {
     const uint16_t* a;                                  // A slab of the current stage
     int tl, ls;                                         // A stage index, step inside the record
@@ -180,12 +180,23 @@ struct PackedSrc {
         load_rows128<BUF>(lds_super + r0 * 64, b_src + (int64_t)sb * 64, ldb, t0 + r0, T - 1, lane);
     }
     __device__ void advance_b() { sb += 2 * (sb + 1) < ksteps ? 1 : 0; }
-    // 32-deep B stages of the 5-stage ring (mainloop5): 16-row x 64-byte pieces
-    // at the A stage's reduction offset (the two operands advance together
-    // there, advance_a moves both)
+    int nbt = 0;                                        // BLK: 16-token blocks per 32-column block
+    // 32-deep B stages of the 5-stage ring (mainloop5), at the A stage's
+    // reduction offset (the two operands advance together there, advance_a
+    // moves both): 16-row x 64-byte pieces of row-major B, or (BLK) B stored
+    // in 16-token x 32-column blocks of 1 KiB (see Bf16Args::nbt), one
+    // contiguous block per load; token blocks past the last are clamped to it
+    // (their rows belong to tokens >= T, never stored)
     __device__ void issue_b32(int g, uint16_t* lds_blocks) {
         const int bb = g * NW + w;
-        load_rows<BUF>(lds_blocks + bb * 512, b_src + (int64_t)tl * 32, ldb, t0 + bb * 16, T - 1, lane);
+        if constexpr (BLK) {
+            const int tb = min((t0 >> 4) + bb, nbt - 1);
+            const int rr = lane >> 2, c = (lane & 3) ^ ((rr >> 1) & 3);   // slot = lane = b_slot(rr, c)
+            const uint16_t* blk = b_src + ((int64_t)tl * nbt + tb) * 512;
+            __builtin_amdgcn_global_load_lds(blk + (rr * 4 + c) * 8, (TSP_LDS void*)(lds_blocks + bb * 512), 16, 0, 0);
+        } else {
+            load_rows<BUF>(lds_blocks + bb * 512, b_src + (int64_t)tl * 32, ldb, t0 + bb * 16, T - 1, lane);
+        }
     }
     // A fragment q: 16-row block ib = rows 16 (ib % 2) + l % 16 of 32-row block
     // ib / 2, reduction indices 8 (l / 16) .. + 7 (two 1 KiB blocks deep).
@@ -525,6 +536,23 @@ struct StagedRows16 {
     uint16_t* lds;
     __device__ __forceinline__ void put4(int r, int c, uint2 v) {
         *reinterpret_cast<uint2*>(lds + r * PITCH + c) = v;
+    }
+    // The staged 256-row tile into H's 16-token x 32-column blocks (see
+    // Bf16Args::nbt): one whole 1 KiB block per store instruction; the tile's
+    // columns start at column block kb0; token blocks past nbt are skipped.
+    __device__ __forceinline__ void flush_blocks(uint16_t* __restrict__ dst, int nbt, int t0, int64_t kb0, int w,
+                                                 int lane) const {
+        static_assert(ROWS == 256 && COLS % 32 == 0, "blocked flush");
+        constexpr int NCB = COLS / 32, NBLK = (ROWS / 16) * NCB;
+        const int r = lane >> 2, c = lane & 3;
+#pragma unroll 4
+        for (int it = 0; it < NBLK / 4; ++it) {
+            const int blk = it * 4 + w;
+            const int i = blk % (ROWS / 16), j = blk / (ROWS / 16);   // token block, column block
+            const int tb = (t0 >> 4) + i;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(lds + (i * 16 + r) * PITCH + j * 32 + c * 8);
+            if (tb < nbt) *reinterpret_cast<u32x4*>(dst + ((kb0 + j) * nbt + tb) * 512 + lane * 8) = v;
+        }
     }
     __device__ __forceinline__ void flush(uint16_t* __restrict__ dst, int64_t ld, int t0, int T, int64_t col0,
                                           int w, int lane, int hh = 0) {
