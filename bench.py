@@ -402,6 +402,9 @@ def measure_mlp(w, args, backward: bool = False, with_cpu: bool = False):
     # region). Running it before the timed region also brings the GPU's clock
     # out of idle: per-step events show the first ~15 ms of work after idle
     # running up to 20 % slower, which 5 warmup steps of this block do not cover.
+    if backward:
+        step()      # the first backward allocates its workspace and unpacks the handle's weights, once
+        torch.cuda.synchronize()
     log(f"kernel-timing pass, {args.steps} steps")
     mlp.read_timing()
     mlp.set_timing(True)

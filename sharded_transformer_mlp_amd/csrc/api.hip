@@ -462,11 +462,12 @@ tsp_status_t tsp_mlp_forward_static(tsp_mlp_t h, int64_t T, const void* X, float
 namespace {
 
 // Backward workspace, regions in bytes for T_max tokens (each 256-aligned):
-// transposed X and dY (d x Tp), dH (T x f fp32), dG, dU, H (T x f bf16) and
-// their transposes (f x Tp), Tp = T_max rounded up to 64; then the weights
-// (bf16, row-major Wg, Wu d x f and Wd f x d) unpacked from the records.
+// transposed X and dY (d x Tp), dH (T x f fp32), dG and dU (T x f bf16, for
+// dX), dG, dU and H transposed (f x Tp, for the weight gradients), Tp = T_max
+// rounded up to 64; then the weights (bf16, row-major Wg, Wu d x f and Wd
+// f x d) unpacked from the records.
 struct BwdLayout {
-    int64_t xt, dyt, dh, dg, du, hb, dgt, dut, ht, wg, wu, wd, total;
+    int64_t xt, dyt, dh, dg, du, dgt, dut, ht, wg, wu, wd, total;
 };
 
 BwdLayout bwd_layout(int64_t T_max, int64_t d, int64_t f) {
@@ -479,7 +480,6 @@ BwdLayout bwd_layout(int64_t T_max, int64_t d, int64_t f) {
     L.dh = o; o += up(T_max * f * 4);
     L.dg = o; o += up(T_max * f * 2);
     L.du = o; o += up(T_max * f * 2);
-    L.hb = o; o += up(T_max * f * 2);
     L.dgt = o; o += up(f * Tp * 2);
     L.dut = o; o += up(f * Tp * 2);
     L.ht = o; o += up(f * Tp * 2);
@@ -540,7 +540,7 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
     }
     char* wsp = static_cast<char*>(h->bwd);
     auto bf = [&](int64_t off) { return reinterpret_cast<uint16_t*>(wsp + off); };
-    uint16_t *xt = bf(L.xt), *dyt = bf(L.dyt), *dg = bf(L.dg), *du = bf(L.du), *hb = bf(L.hb);
+    uint16_t *xt = bf(L.xt), *dyt = bf(L.dyt), *dg = bf(L.dg), *du = bf(L.du);
     uint16_t *dgt = bf(L.dgt), *dut = bf(L.dut), *ht = bf(L.ht);
     float* dh = reinterpret_cast<float*>(wsp + L.dh);
     const int Tp = (int)((T + 63) / 64 * 64);
@@ -583,15 +583,8 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
     a.down_off = h->down_off;
     a.T = (int)T; a.d = (int)d; a.f = (int)f; a.F = F; a.P = P;
     a.swiglu = swiglu ? 1 : 0;
-    tsp::BwdArgs b{dh, dg, du, hb, h->order_dev};
+    tsp::BwdArgs b{dh, dg, du, dgt, dut, ht, Tp, h->order_dev};
     s = timed_launch(h, "bwd_gateup", st, [&] { return tsp::launch_gateup_bwd(a, b, st); });
-    if (s != TSP_OK) return s;
-    s = timed_launch(h, "bwd_transpose_mid", st, [&] {
-        hipError_t e = hipSuccess;
-        if (swiglu) e = tsp::launch_transpose_bf16(dg, (int)T, (int)f, (int)f, dgt, Tp, st);
-        if (e == hipSuccess) e = tsp::launch_transpose_bf16(du, (int)T, (int)f, (int)f, dut, Tp, st);
-        return e != hipSuccess ? e : tsp::launch_transpose_bf16(hb, (int)T, (int)f, (int)f, ht, Tp, st);
-    });
     if (s != TSP_OK) return s;
     // dX[t][i] = sum over ring steps k of dG_k[t] . Wg[i][order[k] F ..] + dU_k[t] . Wu[i][..]
     tsp::NtArgs q{};

@@ -240,9 +240,15 @@ __global__ __launch_bounds__(256) void gateup_bwd_w16(Bf16Args a, BwdArgs b, int
         }
         lgkm_zero();
         stage_barrier();
-        if constexpr (ACT == 1) sg_.flush(b.dg, a.f, t0, a.T, ring0, w, lane, hh);
+        // dG and dU row-major for dX, and dG, dU, H transposed (tokens
+        // contiguous) for the weight gradients, which reduce over tokens
+        if constexpr (ACT == 1) {
+            sg_.flush(b.dg, a.f, t0, a.T, ring0, w, lane, hh);
+            flush_transposed(sg_, b.dgt, b.ldt, ring0, t0, hh, (int)threadIdx.x);
+        }
         su.flush(b.du, a.f, t0, a.T, ring0, w, lane, hh);
-        sh.flush(b.h, a.f, t0, a.T, ring0, w, lane, hh);
+        flush_transposed(su, b.dut, b.ldt, ring0, t0, hh, (int)threadIdx.x);
+        flush_transposed(sh, b.ht, b.ldt, ring0, t0, hh, (int)threadIdx.x);
         lgkm_zero();
     }
 }

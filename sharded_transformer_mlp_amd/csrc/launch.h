@@ -94,7 +94,10 @@ struct BwdArgs {
     const float* dh;          // T x f fp32, natural hidden columns
     uint16_t* dg;             // T x f bf16, ring-ordered hidden columns (SwiGLU only)
     uint16_t* du;             // T x f bf16, ring-ordered
-    uint16_t* h;              // T x f bf16, ring-ordered
+    uint16_t* dgt;            // the same transposed: f x ldt, tokens contiguous (SwiGLU only)
+    uint16_t* dut;            // f x ldt
+    uint16_t* ht;             // H transposed, f x ldt (H itself is not needed row-major)
+    int ldt;                  // T rounded up to 64; columns T..ldt-1 hold finite values
     const int32_t* order;     // ring order (device)
 };
 hipError_t launch_transpose_bf16(const uint16_t* src, int R, int C, int ld_src, uint16_t* dst, int R_pad,

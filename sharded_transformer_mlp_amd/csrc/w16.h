@@ -180,6 +180,7 @@ struct PackedSrc {
         load_rows128<BUF>(lds_super + r0 * 64, b_src + (int64_t)sb * 64, ldb, t0 + r0, T - 1, lane);
     }
     __device__ void advance_b() { sb += 2 * (sb + 1) < ksteps ? 1 : 0; }
+    __device__ void advance5() { advance_a(); }        // the 5-stage ring: B follows A's stage index
     int nbt = 0;                                        // BLK: 16-token blocks per 32-column block
     // 32-deep B stages of the 5-stage ring (mainloop5), at the A stage's
     // reduction offset (the two operands advance together there, advance_a
@@ -468,7 +469,7 @@ __device__ __forceinline__ void step5(int& ld_ref, int& rd_ref, Src& src, uint16
         mf(m0 + 6);
         __builtin_amdgcn_sched_barrier(0);
     }
-    src.advance_a();
+    src.advance5();
     ld_ref = rd_off;
     rd_ref = next5(rd_off);
 #pragma unroll
@@ -496,7 +497,7 @@ __device__ __forceinline__ void mainloop5(uint16_t* lds, f32x4 (&acc)[TM][TN], i
         for (int g = 0; g < LA; ++g) src.issue_a(g, lds + t * R5_STAGE);
 #pragma unroll
         for (int g = 0; g < LOADS - LA; ++g) src.issue_b32(g, lds + t * R5_STAGE + A_STAGE);
-        src.advance_a();
+        src.advance5();
     }
     TSP_VMCNT((NS5 - 1) * LOADS);                       // own loads of stage 0 landed
     stage_barrier();
@@ -569,6 +570,34 @@ struct StagedRows16 {
         }
     }
 };
+
+// Half hh of a StagedRows16<COLS, 128> tile, transposed, into dst (COLS rows
+// of ldt tokens, tokens contiguous) at rows row0 + c and the half's token
+// columns: staged row r is tile row (r / 64) * 128 + hh * 64 + r % 64. Four
+// lanes take one column, each 8 consecutive tokens (8 LDS reads of 2 bytes:
+// for a given read the wave touches 16 neighbouring columns of 4 rows, few
+// bank conflicts), and store them as 16 bytes, so that a store instruction
+// writes 64 contiguous bytes of each of 16 rows; columns t0 + tile row >= ldt
+// are skipped.
+template <int COLS>
+__device__ __forceinline__ void flush_transposed(const StagedRows16<COLS, 128>& stg, uint16_t* __restrict__ dst,
+                                                 int64_t ldt, int64_t row0, int t0, int hh, int tid) {
+    constexpr int PITCH = StagedRows16<COLS, 128>::PITCH;
+    // a 4-lane group covers 32 tokens of one column; 4 such token quarters
+    // per staged half, 16 columns per wave per pass
+#pragma unroll 2
+    for (int it = 0; it < COLS / 16; ++it) {
+        const int id = it * 256 + tid;
+        const int q = id & 3, c = (id >> 2) & (COLS - 1), tq = id / (4 * COLS);   // tq: which 32 tokens
+        const int r = tq * 32 + q * 8;                      // first staged row of the lane's 8 tokens
+        const int col = t0 + (r >> 6) * 128 + hh * 64 + (r & 63);
+        uint32_t v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            v[e] = (uint32_t)stg.lds[(r + 2 * e) * PITCH + c] | ((uint32_t)stg.lds[(r + 2 * e + 1) * PITCH + c] << 16);
+        if (col < ldt) *reinterpret_cast<u32x4*>(dst + (row0 + c) * ldt + col) = u32x4{v[0], v[1], v[2], v[3]};
+    }
+}
 
 // The fp32 counterpart for 256-column result tiles: 128 staged rows, one half
 // hh of each wave row's tokens (as StagedRows16<COLS, 128>), 1 KiB per row so
