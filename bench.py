@@ -11,10 +11,11 @@ Inputs, packed weights and workspace are resident in HBM before timing.
 Prints one JSON line. The default workload is the Llama-3-8B-shaped SwiGLU
 block (T=4096 tokens, d=4096, f=14336, P=8 shards, ring start 3), reported in
 TFLOP/s; ``--workload decode70b`` runs the T=16 weight-streaming workload,
-reported in GB/s. The ``roofline`` object is for the dominant kernel, timed
-with HIP events recorded by the library on the stream the kernel runs on,
-over a region of as many steps run just before the warmup and the
-(event-free) timed region.
+reported in GB/s. An untimed clock pre-heat (~0.1 s of steps) comes before
+the warmup. The ``roofline`` object is for the dominant kernel, timed with
+fence-free HIP events that the library records around every kernel on the
+stream the kernel runs on, over a region of as many steps right after the
+timed region (which has events only at step boundaries).
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 workload on this host's cores. ``--pass backward`` times the backward instead
 (one step = the gradients for a seeded output gradient; TFLOP/s over the
@@ -272,8 +273,11 @@ def bench_attention(args):
     def step():
         attn.forward(x, w.rank, y)
 
-    # kernel-timing pass first (see measure_mlp), then warmup and timed steps
-    log(f"kernel-timing pass, {args.steps} steps")
+    # pre-heat, warmup, timed region, then the kernel region (see measure_mlp)
+    n_pre = preheat(step)
+    log(f"pre-heat {n_pre} steps; warmup {args.warmup}, timing {args.steps} steps")
+    ms, per = time_steps(step, args.steps, args.warmup)
+    log(f"kernel-timing region, {args.steps} steps")
     attn.read_timing()
     attn.set_timing(True)
     for _ in range(args.steps):
@@ -281,8 +285,6 @@ def bench_attention(args):
     torch.cuda.synchronize()
     attn.set_timing(False)
     kernels = {k: v[0] / max(v[1], 1) for k, v in attn.read_timing().items()}
-    log(f"warmup {args.warmup}, timing {args.steps} steps")
-    ms, per = time_steps(step, args.steps, args.warmup)
     log(f"ms/step {ms:.4f}; kernels {kernels}")
     log("per-step ms: " + " ".join(f"{p:.3f}" for p in per))
     total = ao.attention_flops(w.T, w.d, w.H, w.Hkv, w.dh, w.P, w.rank, w.causal)
@@ -329,24 +331,98 @@ def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):
     log(f"copy calibration: {reps} copies of {nbytes} bytes")
 
 
+class HipEvents:
+    """Timing events on a HIP stream, created through the HIP runtime that
+    torch has loaded, with hipEventDisableSystemFence: a timing-only event
+    then skips the system-scope release (a cache writeback and invalidation
+    at every step boundary, which slows the next step's first kernel)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n: int, stream_handle: int):
+        import ctypes
+        import torch
+        torch.cuda.init()
+        path = None
+        with open("/proc/self/maps") as fh:
+            for line in fh:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded")
+        self.c = ctypes
+        hip = ctypes.CDLL(path)
+        vp = ctypes.c_void_p
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [vp, vp]
+        hip.hipEventSynchronize.argtypes = [vp]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        hip.hipEventDestroy.argtypes = [vp]
+        self.hip, self.stream = hip, vp(stream_handle)
+        self.ev = []
+        for _ in range(n):
+            e = vp()
+            self._ok(hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE), "create")
+            self.ev.append(e)
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"hipEvent {what} failed: {rc}")
+
+    def record(self, i: int):
+        self._ok(self.hip.hipEventRecord(self.ev[i], self.stream), "record")
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        self._ok(self.hip.hipEventSynchronize(self.ev[j]), "synchronize")
+        t = self.c.c_float()
+        self._ok(self.hip.hipEventElapsedTime(self.c.byref(t), self.ev[i], self.ev[j]), "elapsed")
+        return t.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
+
+
+def preheat(step, seconds: float = 0.1) -> int:
+    """Untimed steps for about `seconds` before the warmup: the GPU's clock
+    takes ~15 ms of work to come out of idle. Returns the step count."""
+    import torch
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    one = max(time.perf_counter() - t, 1e-5)
+    n = max(0, min(2000, int(seconds / one)))
+    for _ in range(n):
+        step()
+    torch.cuda.synchronize()
+    return n + 1
+
+
 def time_steps(step, steps: int, warmup: int):
     """W untimed warmup steps, then exactly `steps` steps between two device
-    synchronisations, with an event at every step boundary on the stream the
-    steps run on. Returns (ms per step over the whole region, per-step ms)."""
+    synchronisations, with a (fence-free) event at every step boundary on the
+    stream the steps run on. Returns (ms per step over the whole region,
+    per-step ms)."""
     import torch
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    torch.cuda.synchronize()
-    evs[0].record(stream)
-    for i in range(steps):
-        step()
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
-    return evs[0].elapsed_time(evs[steps]) / steps, per
+    evs = HipEvents(steps + 1, torch.cuda.current_stream().cuda_stream)
+    try:
+        torch.cuda.synchronize()
+        evs.record(0)
+        for i in range(steps):
+            step()
+            evs.record(i + 1)
+        torch.cuda.synchronize()
+        per = [evs.elapsed_ms(i, i + 1) for i in range(steps)]
+        total = evs.elapsed_ms(0, steps)
+    finally:
+        evs.close()
+    return total / steps, per
 
 
 def step_stats(per):
@@ -396,16 +472,16 @@ def measure_mlp(w, args, backward: bool = False, with_cpu: bool = False):
         def step():
             mlp.forward(x, y)
 
-    # Kernel region first: as many passes as the timed region, with the
-    # library recording HIP events around every kernel on the stream it runs
-    # on (the events cost ~15 us per step, so they stay out of the timed
-    # region). Running it before the timed region also brings the GPU's clock
-    # out of idle: per-step events show the first ~15 ms of work after idle
-    # running up to 20 % slower, which 5 warmup steps of this block do not cover.
-    if backward:
-        step()      # the first backward allocates its workspace and unpacks the handle's weights, once
-        torch.cuda.synchronize()
-    log(f"kernel-timing pass, {args.steps} steps")
+    # Untimed clock pre-heat (~0.1 s of steps; the first backward also
+    # allocates its workspace and unpacks the handle's weights), the W warmup
+    # steps, the timed region (the headline), then a kernel region of as many
+    # steps with the library recording fence-free HIP events around every
+    # kernel on the stream it runs on (~5 us per step for a two-kernel step:
+    # 2 % of a decode step, which is why it is a region of its own).
+    n_pre = preheat(step)
+    log(f"pre-heat {n_pre} steps; warmup {args.warmup}, timing {args.steps} steps")
+    ms, per = time_steps(step, args.steps, args.warmup)
+    log(f"kernel-timing region, {args.steps} steps")
     mlp.read_timing()
     mlp.set_timing(True)
     for _ in range(args.steps):
@@ -414,8 +490,6 @@ def measure_mlp(w, args, backward: bool = False, with_cpu: bool = False):
     mlp.set_timing(False)
     kt = mlp.read_timing()
     kernels = {k: v[0] / max(v[1], 1) for k, v in kt.items()}
-    log(f"warmup {args.warmup}, timing {args.steps} steps")
-    ms, per = time_steps(step, args.steps, args.warmup)
     log(f"ms/step {ms:.4f}; kernels {kernels}")
     log("per-step ms: " + " ".join(f"{p:.3f}" for p in per))
 

@@ -107,9 +107,11 @@ tsp_status_t timed_launch(tsp_mlp* h, const char* name, hipStream_t st, Fn&& lau
     if (h->timing) {
         if (h->used == h->pool.size()) {
             if (h->pool.size() < (size_t)kMaxTimingPairs) {
+                // timing-only events: no system-scope fence (its cache
+                // writeback and invalidation would slow the next kernel)
                 EventPair e;
-                hipError_t err = hipEventCreate(&e.start);
-                if (err == hipSuccess) err = hipEventCreate(&e.stop);
+                hipError_t err = hipEventCreateWithFlags(&e.start, hipEventDisableSystemFence);
+                if (err == hipSuccess) err = hipEventCreateWithFlags(&e.stop, hipEventDisableSystemFence);
                 if (err != hipSuccess) return hip_fail(err, "hipEventCreate");
                 h->pool.push_back(e);
             } else {
@@ -948,8 +950,8 @@ namespace {
 template <class Fn>
 tsp_status_t time_probe(hipStream_t st, int reps, Fn&& launch, double* ms) {
     hipEvent_t e0 = nullptr, e1 = nullptr;
-    hipError_t err = hipEventCreate(&e0);
-    if (err == hipSuccess) err = hipEventCreate(&e1);
+    hipError_t err = hipEventCreateWithFlags(&e0, hipEventDisableSystemFence);
+    if (err == hipSuccess) err = hipEventCreateWithFlags(&e1, hipEventDisableSystemFence);
     if (err == hipSuccess) err = launch();
     if (err == hipSuccess) err = hipEventRecord(e0, st);
     for (int r = 0; r < reps && err == hipSuccess; ++r) err = launch();
