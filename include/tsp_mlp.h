@@ -154,9 +154,10 @@ tsp_status_t tsp_mlp_forward_static(tsp_mlp_t h, int64_t T, const void* X, float
  *   dW_down[s, :] = H_s^T . dY           (each shard's own blocks),
  * with G_s, U_s, H_s recomputed from X and the handle's packed weights.
  * Every weight the backward reads comes from the handle: the products with dY
- * and with dG / dU read a row-major copy that the first backward call unpacks
- * from the packed records (bit-exact) into the backward workspace, so the
- * gradients always belong to the weights the handle was created with.
+ * and with dG / dU read copies that the first backward call unpacks from the
+ * packed records (bit-exact) into the backward workspace (Wd row-major, Wg
+ * and Wu in the records' fragment-block format transposed), so the gradients
+ * always belong to the weights the handle was created with.
  * bf16 handles only (TSP_ERR_UNSUPPORTED for fp32), and d % 256 == 0 and
  * F % 256 == 0 (TSP_ERR_UNSUPPORTED otherwise).
  * X, dY: device, T x d row-major bf16. Outputs, device, fp32, overwritten:

@@ -469,7 +469,7 @@ namespace {
 // rounded up to 64; then the weights (bf16, row-major Wg, Wu d x f and Wd
 // f x d) unpacked from the records.
 struct BwdLayout {
-    int64_t xt, dyt, dh, dg, du, dgt, dut, ht, wg, wu, wd, total;
+    int64_t xt, dyt, dh, dg, du, dgt, dut, ht, wg, wu, wd, wgf, wuf, total;
 };
 
 BwdLayout bwd_layout(int64_t T_max, int64_t d, int64_t f) {
@@ -488,6 +488,8 @@ BwdLayout bwd_layout(int64_t T_max, int64_t d, int64_t f) {
     L.wg = o; o += up(d * f * 2);                   // row-major weights unpacked from the records
     L.wu = o; o += up(d * f * 2);
     L.wd = o; o += up(f * d * 2);
+    L.wgf = o; o += up(d * f * 2);                  // Wg, Wu again in fragment blocks (rows d, reduction f)
+    L.wuf = o; o += up(d * f * 2);
     L.total = o;
     return L;
 }
@@ -549,23 +551,27 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
     const int F = (int)h->F, P = h->P;
     const auto* x16 = static_cast<const uint16_t*>(X);
     const auto* dy16 = static_cast<const uint16_t*>(dY);
-    const uint16_t* wg16 = swiglu ? bf(L.wg) : nullptr;
-    const uint16_t* wu16 = bf(L.wu);
+    const uint16_t* wgf = swiglu ? bf(L.wgf) : nullptr;
+    const uint16_t* wuf = bf(L.wuf);
     const uint16_t* wd16 = bf(L.wd);
     if (!h->bwd_unpacked) {
-        // the handle's weights in the row-major layout the dY and dG / dU
-        // products read, once per handle (the records never change)
+        // the handle's weights in the layouts the dY and dG / dU products
+        // read, once per handle (the records never change): row-major Wd (dH),
+        // and Wg, Wu in fragment blocks (dX) by way of row-major copies
         tsp_status_t su = timed_launch(h, "bwd_unpack", st, [&] {
-            return tsp::launch_unpack_bf16(h->packed, bf(L.wg), bf(L.wu), bf(L.wd), h->order_dev, h->shard_elems,
-                                           h->down_off, (int)d, (int)f, (int)h->F, h->P, swiglu ? 1 : 0, st);
+            hipError_t e = tsp::launch_unpack_bf16(h->packed, bf(L.wg), bf(L.wu), bf(L.wd), h->order_dev,
+                                                   h->shard_elems, h->down_off, (int)d, (int)f, (int)h->F, h->P,
+                                                   swiglu ? 1 : 0, st);
+            if (e == hipSuccess && swiglu) e = tsp::launch_pack_frag_bf16(bf(L.wg), f, (int)d, (int)f, bf(L.wgf), st);
+            return e != hipSuccess ? e : tsp::launch_pack_frag_bf16(bf(L.wu), f, (int)d, (int)f, bf(L.wuf), st);
         });
         if (su != TSP_OK) return su;
         h->bwd_unpacked = true;
     }
 
     tsp_status_t s = timed_launch(h, "bwd_transpose_in", st, [&] {
-        hipError_t e = tsp::launch_transpose_bf16(x16, (int)T, (int)d, (int)d, xt, Tp, st);
-        return e != hipSuccess ? e : tsp::launch_transpose_bf16(dy16, (int)T, (int)d, (int)d, dyt, Tp, st);
+        hipError_t e = tsp::launch_transpose_bf16(x16, (int)T, (int)d, (int)d, xt, Tp, 0, st);
+        return e != hipSuccess ? e : tsp::launch_transpose_bf16(dy16, (int)T, (int)d, (int)d, dyt, Tp, 1, st);
     });
     if (s != TSP_OK) return s;
     // dH[t][c] = sum_n dY[t][n] Wd[c][n], natural hidden columns
@@ -590,8 +596,9 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
     if (s != TSP_OK) return s;
     // dX[t][i] = sum over ring steps k of dG_k[t] . Wg[i][order[k] F ..] + dU_k[t] . Wu[i][..]
     tsp::NtArgs q{};
-    q.a_base[0] = swiglu ? wg16 : wu16;
-    q.a_base[1] = wu16;
+    q.a_base[0] = swiglu ? wgf : wuf;
+    q.a_base[1] = wuf;
+    q.a_frag = 1;
     q.b_base[0] = swiglu ? dg : du;
     q.b_base[1] = du;
     q.a_seg = F; q.b_seg = F; q.order = h->order_dev;
@@ -609,6 +616,7 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
         r.lda = Tp; r.ldb = Tp; r.M = M; r.N = N;
         r.spp = Tp / 32; r.nseg = 1; r.kinds = 1;
         r.out = out; r.ldc = ldc; r.remap = remap; r.F = F; r.remap_order = h->order_dev;
+        r.a_frag = 1;                                   // dG^T, dU^T, dY^T in fragment blocks
         return r;
     };
     tsp::NtArgs ws[3];

@@ -12,11 +12,13 @@
 //   dWg_s = X^T . dG_s, dWu_s = X^T . dU_s, dWd_s = H_s^T . dY   (the shard's own blocks)
 // G_s, U_s and H_s are recomputed from X with the forward's gate/up kernel
 // and packed records (gateup_bwd_w16), whose epilogue turns them into dG, dU
-// and H. Every product runs on the shape-6 pipeline (w16.h); the backward's
-// products read both operands row-major with the reduction index contiguous
-// (RowSrc), so the token-reduced weight gradients read transposed copies of
-// X, dY, dG, dU and H made by transpose_bf16 (padded with zero tokens to a
-// multiple of 64).
+// and H. Every product runs on the 256 x 256 pipeline (w16.h) with both
+// operands' reduction index contiguous (RowSrc): the B operand row-major, the
+// A operand row-major (dH: Wd) or in 32 x 16 fragment blocks (dX: Wg, Wu
+// packed once from the records; the weight gradients: dG^T, dU^T written so
+// by the gate/up epilogue, dY^T by transpose_bf16). The token-reduced weight
+// gradients read transposed copies of X, dY, dG, dU and H (tokens padded with
+// zeros, or finite values facing zeros, to a multiple of 64).
 #include "common.h"
 #include "launch.h"
 #include "w16.h"
@@ -25,9 +27,12 @@ namespace tsp {
 
 // ------------------------------------------------------------------ transpose
 // dst[c][r] = src[r][c] for r < R, 0 for R <= r < R_pad; 64 x 64 tiles through
-// LDS, each thread moving 16 elements (two 16-byte accesses) each way.
+// LDS, each thread moving 16 elements (two 16-byte accesses) each way. frag:
+// dst in 32 x 16 fragment blocks (rows c, reduction index r, ld_dst / 16
+// blocks per 32-row block), where a thread's two 8-token runs are the two
+// 16-byte lane slots (l, l + 32) of one block.
 __global__ __launch_bounds__(256) void transpose_bf16(const uint16_t* __restrict__ src, int R, int ld_src,
-                                                      uint16_t* __restrict__ dst, int ld_dst) {
+                                                      uint16_t* __restrict__ dst, int ld_dst, int frag) {
     __shared__ uint16_t tile[64][64 + 8];
     const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
     const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
@@ -53,13 +58,20 @@ __global__ __launch_bounds__(256) void transpose_bf16(const uint16_t* __restrict
         o0[e] = (uint32_t)tile[tc + 2 * e][tr] | ((uint32_t)tile[tc + 2 * e + 1][tr] << 16);
         o1[e] = (uint32_t)tile[tc + 8 + 2 * e][tr] | ((uint32_t)tile[tc + 8 + 2 * e + 1][tr] << 16);
     }
-    u32x4* q = reinterpret_cast<u32x4*>(dst + (int64_t)(c0 + tr) * ld_dst + r0 + tc);
-    q[0] = o0;
-    q[1] = o1;
+    const int64_t row = c0 + tr;
+    if (frag) {
+        u32x4* q = reinterpret_cast<u32x4*>(dst + ((row >> 5) * (ld_dst >> 4) + ((r0 + tc) >> 4)) * 512 + (row & 31) * 8);
+        q[0] = o0;                                      // lane slot row % 32: tokens r0 + tc .. + 7
+        q[32] = o1;                                     // lane slot row % 32 + 32: the next 8
+    } else {
+        u32x4* q = reinterpret_cast<u32x4*>(dst + row * ld_dst + r0 + tc);
+        q[0] = o0;
+        q[1] = o1;
+    }
 }
 
 // ------------------------------------------------------------------ NT product
-// C[n][m] = sum_k A[m][k] B[n][k] on the shape-6 pipeline, fp32 out:
+// C[n][m] = sum_k A[m][k] B[n][k] on the 256 x 256 pipeline, fp32 out:
 // out[row(n) * ldc + col(m)], n < N. remap 1: column m is a ring-ordered
 // hidden index (ring step m / F) stored at its shard's natural column
 // order[m / F] * F + m % F; remap 2: the same for the row n. F % 256 == 0, so
@@ -69,7 +81,7 @@ __global__ __launch_bounds__(256) void transpose_bf16(const uint16_t* __restrict
 // One launch runs up to three such products (NtGroup): workgroup ids are
 // dealt out to the products in order, so products whose tile counts are not
 // multiples of the CU count share one tail instead of leaving one each.
-template <bool BUF>
+template <bool BUF, bool FRAG>
 __global__ __launch_bounds__(256) void nt_w16(NtGroup grp) {
     using namespace w16;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
@@ -83,7 +95,7 @@ __global__ __launch_bounds__(256) void nt_w16(NtGroup grp) {
     const int m0 = mtile * BM, n0 = ntile * BN;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w / WN, wn = w % WN;
-    RowSrc<BUF> src;
+    RowSrc<BUF, FRAG> src;
     src.ls = 0;
     src.j = 0;
     src.lsb = 0;
@@ -137,7 +149,7 @@ __global__ __launch_bounds__(256) void nt_w16(NtGroup grp) {
 }
 
 // ------------------------------------------------------------------ gate/up backward
-// The forward's gate/up product (packed records in ring order, shape 6), with
+// The forward's gate/up product (packed records in ring order, tile shape 0), with
 // an epilogue that reads dH at the shard's natural hidden columns and writes
 // dG, dU and H (bf16, ring-ordered hidden columns like the forward's H).
 // SiLU'(g) = sigma (1 + g (1 - sigma)); with z2 = sqrt(8/pi) (u + 0.044715 u^3),
@@ -240,14 +252,15 @@ __global__ __launch_bounds__(256) void gateup_bwd_w16(Bf16Args a, BwdArgs b, int
         }
         lgkm_zero();
         stage_barrier();
-        // dG and dU row-major for dX, and dG, dU, H transposed (tokens
-        // contiguous) for the weight gradients, which reduce over tokens
+        // dG and dU row-major for dX, and transposed (tokens contiguous) for
+        // the weight gradients, which reduce over tokens: dG, dU as their A
+        // operands (fragment blocks), H as a B operand (row-major)
         if constexpr (ACT == 1) {
             sg_.flush(b.dg, a.f, t0, a.T, ring0, w, lane, hh);
-            flush_transposed(sg_, b.dgt, b.ldt, ring0, t0, hh, (int)threadIdx.x);
+            flush_frag_transposed(sg_, b.dgt, b.ldt, ring0, t0, hh, (int)threadIdx.x);
         }
         su.flush(b.du, a.f, t0, a.T, ring0, w, lane, hh);
-        flush_transposed(su, b.dut, b.ldt, ring0, t0, hh, (int)threadIdx.x);
+        flush_frag_transposed(su, b.dut, b.ldt, ring0, t0, hh, (int)threadIdx.x);
         flush_transposed(sh, b.ht, b.ldt, ring0, t0, hh, (int)threadIdx.x);
         lgkm_zero();
     }
@@ -256,11 +269,11 @@ __global__ __launch_bounds__(256) void gateup_bwd_w16(Bf16Args a, BwdArgs b, int
 // ------------------------------------------------------------------ launchers
 static inline int64_t cdiv64(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
-hipError_t launch_transpose_bf16(const uint16_t* src, int R, int C, int ld_src, uint16_t* dst, int R_pad,
+hipError_t launch_transpose_bf16(const uint16_t* src, int R, int C, int ld_src, uint16_t* dst, int R_pad, int frag,
                                  hipStream_t st) {
     if (C % 64 || R_pad % 64 || R > R_pad) return hipErrorInvalidValue;
     hipLaunchKernelGGL(transpose_bf16, dim3((unsigned)(C / 64), (unsigned)(R_pad / 64)), dim3(256), 0, st, src, R,
-                       ld_src, dst, R_pad);
+                       ld_src, dst, R_pad, frag ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -279,6 +292,11 @@ hipError_t launch_nt(const NtArgs* probs, int n, hipStream_t st) {
         if (p.M % BM || p.N < 1 || (p.spp * p.nseg) % 2 || p.spp * p.nseg < 2 || p.kinds < 1 || p.kinds > 2)
             return hipErrorInvalidValue;
         if (p.remap && (p.F % BM || !p.remap_order)) return hipErrorInvalidValue;
+        // fragment-block A: every segment's reduction range lies inside the K = lda indices
+        if (p.a_frag != probs[0].a_frag ||
+            (p.a_frag && (p.lda % 32 || p.nseg % p.kinds ||
+                          (int64_t)(p.nseg / p.kinds - 1) * p.a_seg + (int64_t)p.spp * 32 > p.lda)))
+            return hipErrorInvalidValue;
         grp.p[i] = p;
         tiles += (int64_t)(p.M / BM) * cdiv64(p.N, BN);
         buf = buf && (int64_t)p.M * p.lda * 2 < (int64_t(1) << 31) && (int64_t)p.N * p.ldb * 2 < (int64_t(1) << 31);
@@ -286,8 +304,13 @@ hipError_t launch_nt(const NtArgs* probs, int n, hipStream_t st) {
     for (int i = n; i < 3; ++i) grp.first[i] = (int)tiles;
     if (tiles > INT32_MAX / 2) return hipErrorInvalidValue;
     const dim3 grid((unsigned)tiles);
-    if (buf) hipLaunchKernelGGL((nt_w16<true>), grid, dim3(256), 0, st, grp);
-    else hipLaunchKernelGGL((nt_w16<false>), grid, dim3(256), 0, st, grp);
+    if (probs[0].a_frag) {
+        if (buf) hipLaunchKernelGGL((nt_w16<true, true>), grid, dim3(256), 0, st, grp);
+        else hipLaunchKernelGGL((nt_w16<false, true>), grid, dim3(256), 0, st, grp);
+    } else {
+        if (buf) hipLaunchKernelGGL((nt_w16<true, false>), grid, dim3(256), 0, st, grp);
+        else hipLaunchKernelGGL((nt_w16<false, false>), grid, dim3(256), 0, st, grp);
+    }
     return hipGetLastError();
 }
 

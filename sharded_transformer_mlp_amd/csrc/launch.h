@@ -78,7 +78,9 @@ bool skinny_supported(int d, int F, int P);
 // kinds] : j / kinds) * a_seg and B at b_base[j % kinds] + (j / kinds) * b_seg.
 // Output fp32 out[row(n) * ldc + col(m)] for n < N; remap 1 / 2 maps the
 // column / row index from ring order to the shard's natural position
-// (remap_order, shard width F).
+// (remap_order, shard width F). a_frag: A is stored in 32 x 16 fragment
+// blocks with K = lda (see RowSrc in w16.h), the same for every product of
+// one launch.
 struct NtArgs {
     const uint16_t* a_base[2];
     const uint16_t* b_base[2];
@@ -89,19 +91,25 @@ struct NtArgs {
     int64_t ldc;
     int remap, F;
     const int32_t* remap_order;
+    int a_frag;
 };
 struct BwdArgs {
     const float* dh;          // T x f fp32, natural hidden columns
     uint16_t* dg;             // T x f bf16, ring-ordered hidden columns (SwiGLU only)
     uint16_t* du;             // T x f bf16, ring-ordered
-    uint16_t* dgt;            // the same transposed: f x ldt, tokens contiguous (SwiGLU only)
-    uint16_t* dut;            // f x ldt
-    uint16_t* ht;             // H transposed, f x ldt (H itself is not needed row-major)
+    uint16_t* dgt;            // the same transposed (f rows x ldt tokens) in 32 x 16 fragment blocks (SwiGLU only)
+    uint16_t* dut;            // f x ldt, fragment blocks
+    uint16_t* ht;             // H transposed, f x ldt row-major, tokens contiguous
     int ldt;                  // T rounded up to 64; columns T..ldt-1 hold finite values
     const int32_t* order;     // ring order (device)
 };
-hipError_t launch_transpose_bf16(const uint16_t* src, int R, int C, int ld_src, uint16_t* dst, int R_pad,
+// frag: dst in 32 x 16 fragment blocks (C rows x R_pad reduction indices)
+// instead of row-major C x R_pad.
+hipError_t launch_transpose_bf16(const uint16_t* src, int R, int C, int ld_src, uint16_t* dst, int R_pad, int frag,
                                  hipStream_t st);
+// Row-major M x K (row stride ld) into 32 x 16 fragment blocks (M % 32 == 0,
+// K % 16 == 0, ld % 8 == 0).
+hipError_t launch_pack_frag_bf16(const uint16_t* src, int64_t ld, int M, int K, uint16_t* dst, hipStream_t st);
 // Up to three products in one launch; first[i] is product i's first tile.
 struct NtGroup {
     NtArgs p[3];

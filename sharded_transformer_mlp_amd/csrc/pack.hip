@@ -184,6 +184,33 @@ hipError_t launch_pack_bf16(const void* wg, const void* wu, const void* wd, void
     return hipGetLastError();
 }
 
+// Row-major M x K (row stride ld) into 32 x 16 fragment blocks, the layout
+// of the packed records (block (m / 32, k / 16) at ((m / 32) (K / 16) + k / 16)
+// 512, lane l holding row l % 32 and indices 8 (l / 32) .. + 7): one 16-byte
+// lane slot per thread. The backward's dX product reads Wg and Wu so.
+__global__ void pack_frag_bf16(const uint16_t* __restrict__ src, int64_t ld, int K, uint16_t* __restrict__ dst,
+                               int64_t chunks) {
+    const int kb_per_row = K >> 4;
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks;
+         c += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t block = c >> 6;
+        const int lane = (int)(c & 63);
+        const int64_t nb = block / kb_per_row;
+        const int kb = (int)(block - nb * kb_per_row);
+        const int64_t row = nb * 32 + (lane & 31);
+        const int k0 = kb * 16 + (lane >> 5) * 8;
+        *reinterpret_cast<u32x4*>(dst + c * 8) = *reinterpret_cast<const u32x4*>(src + row * ld + k0);
+    }
+}
+
+hipError_t launch_pack_frag_bf16(const uint16_t* src, int64_t ld, int M, int K, uint16_t* dst, hipStream_t st) {
+    if (M % 32 || K % 16 || ld % 8 || ld < K) return hipErrorInvalidValue;
+    const int64_t chunks = (int64_t)M * K / 8;
+    const dim3 grid((unsigned)std::min<int64_t>((chunks + 255) / 256, 8192));
+    hipLaunchKernelGGL(pack_frag_bf16, grid, dim3(256), 0, st, src, ld, K, dst, chunks);
+    return hipGetLastError();
+}
+
 hipError_t launch_unpack_bf16(const void* src, void* wg, void* wu, void* wd, const int32_t* order,
                               int64_t shard_elems, int64_t down_off, int d, int f, int F, int P, int swiglu,
                               hipStream_t st) {

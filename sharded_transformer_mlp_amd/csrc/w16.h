@@ -217,7 +217,16 @@ struct PackedSrc {
 // ring order for dX. A is loaded in 64-byte row pieces into the A ring, B in
 // whole 128-byte rows into the B ring; the two walk the segments with cursors
 // of their own (B runs ahead of A). spp is even.
-template <bool BUF>
+//
+// FRAG: A is stored in 32 x 16 fragment blocks (the layout of the packed
+// weight records, rows = m, reduction index = k, K = lda: block (m / 32,
+// k / 16) at element ((m / 32) (lda / 16) + k / 16) 512, lane l of a block
+// holding row l % 32 and indices 8 (l / 32) .. + 7). A stage's A loads are
+// then whole 1 KiB blocks (8 cache lines per load instruction instead of the
+// 16 that 64-byte row pieces touch), as for the forward's weights. Offsets
+// along the rows (a_seg, the 32-index steps) keep their row-major meaning and
+// become 32x as many elements.
+template <bool BUF, bool FRAG = false>
 struct RowSrc {
     const uint16_t* a;                                  // A at the current stage's reduction offset
     const uint16_t* b;                                  // B at the current super-stage's offset
@@ -234,15 +243,32 @@ struct RowSrc {
         const int kind = seg % kinds, k = seg / kinds;
         // wave-uniform (the buffer resource built from it must live in SGPRs)
         const int s = order ? __builtin_amdgcn_readfirstlane(order[k]) : k;
-        a = (kind ? a_base1 : a_base0) + (int64_t)s * a_seg;
+        abase = kind ? a_base1 : a_base0;
+        a = abase + (int64_t)s * a_seg;
     }
+    const uint16_t* abase = nullptr;                    // the current segment kind's A base
     __device__ void seek_b(int seg) {
         const int kind = seg % kinds, k = seg / kinds;
         b = (kind ? b_base1 : b_base0) + (int64_t)k * b_seg;
     }
     __device__ void issue_a(int g, uint16_t* lds_stage) {
         const int blk = g * NW + w;
-        load_rows<BUF>(lds_stage + blk * 512, a, lda, m0 + blk * 16, last_m, lane);
+        if constexpr (FRAG) {
+            // block blk of the stage: 32-row block m0 / 32 + blk / 2, the
+            // stage's 16-index block blk % 2 (m0 % 256 == 0, M % 256 == 0)
+            const int64_t off = (int64_t)(m0 / 32 + (blk >> 1)) * 32 * lda + (int64_t)(a - abase) * 32 +
+                                (blk & 1) * 512 + lane * 8;
+            TSP_LDS void* dst = (TSP_LDS void*)(lds_stage + blk * 512);
+            if constexpr (BUF) {
+                const __amdgpu_buffer_rsrc_t rs =
+                    __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, 0x7fffffff, kRawBufferWord3);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (int)(off * 2), 0, 0, 0);
+            } else {
+                __builtin_amdgcn_global_load_lds(abase + off, dst, 16, 0, 0);
+            }
+        } else {
+            load_rows<BUF>(lds_stage + blk * 512, a, lda, m0 + blk * 16, last_m, lane);
+        }
     }
     __device__ void advance_a() {
         if (ls + 1 < spp) {
@@ -267,7 +293,16 @@ struct RowSrc {
         }
     }
     __device__ void read_a(int q, const uint16_t* lds_stage, bf16x8 (&af)[TM]) const {
-        af[q] = read_rows(lds_stage, wm * TM + q, lane);
+        if constexpr (FRAG) {
+            // as PackedSrc::read_a: 16-row block ib = rows 16 (ib % 2) + l % 16
+            // of 32-row block ib / 2, indices 8 (l / 16) .. + 7
+            const int r = lane & 15, c = lane >> 4;
+            const bf16x8* as = reinterpret_cast<const bf16x8*>(lds_stage);
+            const int ib = wm * TM + q;
+            af[q] = as[((ib >> 1) * 2 + (c >> 1)) * 64 + (c & 1) * 32 + (ib & 1) * 16 + r];
+        } else {
+            af[q] = read_rows(lds_stage, wm * TM + q, lane);
+        }
     }
 };
 
@@ -596,6 +631,34 @@ __device__ __forceinline__ void flush_transposed(const StagedRows16<COLS, 128>& 
         for (int e = 0; e < 4; ++e)
             v[e] = (uint32_t)stg.lds[(r + 2 * e) * PITCH + c] | ((uint32_t)stg.lds[(r + 2 * e + 1) * PITCH + c] << 16);
         if (col < ldt) *reinterpret_cast<u32x4*>(dst + (row0 + c) * ldt + col) = u32x4{v[0], v[1], v[2], v[3]};
+    }
+}
+
+// Half hh of a StagedRows16<COLS, 128> tile, transposed, into dst stored in
+// 32 x 16 fragment blocks (rows = the tile's columns at row0 + c, reduction
+// index = token, KB = ldt / 16 blocks per 32-row block; see RowSrc<.., FRAG>):
+// a lane takes one column and 8 consecutive tokens, i.e. one 16-byte lane slot
+// of a block. The 64 lanes of a wave take 64 neighbouring columns of the same
+// 8 staged rows (LDS reads of one 128-byte row segment: no bank conflicts) and
+// store two runs of 512 contiguous bytes; tokens >= ldt are skipped.
+template <int COLS>
+__device__ __forceinline__ void flush_frag_transposed(const StagedRows16<COLS, 128>& stg, uint16_t* __restrict__ dst,
+                                                      int64_t ldt, int64_t row0, int t0, int hh, int tid) {
+    constexpr int PITCH = StagedRows16<COLS, 128>::PITCH;
+    static_assert(COLS % 64 == 0, "frag flush");
+    const int64_t kb_per_row = ldt >> 4;
+#pragma unroll 2
+    for (int it = 0; it < COLS / 16; ++it) {
+        const int id = it * 256 + tid;
+        const int c = id % COLS, r = (id / COLS) * 8;           // column, first staged row of the 8 tokens
+        const int col = t0 + (r >> 6) * 128 + hh * 64 + (r & 63);
+        uint32_t v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            v[e] = (uint32_t)stg.lds[(r + 2 * e) * PITCH + c] | ((uint32_t)stg.lds[(r + 2 * e + 1) * PITCH + c] << 16);
+        const int64_t row = row0 + c;
+        const int64_t off = ((row >> 5) * kb_per_row + (col >> 4)) * 512 + ((row & 31) + 32 * ((col >> 3) & 1)) * 8;
+        if (col < ldt) *reinterpret_cast<u32x4*>(dst + off) = u32x4{v[0], v[1], v[2], v[3]};
     }
 }
 
