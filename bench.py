@@ -53,10 +53,8 @@ KERNEL_SOURCES = {
     "reduce_partials": ["gemm_tiled.hip", "w16.h", "common.h"],
     "bwd_dh": ["backward.hip", "w16.h", "common.h"],
     "bwd_gateup": ["backward.hip", "w16.h", "common.h"],
-    "bwd_dx": ["backward.hip", "w16.h", "common.h"],
-    "bwd_dw": ["backward.hip", "w16.h", "common.h"],
+    "bwd_dw_dx": ["backward.hip", "w16.h", "common.h"],
     "bwd_transpose_in": ["backward.hip", "common.h"],
-    "bwd_transpose_mid": ["backward.hip", "common.h"],
     "attn_qkv": ["attn.hip", "w16.h", "common.h"],
     "attn_core": ["attn_core.hip", "w16.h", "common.h"],
     "attn_out": ["gemm_tiled.hip", "w16.h", "common.h"],
@@ -97,14 +95,12 @@ def kernel_work(w, kernel: str, T: int):
         return 2 * T * d * f, f * d * es + T * d * es + T * f * 4
     if kernel == "bwd_gateup":              # recomputed gate/up product + backward epilogue
         return 2 * n_gu * T * d * f, n_gu * d * f * es + T * d * es + T * f * 4 + (n_gu + 1) * T * f * es
-    if kernel == "bwd_dx":                  # dX = sum dG.Wg^T + dU.Wu^T
-        return 2 * n_gu * T * d * f, n_gu * d * f * es + n_gu * T * f * es + T * d * 4
-    if kernel == "bwd_dw":                  # weight gradients (all of one backward's dW products)
-        return (2 * n_gu + 2) * T * d * f, 2 * T * d * es + (n_gu + 1) * T * f * es + (n_gu + 1) * d * f * 4
+    if kernel == "bwd_dw_dx":               # weight gradients and dX = sum dG.Wg^T + dU.Wu^T, one launch
+        return ((2 * n_gu + 2) * T * d * f + 2 * n_gu * T * d * f,
+                2 * T * d * es + (n_gu + 1) * T * f * es + (n_gu + 1) * d * f * 4      # dW: X, dY, dG/dU, H in, dW out
+                + n_gu * d * f * es + n_gu * T * f * es + T * d * 4)                  # dX: Wg/Wu, dG/dU in, dX out
     if kernel == "bwd_transpose_in":        # copies of X and dY: each byte read and written once
         return 0, 2 * 2 * T * d * es
-    if kernel == "bwd_transpose_mid":       # copies of dG, dU, H
-        return 0, 2 * (n_gu + 1) * T * f * es
     if kernel in ("gateup_tiled", "skinny_gateup", "gateup_f32"):
         flops = 2 * T * w.d * w.f * n_gu
         byts = n_gu * w.d * w.f * es + T * w.d * es + T * w.f * es      # W_gu, X, H out

@@ -605,10 +605,7 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
     q.lda = (int)f; q.ldb = (int)f; q.M = (int)d; q.N = (int)T;
     q.spp = F / 32; q.kinds = swiglu ? 2 : 1; q.nseg = P * q.kinds;
     q.out = dX; q.ldc = d;
-    s = timed_launch(h, "bwd_dx", st, [&] { return tsp::launch_nt(&q, 1, st); });
-    if (s != TSP_OK) return s;
-    // weight gradients: reductions over the (zero-padded) token dimension, all
-    // in one launch
+    // weight gradients: reductions over the (zero-padded) token dimension
     auto dw = [&](const uint16_t* at, const uint16_t* bt, int M, int N, float* out, int64_t ldc, int remap) {
         tsp::NtArgs r{};
         r.a_base[0] = r.a_base[1] = at;
@@ -619,12 +616,16 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
         r.a_frag = 1;                                   // dG^T, dU^T, dY^T in fragment blocks
         return r;
     };
-    tsp::NtArgs ws[3];
+    // one launch: the weight gradients' tiles first, then dX's (each dX tile
+    // reduces over 2f, a weight-gradient tile over T), so that dX tiles start
+    // on the CUs the weight gradients' last partial round leaves idle
+    tsp::NtArgs ws[tsp::kMaxNt];
     int nw = 0;
     if (swiglu) ws[nw++] = dw(dgt, xt, (int)f, (int)d, dW_gate, f, 1);   // dW_gate[i][c]
     ws[nw++] = dw(dut, xt, (int)f, (int)d, dW_up, f, 1);
     ws[nw++] = dw(dyt, ht, (int)d, (int)f, dW_down, d, 2);               // dW_down[c][n]
-    return timed_launch(h, "bwd_dw", st, [&] { return tsp::launch_nt(ws, nw, st); });
+    ws[nw++] = q;
+    return timed_launch(h, "bwd_dw_dx", st, [&] { return tsp::launch_nt(ws, nw, st); });
 }
 
 tsp_status_t tsp_mlp_destroy(tsp_mlp_t h) {

@@ -78,20 +78,29 @@ __global__ __launch_bounds__(256) void transpose_bf16(const uint16_t* __restrict
 // a 256-wide tile never straddles two shards and the remap is one offset per
 // tile.
 //
-// One launch runs up to three such products (NtGroup): workgroup ids are
+// One launch runs up to four such products (NtGroup): workgroup ids are
 // dealt out to the products in order, so products whose tile counts are not
-// multiples of the CU count share one tail instead of leaving one each.
+// multiples of the CU count share one tail instead of leaving one each (the
+// backward puts its long-reduction dX tiles last, where they start on the CUs
+// that the weight gradients' last partial round leaves idle). Each product's
+// range of workgroup ids starts at a multiple of 8 and is remapped to XCDs on
+// its own, so every product's tiles spread over all eight XCDs (remapped as one
+// range, the last product's tiles would all land on the last XCD).
 template <bool BUF, bool FRAG>
 __global__ __launch_bounds__(256) void nt_w16(NtGroup grp) {
     using namespace w16;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
     poison_lds(lds, sizeof(lds));
-    const int lin = xcd_remap(blockIdx.x, gridDim.x);
-    const int gi = lin < grp.first[1] ? 0 : (lin < grp.first[2] ? 1 : 2);
-    const NtArgs& p = gi == 0 ? grp.p[0] : (gi == 1 ? grp.p[1] : grp.p[2]);
+    const int bid = blockIdx.x;
+    const int gi = bid < grp.first[1] ? 0 : (bid < grp.first[2] ? 1 : (bid < grp.first[3] ? 2 : 3));
+    const NtArgs& p = gi == 0 ? grp.p[0] : (gi == 1 ? grp.p[1] : (gi == 2 ? grp.p[2] : grp.p[3]));
     const int n_mt = p.M / BM, n_nt = (p.N + BN - 1) / BN;
+    const int first = gi == 0 ? grp.first[0] : (gi == 1 ? grp.first[1] : (gi == 2 ? grp.first[2] : grp.first[3]));
+    const int next = gi == 0 ? grp.first[1] : (gi == 1 ? grp.first[2] : (gi == 2 ? grp.first[3] : (int)gridDim.x));
+    const int lin = xcd_remap(bid - first, next - first);
+    if (lin >= n_mt * n_nt) return;                     // padding of the product's id range to a multiple of 8
     int ntile, mtile;
-    raster(lin - grp.first[gi], n_mt, n_nt, ntile, mtile);
+    raster(lin, n_mt, n_nt, ntile, mtile);
     const int m0 = mtile * BM, n0 = ntile * BN;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w / WN, wn = w % WN;
@@ -279,14 +288,14 @@ hipError_t launch_transpose_bf16(const uint16_t* src, int R, int C, int ld_src, 
 
 hipError_t launch_nt(const NtArgs* probs, int n, hipStream_t st) {
     using namespace w16;
-    if (n < 1 || n > 3) return hipErrorInvalidValue;
+    if (n < 1 || n > kMaxNt) return hipErrorInvalidValue;
     NtGroup grp{};
     int64_t tiles = 0;
     // buffer offsets are 32-bit: every row of either operand must lie within
     // 2^31 bytes of that operand's base
     bool buf = true;
-    for (int i = 0; i < 3; ++i) {
-        grp.first[i] = (int)tiles;
+    for (int i = 0; i < kMaxNt; ++i) {
+        grp.first[i] = (int)tiles;                      // a multiple of 8 (see nt_w16)
         if (i >= n) continue;
         const NtArgs& p = probs[i];
         if (p.M % BM || p.N < 1 || (p.spp * p.nseg) % 2 || p.spp * p.nseg < 2 || p.kinds < 1 || p.kinds > 2)
@@ -298,10 +307,10 @@ hipError_t launch_nt(const NtArgs* probs, int n, hipStream_t st) {
                           (int64_t)(p.nseg / p.kinds - 1) * p.a_seg + (int64_t)p.spp * 32 > p.lda)))
             return hipErrorInvalidValue;
         grp.p[i] = p;
-        tiles += (int64_t)(p.M / BM) * cdiv64(p.N, BN);
+        tiles += cdiv64((int64_t)(p.M / BM) * cdiv64(p.N, BN), 8) * 8;
         buf = buf && (int64_t)p.M * p.lda * 2 < (int64_t(1) << 31) && (int64_t)p.N * p.ldb * 2 < (int64_t(1) << 31);
     }
-    for (int i = n; i < 3; ++i) grp.first[i] = (int)tiles;
+    for (int i = n; i < kMaxNt; ++i) grp.first[i] = (int)tiles;
     if (tiles > INT32_MAX / 2) return hipErrorInvalidValue;
     const dim3 grid((unsigned)tiles);
     if (probs[0].a_frag) {

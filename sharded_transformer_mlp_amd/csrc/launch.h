@@ -110,10 +110,11 @@ hipError_t launch_transpose_bf16(const uint16_t* src, int R, int C, int ld_src, 
 // Row-major M x K (row stride ld) into 32 x 16 fragment blocks (M % 32 == 0,
 // K % 16 == 0, ld % 8 == 0).
 hipError_t launch_pack_frag_bf16(const uint16_t* src, int64_t ld, int M, int K, uint16_t* dst, hipStream_t st);
-// Up to three products in one launch; first[i] is product i's first tile.
+// Up to four products in one launch; first[i] is product i's first tile.
+constexpr int kMaxNt = 4;
 struct NtGroup {
-    NtArgs p[3];
-    int first[3];
+    NtArgs p[kMaxNt];
+    int first[kMaxNt];
 };
 hipError_t launch_nt(const NtArgs* probs, int n, hipStream_t st);
 hipError_t launch_gateup_bwd(const Bf16Args& a, const BwdArgs& b, hipStream_t st);
