@@ -204,21 +204,27 @@ __global__ __launch_bounds__(256) void gateup_bwd_w16(Bf16Args a, BwdArgs b, int
     Stg sh{lds}, su{lds + Stg::ELEMS}, sg_{lds + 2 * Stg::ELEMS};
     auto col = [&](int ib) { return ACT == 1 ? (wm * 2 + ib / 2) * 32 + (ib % 2) * 16 + fsub
                                              : (wm * TM + ib) * 16 + fsub; };
+    // dH of (half hh, block ib): the half's four (16-token, 4-column) pieces
+    // of the lane, loaded one block ahead of their use (two blocks' worth of
+    // registers), so that a block's arithmetic covers the next block's loads
+    auto load_dh = [&](int hh, int ib, f32x4 (&dv)[TN / 2]) {
+        const int c = col(ib);
+#pragma unroll
+        for (int jj = 0; jj < TN / 2; ++jj) {
+            const int tok = min(t0 + wn * 128 + hh * 64 + jj * 16 + (lane & 15), a.T - 1);
+            dv[jj] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(dh + (int64_t)tok * a.f + nat0 + c));
+        }
+    };
+    f32x4 dvb[2][TN / 2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
+        load_dh(hh, 0, dvb[0]);
         stage_barrier();                                // fragment reads / the last flush's reads are done
 #pragma unroll
         for (int ib = 0; ib < NB; ++ib) {
             const int c = col(ib);
-            // the dH values of the half's four (16-token, 4-column) pieces are
-            // loaded together before any of them is used
-            f32x4 dv[TN / 2];
-#pragma unroll
-            for (int jj = 0; jj < TN / 2; ++jj) {
-                const int tok = min(t0 + wn * 128 + hh * 64 + jj * 16 + (lane & 15), a.T - 1);
-                dv[jj] = __builtin_nontemporal_load(
-                    reinterpret_cast<const f32x4*>(dh + (int64_t)tok * a.f + nat0 + c));
-            }
+            if (ib + 1 < NB) load_dh(hh, ib + 1, dvb[(ib + 1) & 1]);
+            const f32x4 (&dv)[TN / 2] = dvb[ib & 1];
 #pragma unroll
             for (int jj = 0; jj < TN / 2; ++jj) {
                 const int j = hh * (TN / 2) + jj, r = wn * 64 + jj * 16 + (lane & 15);
@@ -254,7 +260,7 @@ __global__ __launch_bounds__(256) void gateup_bwd_w16(Bf16Args a, BwdArgs b, int
                     sh.put4(r, c, pack4_bf16(h[0], h[1], h[2], h[3]));
                 }
             }
-            // one block's dH loads in flight at a time: hoisting every block's
+            // at most two blocks' dH loads in flight: hoisting every block's
             // loads ahead of the arithmetic (8 blocks x 16 registers for GeLU)
             // ran the kernel out of registers
             __builtin_amdgcn_sched_barrier(0);
