@@ -33,7 +33,7 @@ namespace tsp {
 // 16-byte lane slots (l, l + 32) of one block.
 __global__ __launch_bounds__(256) void transpose_bf16(const uint16_t* __restrict__ src, int R, int ld_src,
                                                       uint16_t* __restrict__ dst, int ld_dst, int frag) {
-    __shared__ uint16_t tile[64][64 + 8];
+    __shared__ uint16_t tile[64][64 + 2];           // 33-word rows: the column reads spread over the banks
     const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
     const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
     const int r = r0 + tr;
