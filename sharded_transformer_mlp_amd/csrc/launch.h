@@ -51,7 +51,7 @@ hipError_t launch_pack_f32(const void* wg, const void* wu, const void* wd, void*
 
 // Tiled MFMA path. Each returns the launch status; `cfg` picks a tile shape.
 hipError_t launch_gateup_tiled(const Bf16Args& a, int cfg, hipStream_t st);
-// split > 1 (shape 5 only): the ring is cut into `split` groups of
+// split > 1 (tile shape 0 only): the ring is cut into `split` groups of
 // consecutive ring steps, each group's sum goes to its own fp32 partial in
 // a.part, and launch_reduce_partials adds the partials in ring order into Y.
 hipError_t launch_down_tiled(const Bf16Args& a, int cfg, int split, hipStream_t st);
