@@ -257,6 +257,7 @@ tsp_status_t tsp_mlp_create(tsp_mlp_t* out, int64_t T_max, int64_t d, int64_t f,
     h->work_bytes = (h->work_bytes + 255) / 256 * 256;
     h->part_off = h->work_bytes;
     if (dtype == TSP_DTYPE_BF16) h->work_bytes += tsp::down_split_bytes(T_max, (int)d, P);
+    else h->work_bytes += tsp::f32_split_bytes(T_max, (int)d, (int)h->F);
 
     if ((e = hipMalloc(&h->order_dev, sizeof(int32_t) * (size_t)P)) != hipSuccess ||
         (e = hipMalloc(&h->packed, (size_t)h->packed_bytes)) != hipSuccess ||
@@ -323,6 +324,7 @@ tsp_status_t plan_forward(const tsp_mlp* h, int64_t T, FwdPlan& pl) {
     } else {
         if (h->path == TSP_PATH_SKINNY) return fail(TSP_ERR_UNSUPPORTED, "skinny path is bf16 only");
         pl.h_bytes = T * f * 4;
+        pl.split = tsp::choose_f32_split((int)T, (int)d, (int)h->F);
     }
     pl.part_off = (pl.h_bytes + 255) / 256 * 256;
     pl.total = pl.part_off + (pl.split > 1 ? (int64_t)pl.split * T * d * 4 : 0);
@@ -378,12 +380,16 @@ tsp_status_t run_forward(tsp_mlp* h, int64_t T, const void* X, float* Y, hipStre
     a.x = static_cast<const float*>(X);
     a.h = static_cast<float*>(work);
     a.y = Y;
+    a.part = reinterpret_cast<float*>(static_cast<char*>(work) + pl.part_off);
     a.shard_elems = h->shard_elems;
     a.T = (int)T; a.d = (int)h->d; a.f = (int)h->f; a.F = (int)h->F; a.P = h->P;
     a.swiglu = swiglu ? 1 : 0;
+    a.split = pl.split;
     s = timed_launch(h, "gateup_f32", st, [&] { return tsp::launch_gateup_f32(a, st); });
     if (s != TSP_OK) return s;
-    return timed_launch(h, "down_f32", st, [&] { return tsp::launch_down_f32(a, st); });
+    s = timed_launch(h, "down_f32", st, [&] { return tsp::launch_down_f32(a, st); });
+    if (s != TSP_OK || pl.split == 1) return s;
+    return timed_launch(h, "reduce_partials", st, [&] { return tsp::launch_reduce_f32(a.part, pl.split, T * a.d, Y, st); });
 }
 
 }  // namespace

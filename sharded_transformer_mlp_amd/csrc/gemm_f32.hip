@@ -14,7 +14,11 @@
 //
 // Both products put output features on the MFMA rows and tokens on its
 // columns: a workgroup tile is 64 features x 64 tokens, four waves of 32 x 32
-// (2 x 2 blocks of 16 x 16), 16 reduction indices per LDS stage. For
+// (2 x 2 blocks of 16 x 16), 32 reduction indices per LDS stage. When the
+// output has few tiles (the parity-sized shapes), the down product's
+// reduction is split into up to 16 groups: group g takes the same sub-range
+// of every ring step's hidden indices and writes an fp32 partial, and the
+// partials are added in group order into Y (deterministic). For
 // v_mfma_f32_16x16x4_f32 lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]
 // and receives D[4 (l / 16) + r][l % 16], r = 0..3: four consecutive features
 // of one token.
@@ -25,7 +29,14 @@ namespace tsp {
 
 constexpr int F32_MT = 64;   // features per workgroup tile
 constexpr int F32_NT = 64;   // tokens per workgroup tile
-constexpr int F32_KT = 16;   // reduction indices per stage
+constexpr int F32_KT = 32;   // reduction indices per stage
+
+// Hidden indices per reduction group of a split down product: a multiple of
+// the stage depth (the last group may be shorter).
+__host__ __device__ inline int f32_split_chunk(int F, int split) {
+    const int c = (F + split - 1) / split;
+    return (c + F32_KT - 1) / F32_KT * F32_KT;
+}
 
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -122,6 +133,9 @@ __global__ __launch_bounds__(256) void down_f32(F32Args a) {
     poison_lds(ds, sizeof(ds));
     const int n0 = blockIdx.x * F32_MT;                  // first output feature
     const int t0 = blockIdx.y * F32_NT;
+    const int g = blockIdx.z;                            // reduction group (split > 1)
+    const int kchunk = f32_split_chunk(a.F, a.split);
+    const int kg0 = g * kchunk, kg1 = min(a.F, kg0 + kchunk);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w >> 1, wn = w & 1;
     const int64_t down_off = (a.swiglu ? 2 : 1) * (int64_t)a.d * a.F;
@@ -132,9 +146,9 @@ __global__ __launch_bounds__(256) void down_f32(F32Args a) {
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int step = 0; step < a.P; ++step) {             // records and H columns in ring order
         const float* wd = a.packed + (int64_t)step * a.shard_elems + down_off;   // F x d
-        for (int k0 = 0; k0 < a.F; k0 += F32_KT) {
-            load_x_tile(hs, a.h, a.f, (int64_t)step * a.F, t0, a.T, k0, a.F);
-            load_w_tile(ds, wd, a.d, k0, a.F, n0, a.d);
+        for (int k0 = kg0; k0 < kg1; k0 += F32_KT) {
+            load_x_tile(hs, a.h, a.f, (int64_t)step * a.F, t0, a.T, k0, kg1);
+            load_w_tile(ds, wd, a.d, k0, kg1, n0, a.d);
             __syncthreads();
 #pragma unroll
             for (int ks = 0; ks < F32_KT / 4; ++ks) {
@@ -152,6 +166,7 @@ __global__ __launch_bounds__(256) void down_f32(F32Args a) {
             __syncthreads();
         }
     }
+    float* out = a.split > 1 ? a.part + (int64_t)g * a.T * a.d : a.y;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -159,7 +174,7 @@ __global__ __launch_bounds__(256) void down_f32(F32Args a) {
             const int tok = t0 + wn * 32 + j * 16 + (lane & 15);
             if (tok >= a.T) continue;
             const int n = n0 + wm * 32 + i * 16 + 4 * (lane >> 4);
-            float* yrow = a.y + (int64_t)tok * a.d;
+            float* yrow = out + (int64_t)tok * a.d;
             if (n + 3 < a.d && (a.d & 3) == 0) {
                 *reinterpret_cast<f32x4*>(yrow + n) = acc[i][j];
             } else {
@@ -168,6 +183,33 @@ __global__ __launch_bounds__(256) void down_f32(F32Args a) {
                     if (n + r < a.d) yrow[n + r] = acc[i][j][r];
             }
         }
+}
+
+// y[i] = sum over groups g = 0.. of part[g][i], in group order.
+__global__ __launch_bounds__(256) void reduce_f32(const float* __restrict__ part, int split, int64_t n,
+                                                  float* __restrict__ y) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        float s = part[i];
+        for (int g = 1; g < split; ++g) s += part[(int64_t)g * n + i];
+        y[i] = s;
+    }
+}
+
+int choose_f32_split(int T, int d, int F) {
+    const int64_t tiles = (int64_t)((d + F32_MT - 1) / F32_MT) * ((T + F32_NT - 1) / F32_NT);
+    int s = 1;
+    while (s < 16 && tiles * s * 2 <= 256 && f32_split_chunk(F, s * 2) * (s * 2 - 1) < F) s *= 2;
+    return s;
+}
+
+int64_t f32_split_bytes(int64_t T_max, int d, int F) {
+    int64_t most = 0;
+    for (int64_t t = F32_NT; t < T_max + F32_NT; t += F32_NT) {
+        const int64_t T = t < T_max ? t : T_max;
+        const int s = choose_f32_split((int)T, d, F);
+        if (s > 1 && s * T * d * 4 > most) most = s * T * d * 4;
+    }
+    return most;
 }
 
 hipError_t launch_gateup_f32(const F32Args& a, hipStream_t st) {
@@ -180,8 +222,16 @@ hipError_t launch_gateup_f32(const F32Args& a, hipStream_t st) {
 }
 
 hipError_t launch_down_f32(const F32Args& a, hipStream_t st) {
-    const dim3 grid((unsigned)((a.d + F32_MT - 1) / F32_MT), (unsigned)((a.T + F32_NT - 1) / F32_NT));
+    if (a.split < 1 || a.split > 16 || (a.split > 1 && !a.part)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((a.d + F32_MT - 1) / F32_MT), (unsigned)((a.T + F32_NT - 1) / F32_NT),
+                    (unsigned)a.split);
     hipLaunchKernelGGL(down_f32, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce_f32(const float* part, int split, int64_t n, float* y, hipStream_t st) {
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 2048);
+    hipLaunchKernelGGL(reduce_f32, dim3((unsigned)blocks), dim3(256), 0, st, part, split, n, y);
     return hipGetLastError();
 }
 

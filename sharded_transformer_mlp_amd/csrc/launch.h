@@ -31,9 +31,11 @@ struct F32Args {
     const float* x;
     float* h;
     float* y;
+    float* part;              // split > 1: split fp32 partials of T x d
     int64_t shard_elems;
     int T, d, f, F, P;
     int swiglu;
+    int split = 1;            // reduction groups of the down product (choose_f32_split)
 };
 
 // Pack the weights into P records in ring order (record k = shard order[k]).
@@ -122,6 +124,11 @@ hipError_t launch_gateup_bwd(const Bf16Args& a, const BwdArgs& b, hipStream_t st
 // fp32 path.
 hipError_t launch_gateup_f32(const F32Args& a, hipStream_t st);
 hipError_t launch_down_f32(const F32Args& a, hipStream_t st);
+hipError_t launch_reduce_f32(const float* part, int split, int64_t n, float* y, hipStream_t st);
+// Reduction groups of the fp32 down product at this shape (1 = none), and the
+// partials' bytes the largest split needs for any T <= T_max.
+int choose_f32_split(int T, int d, int F);
+int64_t f32_split_bytes(int64_t T_max, int d, int F);
 
 // Ceiling probes (measurement only).
 hipError_t launch_probe_hbm_read(const void* buf, int64_t bytes, void* sink, hipStream_t st);
