@@ -25,8 +25,10 @@
 // registers on every trip).
 //
 // PackedSrc takes the A operand from packed 32 x 16 fragment blocks (the
-// forward's weight records); RowSrc takes it from a row-major matrix with
-// the reduction index contiguous (the backward). B is always row-major.
+// forward's weight records); RowSrc (the backward) walks reduction segments
+// and takes A either from a row-major matrix with the reduction index
+// contiguous or (FRAG) from the same fragment-block layout. B is always
+// row-major.
 #pragma once
 
 #include "common.h"
