@@ -132,12 +132,14 @@ def test_backward_ring_orders_and_reuse():
         mlp.close()
 
 
-def test_backward_llama_shape_sampled():
-    """Llama-3-8B shape (T 4096, d 4096, f 14336, P 8, ring from 3) at full
-    size: dX on sampled token rows, the weight gradients on sampled hidden
-    columns (both computed by the oracle on their own)."""
-    w = workload("llama8b")
-    say("[gpu] backward llama8b full size")
+@pytest.mark.parametrize("name", ["llama8b", "gelu"])
+def test_backward_full_size_sampled(name):
+    """The Llama-3-8B shape (T 4096, d 4096, f 14336, P 8, ring from 3) and the
+    Megatron GeLU block (T 2048, d 4096, f 16384, P 2) at full size: dX on
+    sampled token rows, the weight gradients on sampled hidden columns (both
+    computed by the oracle on their own)."""
+    w = workload(name)
+    say(f"[gpu] backward {name} full size")
     inp, dy = make_inputs(w), make_output_grad(w)
     got, mlp = run_bwd(w, inp, dy)
     mlp.close()
@@ -147,9 +149,12 @@ def test_backward_llama_shape_sampled():
                                    w.order(), w.act)["dX"]
     cols = np.sort(np.random.default_rng(92).choice(w.f, 12, replace=False))
     refc = oracle.mlp_backward_columns(X, _np(inp.w_gate), _np(inp.w_up), _np(inp.w_down), dY, cols, w.act)
-    pairs = {"dX rows": (got["dX"][rows], ref_rows), "dW_gate cols": (got["dW_gate"][:, cols], refc["dW_gate"]),
-             "dW_up cols": (got["dW_up"][:, cols], refc["dW_up"]),
+    pairs = {"dX rows": (got["dX"][rows], ref_rows), "dW_up cols": (got["dW_up"][:, cols], refc["dW_up"]),
              "dW_down rows": (got["dW_down"][cols, :], refc["dW_down"])}
+    if w.act == "swiglu":
+        pairs["dW_gate cols"] = (got["dW_gate"][:, cols], refc["dW_gate"])
+    else:
+        assert got["dW_gate"] is None and refc["dW_gate"] is None
     for name, (g, r) in pairs.items():
         e2 = float(np.linalg.norm(g - r) / np.linalg.norm(r))
         em = float(np.max(np.abs(g - r)) / np.max(np.abs(r)))
