@@ -42,26 +42,47 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// One stage of a k-major weight tile ws[k][feature] (k < F32_KT, feature <
-// F32_MT) from a row-major matrix w (rows = reduction index, ld columns),
-// zero outside [k_lim) x [f_lim).
-__device__ __forceinline__ void load_w_tile(float (*ws)[F32_MT + 4], const float* __restrict__ w, int64_t ld,
-                                            int k0, int k_lim, int c0, int f_lim) {
-    for (int i = threadIdx.x; i < F32_KT * F32_MT; i += 256) {
-        const int r = i / F32_MT, c = i % F32_MT;
+// Stage loads go through registers so that the next stage's global loads are
+// in flight while the current stage's MFMAs run: fetch_* loads a thread's
+// share (8 values), put_* writes it to LDS. Shares: element i = tid + 256 j.
+constexpr int F32_PER = F32_KT * F32_MT / 256;          // values per thread per tile (8)
+static_assert(F32_KT * F32_MT == F32_NT * F32_KT, "tile sizes");
+
+// A k-major weight tile ws[k][feature] (k < F32_KT, feature < F32_MT) from a
+// row-major matrix w (rows = reduction index, ld columns), zero outside
+// [k_lim) x [f_lim).
+__device__ __forceinline__ void fetch_w(float (&v)[F32_PER], const float* __restrict__ w, int64_t ld, int k0,
+                                        int k_lim, int c0, int f_lim) {
+#pragma unroll
+    for (int j = 0; j < F32_PER; ++j) {
+        const int i = threadIdx.x + 256 * j, r = i / F32_MT, c = i % F32_MT;
         const int k = k0 + r, fc = c0 + c;
-        ws[r][c] = (k < k_lim && fc < f_lim) ? w[(int64_t)k * ld + fc] : 0.f;
+        v[j] = (k < k_lim && fc < f_lim) ? w[(int64_t)k * ld + fc] : 0.f;
     }
 }
-
-// One stage of a token tile xs[token][k] from a row-major activation matrix
-// (rows = tokens, ld columns, the stage's reduction indices at col0 + k0..).
-__device__ __forceinline__ void load_x_tile(float (*xs)[F32_KT + 1], const float* __restrict__ x, int64_t ld,
-                                            int64_t col0, int t0, int T, int k0, int k_lim) {
-    for (int i = threadIdx.x; i < F32_NT * F32_KT; i += 256) {
-        const int r = i / F32_KT, c = i % F32_KT;
+__device__ __forceinline__ void put_w(float (*ws)[F32_MT + 4], const float (&v)[F32_PER]) {
+#pragma unroll
+    for (int j = 0; j < F32_PER; ++j) {
+        const int i = threadIdx.x + 256 * j;
+        ws[i / F32_MT][i % F32_MT] = v[j];
+    }
+}
+// A token tile xs[token][k] from a row-major activation matrix (rows =
+// tokens, ld columns, the stage's reduction indices at col0 + k0..).
+__device__ __forceinline__ void fetch_x(float (&v)[F32_PER], const float* __restrict__ x, int64_t ld, int64_t col0,
+                                        int t0, int T, int k0, int k_lim) {
+#pragma unroll
+    for (int j = 0; j < F32_PER; ++j) {
+        const int i = threadIdx.x + 256 * j, r = i / F32_KT, c = i % F32_KT;
         const int tok = t0 + r, k = k0 + c;
-        xs[r][c] = (tok < T && k < k_lim) ? x[(int64_t)tok * ld + col0 + k] : 0.f;
+        v[j] = (tok < T && k < k_lim) ? x[(int64_t)tok * ld + col0 + k] : 0.f;
+    }
+}
+__device__ __forceinline__ void put_x(float (*xs)[F32_KT + 1], const float (&v)[F32_PER]) {
+#pragma unroll
+    for (int j = 0; j < F32_PER; ++j) {
+        const int i = threadIdx.x + 256 * j;
+        xs[i / F32_KT][i % F32_KT] = v[j];
     }
 }
 
@@ -86,11 +107,20 @@ __global__ __launch_bounds__(256) void gateup_f32(F32Args a) {
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < a.d; k0 += F32_KT) {
-        load_x_tile(xs, a.x, a.d, 0, t0, a.T, k0, a.d);
+    float xv[F32_PER], wv[NM][F32_PER];
+    fetch_x(xv, a.x, a.d, 0, t0, a.T, 0, a.d);
 #pragma unroll
-        for (int m = 0; m < NM; ++m) load_w_tile(ws[m], rec + m * dF, a.F, k0, a.d, c0, a.F);
+    for (int m = 0; m < NM; ++m) fetch_w(wv[m], rec + m * dF, a.F, 0, a.d, c0, a.F);
+    for (int k0 = 0; k0 < a.d; k0 += F32_KT) {
+        put_x(xs, xv);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) put_w(ws[m], wv[m]);
         __syncthreads();
+        if (k0 + F32_KT < a.d) {                         // the next stage's loads, in flight during the MFMAs
+            fetch_x(xv, a.x, a.d, 0, t0, a.T, k0 + F32_KT, a.d);
+#pragma unroll
+            for (int m = 0; m < NM; ++m) fetch_w(wv[m], rec + m * dF, a.F, k0 + F32_KT, a.d, c0, a.F);
+        }
 #pragma unroll
         for (int ks = 0; ks < F32_KT / 4; ++ks) {
             const int kk = ks * 4 + (lane >> 4);
@@ -144,27 +174,38 @@ __global__ __launch_bounds__(256) void down_f32(F32Args a) {
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int step = 0; step < a.P; ++step) {             // records and H columns in ring order
+    // stages: ring steps in order (records and H columns in ring order), each
+    // the group's hidden sub-range in F32_KT slices; the next stage's loads
+    // are in flight during the current stage's MFMAs
+    const int per_step = (kg1 - kg0 + F32_KT - 1) / F32_KT;
+    const int n_stages = a.P * per_step;
+    float hv[F32_PER], dv[F32_PER];
+    auto fetch = [&](int st) {
+        const int step = st / per_step, k0 = kg0 + (st - step * per_step) * F32_KT;
         const float* wd = a.packed + (int64_t)step * a.shard_elems + down_off;   // F x d
-        for (int k0 = kg0; k0 < kg1; k0 += F32_KT) {
-            load_x_tile(hs, a.h, a.f, (int64_t)step * a.F, t0, a.T, k0, kg1);
-            load_w_tile(ds, wd, a.d, k0, kg1, n0, a.d);
-            __syncthreads();
+        fetch_x(hv, a.h, a.f, (int64_t)step * a.F, t0, a.T, k0, kg1);
+        fetch_w(dv, wd, a.d, k0, kg1, n0, a.d);
+    };
+    if (n_stages > 0) fetch(0);
+    for (int st = 0; st < n_stages; ++st) {
+        put_x(hs, hv);
+        put_w(ds, dv);
+        __syncthreads();
+        if (st + 1 < n_stages) fetch(st + 1);
 #pragma unroll
-            for (int ks = 0; ks < F32_KT / 4; ++ks) {
-                const int kk = ks * 4 + (lane >> 4);
-                float bh[2];
+        for (int ks = 0; ks < F32_KT / 4; ++ks) {
+            const int kk = ks * 4 + (lane >> 4);
+            float bh[2];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) bh[j] = hs[wn * 32 + j * 16 + (lane & 15)][kk];
+            for (int j = 0; j < 2; ++j) bh[j] = hs[wn * 32 + j * 16 + (lane & 15)][kk];
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const float aw = ds[kk][wm * 32 + i * 16 + (lane & 15)];
+            for (int i = 0; i < 2; ++i) {
+                const float aw = ds[kk][wm * 32 + i * 16 + (lane & 15)];
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f32(aw, bh[j], acc[i][j]);
-                }
+                for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f32(aw, bh[j], acc[i][j]);
             }
-            __syncthreads();
         }
+        __syncthreads();
     }
     float* out = a.split > 1 ? a.part + (int64_t)g * a.T * a.d : a.y;
 #pragma unroll
