@@ -455,7 +455,7 @@ __global__ __launch_bounds__(256) void gateup_w16(Bf16Args a, int n_ft_shard, in
     }
 }
 
-template <bool BLK>
+template <bool BLK, bool BUF>
 __global__ __launch_bounds__(256) void down_w16(Bf16Args a, int n_ft, int n_tt, int split) {
     using namespace w16;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
@@ -477,9 +477,9 @@ __global__ __launch_bounds__(256) void down_w16(Bf16Args a, int n_ft, int n_tt, 
     const int t0 = ttile * BN;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w / WN, wn = w % WN;
-    PackedSrc<false, BLK> src{a_ft, 0, 0, steps_per_group * spp, spp, a.shard_elems, a_rs, h_g, a.f, t0, a.T,
+    PackedSrc<BUF, BLK> src{a_ft, 0, 0, steps_per_group * spp, spp, a.shard_elems, a_rs, h_g, a.f, t0, a.T,
                               __builtin_amdgcn_readfirstlane(w), wm, wn, lane};
-    src.nbt = a.nbt;
+    src.set_blocked(a.nbt);
     f32x4 acc[TM][TN];
     w16::mainloop5(lds, acc, steps_per_group * spp, src);
 
@@ -645,8 +645,16 @@ hipError_t launch_down_tiled(const Bf16Args& a, int cfg, int split, hipStream_t 
         case 0: {
             const int n_ft = a.d / 256, n_tt = (int)cdiv(a.T, 256);
             const dim3 grid((unsigned)(n_ft * n_tt * split));
-            if (a.nbt) hipLaunchKernelGGL(down_w16<true>, grid, dim3(256), 0, st, a, n_ft, n_tt, split);
-            else hipLaunchKernelGGL(down_w16<false>, grid, dim3(256), 0, st, a, n_ft, n_tt, split);
+            // buffer offsets are 32-bit: one stage's weight slab (8 rows of
+            // 32 x F-element blocks) and the operand H must each span < 2^31
+            // bytes from their resource bases (blocked H: one column block of
+            // nbt 1 KiB token blocks; row-major H: T x f)
+            const bool buf = (int64_t)a.F * 512 < (int64_t(1) << 31) &&
+                             (a.nbt ? (int64_t)a.nbt * 1024 : (int64_t)a.T * a.f * 2) < (int64_t(1) << 31);
+#define TSP_DN(BLK, BUF) hipLaunchKernelGGL((down_w16<BLK, BUF>), grid, dim3(256), 0, st, a, n_ft, n_tt, split)
+            if (a.nbt) { if (buf) TSP_DN(true, true); else TSP_DN(true, false); }
+            else { if (buf) TSP_DN(false, true); else TSP_DN(false, false); }
+#undef TSP_DN
             return hipGetLastError();
         }
         case 1: if (a.nbt) return hipErrorInvalidValue; return down_go<256, 128, 4, 2>(a, st);
