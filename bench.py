@@ -19,7 +19,11 @@ timed region (which has events only at step boundaries).
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 workload on this host's cores. ``--pass backward`` times the backward instead
 (one step = the gradients for a seeded output gradient; TFLOP/s over the
-gradient products, the recomputed forward product not counted).
+gradient products, the recomputed forward product not counted); its
+``variants`` time, in the same process, the backward from the pre-activations
+a training forward saved (no recomputation), and whole training steps
+(forward + backward, TFLOP/s over both passes' algorithmic flops) with and
+without saving them.
 ``--pass attention`` times one rank's TSP attention block instead (default
 workload: the Llama-3-8B attention shape, rank 3 of 8, causal; one step =
 the Q/K/V projection of the rank's tokens, attention over the context that
@@ -55,6 +59,8 @@ KERNEL_SOURCES = {
     "bwd_gateup": ["backward.hip", "w16.h", "common.h"],
     "bwd_dw_dx": ["backward.hip", "w16.h", "common.h"],
     "bwd_transpose_in": ["backward.hip", "common.h"],
+    "bwd_saved": ["backward.hip", "w16.h", "common.h"],
+    "gateup_save": ["gemm_tiled.hip", "w16.h", "common.h"],
     "attn_qkv": ["attn.hip", "w16.h", "common.h"],
     "attn_core": ["attn_core.hip", "w16.h", "common.h"],
     "attn_out": ["gemm_tiled.hip", "w16.h", "common.h"],
@@ -101,6 +107,10 @@ def kernel_work(w, kernel: str, T: int):
                 + n_gu * d * f * es + n_gu * T * f * es + T * d * 4)                  # dX: Wg/Wu, dG/dU in, dX out
     if kernel == "bwd_transpose_in":        # copies of X and dY: each byte read and written once
         return 0, 2 * 2 * T * d * es
+    if kernel == "bwd_saved":               # the backward epilogue on saved pre-activations (no product)
+        return 0, n_gu * T * f * 4 + T * f * 4 + (n_gu + 1) * T * f * es
+    if kernel == "gateup_save":             # the gate/up product that also writes its pre-activations
+        return 2 * n_gu * T * d * f, n_gu * d * f * es + T * d * es + T * f * es + n_gu * T * f * 4
     if kernel in ("gateup_tiled", "skinny_gateup", "gateup_f32"):
         flops = 2 * T * w.d * w.f * n_gu
         byts = n_gu * w.d * w.f * es + T * w.d * es + T * w.f * es      # W_gu, X, H out
@@ -428,9 +438,13 @@ def step_stats(per):
     return {"median_ms": med, "min_ms": s[0], "max_ms": s[-1], "first_ms": per[0]}
 
 
-def measure_mlp(w, args, backward: bool = False, with_cpu: bool = False):
+def measure_mlp(w, args, backward: bool = False, with_cpu: bool = False, variant: str = ""):
     """One workload's timed region, kernel region and roofline (a dict in the
-    shape of the bench's JSON line)."""
+    shape of the bench's JSON line). variant (with backward): "" = the
+    backward recomputing the gate/up product, "saved" = the backward from the
+    pre-activations a training forward kept, "train" = forward + backward
+    (recomputing), "train_saved" = training forward + backward from its
+    saved pre-activations."""
     import torch
     from sharded_transformer_mlp_amd.binding import TspMLP
     from sharded_transformer_mlp_amd.inputs import make_inputs, make_output_grad
@@ -460,8 +474,28 @@ def measure_mlp(w, args, backward: bool = False, with_cpu: bool = False):
                  "dW_up": torch.empty(w.d, w.f, dtype=torch.float32, device=dev),
                  "dW_down": torch.empty(w.f, w.d, dtype=torch.float32, device=dev)}
 
-        def step():
-            mlp.backward(x, dy_dev, out=grads)
+        saved = None
+        if variant in ("saved", "train_saved"):
+            saved = torch.empty(mlp.saved_bytes(w.T), dtype=torch.uint8, device=dev)
+            y = torch.empty(w.T, w.d, dtype=torch.float32, device=dev)
+            mlp.forward_train(x, saved=saved, y=y)     # the step reads these
+        elif variant == "train":
+            y = torch.empty(w.T, w.d, dtype=torch.float32, device=dev)
+
+        if variant == "saved":
+            def step():
+                mlp.backward(x, dy_dev, out=grads, saved=saved)
+        elif variant == "train":
+            def step():
+                mlp.forward(x, y)
+                mlp.backward(x, dy_dev, out=grads)
+        elif variant == "train_saved":
+            def step():
+                mlp.forward_train(x, saved=saved, y=y)
+                mlp.backward(x, dy_dev, out=grads, saved=saved)
+        else:
+            def step():
+                mlp.backward(x, dy_dev, out=grads)
     else:
         y = torch.empty(w.T, w.d, dtype=torch.float32, device=dev)
 
@@ -493,6 +527,8 @@ def measure_mlp(w, args, backward: bool = False, with_cpu: bool = False):
     if backward:
         import oracle
         flops_step = oracle.backward_flops(w.T, w.d, w.f, w.act)
+        if variant.startswith("train"):
+            flops_step += w.flops()
         value, unit = flops_step / (ms * 1e-3) / 1e12, "TFLOP/s"
     elif decode:
         value, unit = w.bytes() / (ms * 1e-3) / 1e9, "GB/s"
@@ -534,7 +570,10 @@ def measure_mlp(w, args, backward: bool = False, with_cpu: bool = False):
     }
     if backward:
         out["config"]["parallelism"] = "one TSP rank's backward (shard loop on one GPU)"
-        del grads, dy_dev
+        out["variant"] = variant or "recompute"
+        if saved is not None:
+            out["saved_bytes"] = saved.numel()
+        del grads, dy_dev, saved
     else:
         del y
     mlp.close()
@@ -610,6 +649,13 @@ def main():
     out["cpu_baseline"] = None
     if backward:
         out["pass"] = "backward"
+        # the same backward from saved pre-activations, and whole training
+        # steps (forward + backward) both ways, same process and --steps/--warmup
+        out["variants"] = {}
+        for v in ("saved", "train", "train_saved"):
+            rv = measure_mlp(w, args, backward=True, variant=v)
+            out["variants"][v] = {k: rv[k] for k in ("value", "unit", "ms_per_step", "median_ms", "min_ms",
+                                                     "kernels_ms", "kernel_sum_ms", "saved_bytes") if k in rv}
     also = [a for a in args.also.split(",") if a.strip()] if not backward else []
     if also:
         out["also"] = []

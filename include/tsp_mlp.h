@@ -174,6 +174,45 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
                               float* dX, float* dW_gate, float* dW_up, float* dW_down,
                               hipStream_t stream);
 
+/*
+ * The backward from saved pre-activations instead of recomputing them: the
+ * same training step ("Folding Tensor and Sequence Parallelism ...",
+ * Abstract; "Tensor Parallelism: Splitting the Math", the paragraph after the
+ * walk-through) with the gate and up pre-activations G_s, U_s that the
+ * forward computes kept in device memory until the backward, trading
+ * tsp_mlp_saved_bytes of memory for the backward's recomputation of the
+ * gate/up product (a quarter of its matrix work).
+ *
+ * tsp_mlp_saved_bytes: *bytes = the size of the saved buffer for T tokens
+ * (fp32 pre-activations of whole 256-token tiles: P * ceil(T / 256) * n * 256
+ * KiB, n = 2F / 256 for SwiGLU, F / 256 for GeLU). TSP_ERR_INVALID_ARG for a
+ * NULL argument or T outside [0, T_max].
+ *
+ * tsp_mlp_forward_train: tsp_mlp_forward (Y bit for bit the same as
+ * tsp_mlp_forward's with the same tile settings for the down product) that
+ * also writes the pre-activations to `saved`, a caller-owned device buffer of
+ * saved_bytes >= tsp_mlp_saved_bytes(T) bytes, 16-byte aligned, overlapping
+ * neither X nor Y. Its layout is private to the library. It always runs the
+ * gate/up product on the tiled kernel of shape 0 (path and gate/up tile
+ * settings do not apply). bf16 handles with d % 256 == 0 and F % 256 == 0
+ * (TSP_ERR_UNSUPPORTED otherwise); other errors as tsp_mlp_forward, plus
+ * TSP_ERR_INVALID_ARG for a NULL, misaligned, too small or overlapping saved.
+ *
+ * tsp_mlp_backward_saved: tsp_mlp_backward with the pre-activations read from
+ * `saved` (saved_bytes as above), which must hold what tsp_mlp_forward_train
+ * wrote for the same handle, T and X (the library cannot check this; other
+ * contents give wrong gradients). The gradients are bit for bit those of
+ * tsp_mlp_backward. Arguments and errors as tsp_mlp_backward, plus
+ * TSP_ERR_INVALID_ARG for a NULL, misaligned or too small saved, or an output
+ * overlapping it. saved is only read.
+ */
+tsp_status_t tsp_mlp_saved_bytes(tsp_mlp_t h, int64_t T, int64_t* bytes);
+tsp_status_t tsp_mlp_forward_train(tsp_mlp_t h, int64_t T, const void* X, float* Y, void* saved,
+                                   int64_t saved_bytes, hipStream_t stream);
+tsp_status_t tsp_mlp_backward_saved(tsp_mlp_t h, int64_t T, const void* X, const void* dY,
+                                    const void* saved, int64_t saved_bytes, float* dX, float* dW_gate,
+                                    float* dW_up, float* dW_down, hipStream_t stream);
+
 /* Synchronise the handle's stream and free everything it owns. NULL is a no-op. */
 tsp_status_t tsp_mlp_destroy(tsp_mlp_t h);
 

@@ -26,6 +26,9 @@ SIGNATURES = {
     "tsp_mlp_forward": (_i32, [_vp, _i64, _vp, _vp, _vp]),
     "tsp_mlp_forward_static": (_i32, [_vp, _i64, _vp, _vp, _vp]),
     "tsp_mlp_backward": (_i32, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "tsp_mlp_saved_bytes": (_i32, [_vp, _i64, ctypes.POINTER(_i64)]),
+    "tsp_mlp_forward_train": (_i32, [_vp, _i64, _vp, _vp, _vp, _i64, _vp]),
+    "tsp_mlp_backward_saved": (_i32, [_vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp]),
     "tsp_mlp_destroy": (_i32, [_vp]),
     "tsp_mlp_set_path": (_i32, [_vp, _i32]),
     "tsp_mlp_set_tiles": (_i32, [_vp, _i32, _i32]),
@@ -185,11 +188,38 @@ class TspMLP:
 
     __call__ = forward
 
-    def backward(self, x, dy, out=None, stream=None):
+    def saved_bytes(self, T: int) -> int:
+        """Bytes of the saved pre-activations forward_train keeps for T tokens."""
+        n = _i64()
+        check(lib().tsp_mlp_saved_bytes(self.handle, int(T), ctypes.byref(n)))
+        return n.value
+
+    def forward_train(self, x, saved=None, y=None, stream=None):
+        """forward() that also keeps the gate/up pre-activations for
+        backward(..., saved=...): returns (y, saved), saved a uint8 CUDA
+        tensor of saved_bytes(T) bytes (allocated when not given)."""
+        import torch
+        T = x.shape[0]
+        if x.dtype != self.tdtype or not x.is_cuda or not x.is_contiguous() or x.shape[1] != self.d:
+            raise ValueError("x must be a contiguous CUDA tensor T x d of the handle's dtype")
+        if y is None:
+            y = torch.empty(T, self.d, dtype=torch.float32, device=x.device)
+        elif y.dtype != torch.float32 or not y.is_contiguous() or tuple(y.shape) != (T, self.d):
+            raise ValueError("y must be a contiguous fp32 T x d tensor")
+        if saved is None:
+            saved = torch.empty(self.saved_bytes(T), dtype=torch.uint8, device=x.device)
+        elif not saved.is_cuda or not saved.is_contiguous():
+            raise ValueError("saved must be a contiguous CUDA tensor")
+        check(lib().tsp_mlp_forward_train(self.handle, T, x.data_ptr(), y.data_ptr(), saved.data_ptr(),
+                                          saved.numel() * saved.element_size(), _stream_ptr(stream)))
+        return y, saved
+
+    def backward(self, x, dy, out=None, stream=None, saved=None):
         """Gradients for output gradient dy: {"dX", "dW_gate", "dW_up",
         "dW_down"} (fp32 CUDA tensors; dW_gate is None for GeLU) of the
         weights the handle holds. ``out``: a dict of that form to write into
-        instead of new tensors."""
+        instead of new tensors. ``saved``: the pre-activations forward_train
+        kept for the same x (no recomputation)."""
         import torch
         T = x.shape[0]
         for t in (x, dy):
@@ -212,8 +242,15 @@ class TspMLP:
             dWu = torch.empty(self.d, self.f, dtype=torch.float32, device=dev)
             dWd = torch.empty(self.f, self.d, dtype=torch.float32, device=dev)
         ptr = lambda t: None if t is None else t.data_ptr()
-        check(lib().tsp_mlp_backward(self.handle, T, x.data_ptr(), dy.data_ptr(), dX.data_ptr(), ptr(dWg),
-                                     dWu.data_ptr(), dWd.data_ptr(), _stream_ptr(stream)))
+        if saved is None:
+            check(lib().tsp_mlp_backward(self.handle, T, x.data_ptr(), dy.data_ptr(), dX.data_ptr(), ptr(dWg),
+                                         dWu.data_ptr(), dWd.data_ptr(), _stream_ptr(stream)))
+        else:
+            if not saved.is_cuda or not saved.is_contiguous():
+                raise ValueError("saved must be a contiguous CUDA tensor")
+            check(lib().tsp_mlp_backward_saved(self.handle, T, x.data_ptr(), dy.data_ptr(), saved.data_ptr(),
+                                               saved.numel() * saved.element_size(), dX.data_ptr(), ptr(dWg),
+                                               dWu.data_ptr(), dWd.data_ptr(), _stream_ptr(stream)))
         return {"dX": dX, "dW_gate": dWg, "dW_up": dWu, "dW_down": dWd}
 
     def sizes(self):

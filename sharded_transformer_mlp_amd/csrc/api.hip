@@ -296,11 +296,15 @@ struct FwdPlan {
     int64_t h_bytes = 0, part_off = 0, total = 0;
 };
 
-tsp_status_t plan_forward(const tsp_mlp* h, int64_t T, FwdPlan& pl) {
+// train: the forward that saves the gate/up pre-activations, which only the
+// tiled gate/up kernel of shape 0 does (whatever the path and tile settings).
+tsp_status_t plan_forward(const tsp_mlp* h, int64_t T, FwdPlan& pl, bool train = false) {
     const int64_t d = h->d, f = h->f;
     if (h->dtype == TSP_DTYPE_BF16) {
         const bool sk_ok = T <= tsp::SKINNY_T_MAX && tsp::skinny_supported((int)d, (int)h->F, h->P);
-        if (h->path == TSP_PATH_SKINNY) {
+        if (train) {
+            pl.skinny = false;
+        } else if (h->path == TSP_PATH_SKINNY) {
             if (!sk_ok) return fail(TSP_ERR_UNSUPPORTED, "skinny path needs T <= %d, d %% 256 == 0 and P*F %% 1024 == 0", tsp::SKINNY_T_MAX);
             pl.skinny = true;
         } else if (h->path == TSP_PATH_AUTO) {
@@ -310,7 +314,7 @@ tsp_status_t plan_forward(const tsp_mlp* h, int64_t T, FwdPlan& pl) {
             pl.h_bytes = (T + 31) / 32 * 32 * f * 2;
         } else {
             const int swiglu = h->act == TSP_ACT_SWIGLU ? 1 : 0;
-            pl.cg = h->cfg_gateup >= 0 ? h->cfg_gateup : tsp::choose_gateup_cfg((int)T, (int)d, (int)h->F, h->P, swiglu);
+            pl.cg = train ? 0 : h->cfg_gateup >= 0 ? h->cfg_gateup : tsp::choose_gateup_cfg((int)T, (int)d, (int)h->F, h->P, swiglu);
             pl.cd = h->cfg_down >= 0 ? h->cfg_down : tsp::choose_down_cfg((int)T, (int)d, (int)h->F, h->P);
             if (pl.cg < 0 || pl.cd < 0) return fail(TSP_ERR_UNSUPPORTED, "no tile shape fits d=%lld F=%lld", (long long)d, (long long)h->F);
             pl.split = tsp::choose_down_split((int)T, (int)d, h->P, pl.cd);
@@ -344,8 +348,9 @@ tsp_status_t check_forward_args(const tsp_mlp* h, int64_t T, const void* X, cons
 // The forward's launches with the workspace at `work` (hidden activations at
 // 0, split partials at pl.part_off). timing = false launches nothing but the
 // kernels (no events are created or recorded).
+// save: the gate/up accumulators go there too (tile shape 0 only).
 tsp_status_t run_forward(tsp_mlp* h, int64_t T, const void* X, float* Y, hipStream_t st, const FwdPlan& pl,
-                         void* work, bool timing) {
+                         void* work, bool timing, float* save = nullptr) {
     const bool swiglu = h->act == TSP_ACT_SWIGLU;
     const bool saved = h->timing;
     h->timing = h->timing && timing;
@@ -363,12 +368,14 @@ tsp_status_t run_forward(tsp_mlp* h, int64_t T, const void* X, float* Y, hipStre
         a.T = (int)T; a.d = (int)h->d; a.f = (int)h->f; a.F = (int)h->F; a.P = h->P;
         a.swiglu = swiglu ? 1 : 0;
         a.nbt = pl.nbt;
+        a.save = save;
         if (pl.skinny) {
             s = timed_launch(h, "skinny_gateup", st, [&] { return tsp::launch_gateup_skinny(a, st); });
             if (s != TSP_OK) return s;
             return timed_launch(h, "skinny_down", st, [&] { return tsp::launch_down_skinny(a, st); });
         }
-        s = timed_launch(h, "gateup_tiled", st, [&] { return tsp::launch_gateup_tiled(a, pl.cg, st); });
+        s = timed_launch(h, save ? "gateup_save" : "gateup_tiled", st,
+                         [&] { return tsp::launch_gateup_tiled(a, pl.cg, st); });
         if (s != TSP_OK) return s;
         s = timed_launch(h, "down_tiled", st, [&] { return tsp::launch_down_tiled(a, pl.cd, pl.split, st); });
         if (s != TSP_OK || pl.split == 1) return s;
@@ -507,8 +514,10 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 
 }  // namespace
 
-tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void* dY, float* dX, float* dW_gate,
-                              float* dW_up, float* dW_down, hipStream_t stream) {
+// The backward, from recomputed (saved == nullptr) or saved pre-activations.
+static tsp_status_t backward_impl(tsp_mlp_t h, int64_t T, const void* X, const void* dY, const void* saved,
+                                  int64_t saved_bytes, float* dX, float* dW_gate, float* dW_up, float* dW_down,
+                                  hipStream_t stream) {
     if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
     if (T < 0 || T > h->T_max) return fail(TSP_ERR_INVALID_ARG, "T=%lld out of [0, T_max=%lld]", (long long)T, (long long)h->T_max);
     if (h->dtype != TSP_DTYPE_BF16) return fail(TSP_ERR_UNSUPPORTED, "the backward is bf16 only");
@@ -523,15 +532,22 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
         if (q && !aligned16(q)) return fail(TSP_ERR_INVALID_ARG, "every pointer must be 16-byte aligned");
     const int64_t d = h->d, f = h->f;
     struct Span { const void* p; int64_t n; };
+    const int64_t need_saved = tsp::gateup_saved_bytes(T, h->F, h->P, swiglu ? 1 : 0);
+    if (saved) {
+        if (!aligned16(saved)) return fail(TSP_ERR_INVALID_ARG, "every pointer must be 16-byte aligned");
+        if (saved_bytes < need_saved)
+            return fail(TSP_ERR_INVALID_ARG, "saved holds %lld bytes; T=%lld needs %lld", (long long)saved_bytes,
+                        (long long)T, (long long)need_saved);
+    }
     const Span outs[] = {{dX, T * d * 4}, {dW_gate, d * f * 4}, {dW_up, d * f * 4}, {dW_down, f * d * 4}};
-    const Span ins[] = {{X, T * d * 2}, {dY, T * d * 2}};
+    const Span ins[] = {{X, T * d * 2}, {dY, T * d * 2}, {saved, saved ? need_saved : 0}};
     for (int i = 0; i < 4; ++i) {
         if (!outs[i].p) continue;
         for (int j = i + 1; j < 4; ++j)
             if (outs[j].p && overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n))
                 return fail(TSP_ERR_INVALID_ARG, "gradient outputs overlap each other");
         for (const Span& in : ins)
-            if (overlaps(outs[i].p, outs[i].n, in.p, in.n))
+            if (in.p && overlaps(outs[i].p, outs[i].n, in.p, in.n))
                 return fail(TSP_ERR_INVALID_ARG, "a gradient output overlaps an input");
     }
     hipStream_t st = stream ? stream : h->stream;
@@ -597,8 +613,8 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
     a.down_off = h->down_off;
     a.T = (int)T; a.d = (int)d; a.f = (int)f; a.F = F; a.P = P;
     a.swiglu = swiglu ? 1 : 0;
-    tsp::BwdArgs b{dh, dg, du, dgt, dut, ht, Tp, h->order_dev};
-    s = timed_launch(h, "bwd_gateup", st, [&] { return tsp::launch_gateup_bwd(a, b, st); });
+    tsp::BwdArgs b{dh, dg, du, dgt, dut, ht, Tp, h->order_dev, static_cast<const float*>(saved)};
+    s = timed_launch(h, saved ? "bwd_saved" : "bwd_gateup", st, [&] { return tsp::launch_gateup_bwd(a, b, st); });
     if (s != TSP_OK) return s;
     // dX[t][i] = sum over ring steps k of dG_k[t] . Wg[i][order[k] F ..] + dU_k[t] . Wu[i][..]
     tsp::NtArgs q{};
@@ -632,6 +648,53 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
     ws[nw++] = dw(dyt, ht, (int)d, (int)f, dW_down, d, 2);               // dW_down[c][n]
     ws[nw++] = q;
     return timed_launch(h, "bwd_dw_dx", st, [&] { return tsp::launch_nt(ws, nw, st); });
+}
+
+tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void* dY, float* dX, float* dW_gate,
+                              float* dW_up, float* dW_down, hipStream_t stream) {
+    return backward_impl(h, T, X, dY, nullptr, 0, dX, dW_gate, dW_up, dW_down, stream);
+}
+
+tsp_status_t tsp_mlp_saved_bytes(tsp_mlp_t h, int64_t T, int64_t* bytes) {
+    if (!h || !bytes) return fail(TSP_ERR_INVALID_ARG, "handle or bytes is NULL");
+    if (T < 0 || T > h->T_max) return fail(TSP_ERR_INVALID_ARG, "T=%lld out of [0, T_max=%lld]", (long long)T, (long long)h->T_max);
+    *bytes = tsp::gateup_saved_bytes(T, h->F, h->P, h->act == TSP_ACT_SWIGLU ? 1 : 0);
+    return TSP_OK;
+}
+
+tsp_status_t tsp_mlp_forward_train(tsp_mlp_t h, int64_t T, const void* X, float* Y, void* saved, int64_t saved_bytes,
+                                   hipStream_t stream) {
+    if (!h) return fail(TSP_ERR_INVALID_ARG, "handle is NULL");
+    if (T < 0 || T > h->T_max) return fail(TSP_ERR_INVALID_ARG, "T=%lld out of [0, T_max=%lld]", (long long)T, (long long)h->T_max);
+    if (h->dtype != TSP_DTYPE_BF16) return fail(TSP_ERR_UNSUPPORTED, "saved activations are bf16 only");
+    if (h->d % 256 || h->F % 256) return fail(TSP_ERR_UNSUPPORTED, "saved activations need d %% 256 == 0 and F %% 256 == 0");
+    if (T == 0) return TSP_OK;
+    tsp_status_t s = check_forward_args(h, T, X, Y);
+    if (s != TSP_OK) return s;
+    if (!saved) return fail(TSP_ERR_INVALID_ARG, "saved is NULL");
+    if (!aligned16(saved)) return fail(TSP_ERR_INVALID_ARG, "saved must be 16-byte aligned");
+    const int64_t need = tsp::gateup_saved_bytes(T, h->F, h->P, h->act == TSP_ACT_SWIGLU ? 1 : 0);
+    if (saved_bytes < need)
+        return fail(TSP_ERR_INVALID_ARG, "saved holds %lld bytes; T=%lld needs %lld", (long long)saved_bytes,
+                    (long long)T, (long long)need);
+    if (overlaps(saved, need, X, T * h->d * 2) || overlaps(saved, need, Y, T * h->d * 4))
+        return fail(TSP_ERR_INVALID_ARG, "saved overlaps X or Y");
+    FwdPlan pl;
+    s = plan_forward(h, T, pl, true);
+    if (s != TSP_OK) return s;
+    if (pl.h_bytes > h->part_off || pl.total - pl.part_off > h->work_bytes - h->part_off)
+        return fail(TSP_ERR_HIP, "internal: the forward's workspace exceeds the handle's");
+    pl.part_off = h->part_off;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return fail(TSP_ERR_HIP, "cannot select the handle's device");
+    return run_forward(h, T, X, Y, stream ? stream : h->stream, pl, h->work, true, static_cast<float*>(saved));
+}
+
+tsp_status_t tsp_mlp_backward_saved(tsp_mlp_t h, int64_t T, const void* X, const void* dY, const void* saved,
+                                    int64_t saved_bytes, float* dX, float* dW_gate, float* dW_up, float* dW_down,
+                                    hipStream_t stream) {
+    if (h && T > 0 && !saved) return fail(TSP_ERR_INVALID_ARG, "saved is NULL");
+    return backward_impl(h, T, X, dY, saved, saved_bytes, dX, dW_gate, dW_up, dW_down, stream);
 }
 
 tsp_status_t tsp_mlp_destroy(tsp_mlp_t h) {

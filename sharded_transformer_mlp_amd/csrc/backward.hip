@@ -167,7 +167,10 @@ __global__ __launch_bounds__(256) void nt_w16(NtGroup grp) {
 // 1 + tanh(z2 / 2) = 2 sigma2). Reciprocals use v_rcp_f32 as in the forward.
 __device__ inline float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
-template <int ACT, bool BUF>
+// SAVED: the accumulators come from a forward's saved pre-activations
+// (b.saved, w16::save_acc's layout, bit for bit what the product would give)
+// instead of the product, and the epilogue is the same.
+template <int ACT, bool BUF, bool SAVED>
 __global__ __launch_bounds__(256) void gateup_bwd_w16(Bf16Args a, BwdArgs b, int n_ft_shard, int n_tt) {
     using namespace w16;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
@@ -184,7 +187,8 @@ __global__ __launch_bounds__(256) void gateup_bwd_w16(Bf16Args a, BwdArgs b, int
     PackedSrc<BUF> src{a_tile, 0, 0, a.d >> 5, 0, 0, a_rs, a.x, a.d, t0, a.T,
                        __builtin_amdgcn_readfirstlane(w), wm, wn, lane};
     f32x4 acc[TM][TN];
-    w16::mainloop(lds, acc, a.d >> 5, src);
+    if constexpr (SAVED) load_acc(b.saved, (int64_t)flin * n_tt + ttile, __builtin_amdgcn_readfirstlane(w), lane, acc);
+    else w16::mainloop(lds, acc, a.d >> 5, src);
 
     // Epilogue. The tile covers hidden columns [lc0, lc0 + COLS) of shard
     // order[k] (COLS = 128 for SwiGLU, 256 for GeLU): dH is read at the shard's
@@ -335,14 +339,23 @@ hipError_t launch_gateup_bwd(const Bf16Args& a, const BwdArgs& b, hipStream_t st
     const int n_ft_shard = ngu / 256, n_tt = (int)cdiv64(a.T, 256);
     const dim3 grid((unsigned)(a.P * n_ft_shard * n_tt));
     const bool buf = (int64_t)a.T * a.d * 2 < (int64_t(1) << 31) && (int64_t)a.d * 512 < (int64_t(1) << 31);
+#define TSP_GB(ACT, BUF, SAVED) hipLaunchKernelGGL((gateup_bwd_w16<ACT, BUF, SAVED>), grid, dim3(256), 0, st, a, b, n_ft_shard, n_tt)
     if (a.swiglu) {
-        if (buf) hipLaunchKernelGGL((gateup_bwd_w16<1, true>), grid, dim3(256), 0, st, a, b, n_ft_shard, n_tt);
-        else hipLaunchKernelGGL((gateup_bwd_w16<1, false>), grid, dim3(256), 0, st, a, b, n_ft_shard, n_tt);
+        if (b.saved) TSP_GB(1, true, true);
+        else if (buf) TSP_GB(1, true, false);
+        else TSP_GB(1, false, false);
     } else {
-        if (buf) hipLaunchKernelGGL((gateup_bwd_w16<2, true>), grid, dim3(256), 0, st, a, b, n_ft_shard, n_tt);
-        else hipLaunchKernelGGL((gateup_bwd_w16<2, false>), grid, dim3(256), 0, st, a, b, n_ft_shard, n_tt);
+        if (b.saved) TSP_GB(2, true, true);
+        else if (buf) TSP_GB(2, true, false);
+        else TSP_GB(2, false, false);
     }
+#undef TSP_GB
     return hipGetLastError();
+}
+
+int64_t gateup_saved_bytes(int64_t T, int64_t F, int P, int swiglu) {
+    const int64_t n_ft_shard = (swiglu ? 2 * F : F) / 256, n_tt = cdiv64(T, 256);
+    return (int64_t)P * n_ft_shard * n_tt * w16::BM * w16::BN * 4;
 }
 
 }  // namespace tsp

@@ -391,7 +391,8 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(1,
 // registers, and of a persistent grid that streams the next tile's first
 // stages during the epilogue.
 
-template <int ACT, bool BUF, bool BLK>
+// SAVE: the accumulators (pre-activations) also go to a.save (w16::save_acc).
+template <int ACT, bool BUF, bool BLK, bool SAVE>
 __global__ __launch_bounds__(256) void gateup_w16(Bf16Args a, int n_ft_shard, int n_tt) {
     using namespace w16;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
@@ -409,6 +410,8 @@ __global__ __launch_bounds__(256) void gateup_w16(Bf16Args a, int n_ft_shard, in
                        __builtin_amdgcn_readfirstlane(w), wm, wn, lane};
     f32x4 acc[TM][TN];
     w16::mainloop(lds, acc, a.d >> 5, src);
+    // the pre-activations for a backward, before the epilogue consumes them
+    if constexpr (SAVE) save_acc(a.save, (int64_t)flin * n_tt + ttile, __builtin_amdgcn_readfirstlane(w), lane, acc);
 
     // H through the LDS ring (StagedRows16): every wave's last fragment reads
     // are done at the first barrier, its LDS writes at the second
@@ -621,7 +624,11 @@ hipError_t launch_gateup_tiled(const Bf16Args& a, int cfg, hipStream_t st) {
             // slab (8 rows of 32 x d-element blocks) must each span < 2^31 bytes
             const bool buf = (int64_t)a.T * a.d * 2 < (int64_t(1) << 31) && (int64_t)a.d * 512 < (int64_t(1) << 31);
             const bool blk = a.nbt > 0;
-#define TSP_GU(ACT, BUF, BLK) hipLaunchKernelGGL((gateup_w16<ACT, BUF, BLK>), grid, dim3(256), 0, st, a, n_ft_shard, n_tt)
+#define TSP_GU(ACT, BUF, BLK)                                                                             \
+    do {                                                                                                  \
+        if (a.save) hipLaunchKernelGGL((gateup_w16<ACT, BUF, BLK, true>), grid, dim3(256), 0, st, a, n_ft_shard, n_tt); \
+        else hipLaunchKernelGGL((gateup_w16<ACT, BUF, BLK, false>), grid, dim3(256), 0, st, a, n_ft_shard, n_tt);     \
+    } while (0)
             if (a.swiglu) {
                 if (buf) { if (blk) TSP_GU(1, true, true); else TSP_GU(1, true, false); }
                 else { if (blk) TSP_GU(1, false, true); else TSP_GU(1, false, false); }
@@ -632,9 +639,9 @@ hipError_t launch_gateup_tiled(const Bf16Args& a, int cfg, hipStream_t st) {
 #undef TSP_GU
             return hipGetLastError();
         }
-        case 1: if (a.nbt) return hipErrorInvalidValue; return gateup_go<256, 128, 4, 2>(a, st);
-        case 2: if (a.nbt) return hipErrorInvalidValue; return gateup_go<128, 128, 2, 2>(a, st);
-        case 3: if (a.nbt) return hipErrorInvalidValue; return gateup_go<64, 128, 1, 4>(a, st);
+        case 1: if (a.nbt || a.save) return hipErrorInvalidValue; return gateup_go<256, 128, 4, 2>(a, st);
+        case 2: if (a.nbt || a.save) return hipErrorInvalidValue; return gateup_go<128, 128, 2, 2>(a, st);
+        case 3: if (a.nbt || a.save) return hipErrorInvalidValue; return gateup_go<64, 128, 1, 4>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

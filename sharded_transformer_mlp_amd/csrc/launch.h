@@ -24,6 +24,10 @@ struct Bf16Args {
     // nbt = ceil(T / 16); 0 = H row-major T x f. Only the 256 x 256 kernels
     // (tile shape 0 for both products) take the blocked layout.
     int nbt = 0;
+    // Tile shape 0 gate/up only, may be null: every tile's accumulators (the
+    // gate and up pre-activations, fp32) in the saved-activation layout (see
+    // w16::save_acc), gateup_saved_bytes(T, F, P, swiglu) bytes.
+    float* save = nullptr;
 };
 
 struct F32Args {
@@ -104,6 +108,9 @@ struct BwdArgs {
     uint16_t* ht;             // H transposed, f x ldt row-major, tokens contiguous
     int ldt;                  // T rounded up to 64; columns T..ldt-1 hold finite values
     const int32_t* order;     // ring order (device)
+    // null: recompute the gate/up product; else the accumulators a forward
+    // saved (Bf16Args::save) for the same weights, T and X
+    const float* saved = nullptr;
 };
 // frag: dst in 32 x 16 fragment blocks (C rows x R_pad reduction indices)
 // instead of row-major C x R_pad.
@@ -120,6 +127,9 @@ struct NtGroup {
 };
 hipError_t launch_nt(const NtArgs* probs, int n, hipStream_t st);
 hipError_t launch_gateup_bwd(const Bf16Args& a, const BwdArgs& b, hipStream_t st);
+// Bytes of the saved gate/up accumulators for T tokens: one 256 KiB tile per
+// (256-token tile, 256-row block of a shard's packed gate/up rows).
+int64_t gateup_saved_bytes(int64_t T, int64_t F, int P, int swiglu);
 
 // fp32 path.
 hipError_t launch_gateup_f32(const F32Args& a, hipStream_t st);

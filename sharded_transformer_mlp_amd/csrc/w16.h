@@ -341,6 +341,36 @@ struct RowSrc {
     }
 };
 
+// A 256 x 256 tile's accumulators in the saved-activation layout: wave w's
+// accumulator (i, j) of lane l is the f32x4 at ((tile * NW + w) * 64 +
+// i * TN + j) * 64 + l, so that each store or load instruction moves 1 KiB of
+// contiguous memory. Each instruction's base is wave-uniform (scalar
+// registers) and the lane offset the only vector address, which keeps the
+// 64 stores from tying up vector registers for addresses. Nontemporal both
+// ways: a forward writes them for a backward that runs much later.
+__device__ __forceinline__ void save_acc(float* __restrict__ base, int64_t tile, int w, int lane,
+                                         const f32x4 (&acc)[TM][TN]) {
+    f32x4* p = reinterpret_cast<f32x4*>(base) + (tile * NW + w) * (TM * TN * 64);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            f32x4* q = static_cast<f32x4*>(uniform_ptr(p + (i * TN + j) * 64));
+            __builtin_nontemporal_store(acc[i][j], q + lane);
+        }
+}
+__device__ __forceinline__ void load_acc(const float* __restrict__ base, int64_t tile, int w, int lane,
+                                         f32x4 (&acc)[TM][TN]) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(base) + (tile * NW + w) * (TM * TN * 64);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const f32x4* q = static_cast<const f32x4*>(uniform_ptr(p + (i * TN + j) * 64));
+            acc[i][j] = __builtin_nontemporal_load(q + lane);
+        }
+}
+
 // Ring bookkeeping: byte-free element offsets of the stage/super-stage that
 // step t loads into and the one whose fragments it reads.
 struct Ring {

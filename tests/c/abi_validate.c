@@ -60,6 +60,13 @@ int main(void) {
 
     expect("forward: NULL handle", tsp_mlp_forward(NULL, 1, fake, (float*)fake, NULL), TSP_ERR_INVALID_ARG);
     expect("destroy: NULL handle", tsp_mlp_destroy(NULL), TSP_OK);
+    expect("forward_train: NULL handle", tsp_mlp_forward_train(NULL, 1, fake, (float*)fake, fake, 1 << 20, NULL),
+           TSP_ERR_INVALID_ARG);
+    expect("backward_saved: NULL handle", tsp_mlp_backward_saved(NULL, 1, fake, fake, fake, 1 << 20, (float*)fake,
+                                                                 (float*)fake, (float*)fake, (float*)fake, NULL),
+           TSP_ERR_INVALID_ARG);
+    int64_t nb = 0;
+    expect("saved_bytes: NULL handle", tsp_mlp_saved_bytes(NULL, 1, &nb), TSP_ERR_INVALID_ARG);
     expect("set_path: NULL handle", tsp_mlp_set_path(NULL, 0), TSP_ERR_INVALID_ARG);
     expect("set_tiles: NULL handle", tsp_mlp_set_tiles(NULL, 5, 5), TSP_ERR_INVALID_ARG);
     expect("set_timing: NULL handle", tsp_mlp_set_timing(NULL, 1), TSP_ERR_INVALID_ARG);
