@@ -86,7 +86,8 @@ BWD_CASES = [
 @pytest.mark.parametrize("name,w", BWD_CASES, ids=[c[0] for c in BWD_CASES])
 def test_backward_with_poisoned_lds(name, w):
     """The backward kernels stage operands and results in LDS too: NaN in a
-    gradient means a read ran ahead of its data."""
+    gradient means a read ran ahead of its data. The backward from saved
+    pre-activations (same epilogue, no product) must give the same bits."""
     from sharded_transformer_mlp_amd.inputs import make_output_grad
     assert binding.LIB_PATH == DEBUG_LIB
     say(f"[gpu] LDS poison: {name}")
@@ -95,9 +96,14 @@ def test_backward_with_poisoned_lds(name, w):
     wg = None if inp.w_gate is None else inp.w_gate.to(dev)
     wu, wd = inp.w_up.to(dev), inp.w_down.to(dev)
     mlp = binding.TspMLP(wg, wu, wd, w.P, order=w.order(), act=w.act, T_max=w.T)
-    g = mlp.backward(inp.x.to(dev), dy.to(dev))
+    x, d_y = inp.x.to(dev), dy.to(dev)
+    g = mlp.backward(x, d_y)
+    _, saved = mlp.forward_train(x)
+    gs = mlp.backward(x, d_y, saved=saved)
     torch.cuda.synchronize()
     mlp.close()
+    for k in g:
+        assert (g[k] is None and gs[k] is None) or torch.equal(g[k], gs[k]), f"{name} {k}: saved != recomputed"
     f = lambda t: None if t is None else t.float().numpy()
     ref = oracle.mlp_backward(f(inp.x), f(inp.w_gate), f(inp.w_up), f(inp.w_down), f(dy), w.P, w.order(), w.act)
     for k, r in ref.items():
