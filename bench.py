@@ -81,7 +81,9 @@ def log(*a):
 
 def kernel_source_hash(kernel: str) -> str:
     """Hash of the code (comments and blank lines removed) of the sources a
-    kernel is built from: counter summaries stay valid across comment edits."""
+    kernel is built from, and of the file-specific compiler options the build
+    gives them: counter summaries stay valid across comment edits."""
+    from sharded_transformer_mlp_amd.build import EXTRA_FLAGS
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "sharded_transformer_mlp_amd", "csrc", f)) as fh:
@@ -89,6 +91,8 @@ def kernel_source_hash(kernel: str) -> str:
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
         h.update("\n".join(line for line in lines if line.strip()).encode())
+        if f in EXTRA_FLAGS:
+            h.update(" ".join(EXTRA_FLAGS[f]).encode())
     return h.hexdigest()[:16]
 
 
