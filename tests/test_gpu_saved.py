@@ -148,6 +148,29 @@ def test_saved_pair_llama_shape():
     mlp.close()
 
 
+def test_saved_pair_beyond_2gib():
+    """The 70B shape (d 8192, f 28672, P 8) at a ragged T of 10000 tokens: a
+    saved buffer of 40 token tiles x 56 MiB = 2.35 GB, past the 2 GiB that a
+    32-bit offset reaches, against the recomputing path bit for bit."""
+    w = workload("long70b").with_(T=10000)
+    say("[gpu] saved pair 70b shape T=10000 (saved buffer beyond 2 GiB)")
+    inp, dy = make_inputs(w), make_output_grad(w)
+    dev = torch.device("cuda:0")
+    x, d_y = inp.x.to(dev).contiguous(), dy.to(dev).contiguous()
+    mlp = _handle(w, inp)
+    assert mlp.saved_bytes(w.T) == 40 * 8 * 28 * 256 * 1024 > 2 ** 31
+    y_t, saved = mlp.forward_train(x)
+    y_f = mlp.forward(x)
+    g_s = mlp.backward(x, d_y, saved=saved)
+    g_r = mlp.backward(x, d_y)
+    torch.cuda.synchronize()
+    assert torch.equal(y_t, y_f)
+    for k in KEYS:
+        assert torch.equal(g_s[k], g_r[k]), k
+    assert all(torch.isfinite(g_s[k]).all() for k in KEYS)
+    mlp.close()
+
+
 def test_saved_pair_errors():
     from sharded_transformer_mlp_amd.binding import TSP_ERR_INVALID_ARG, TSP_ERR_UNSUPPORTED, TspError, lib
     dev = torch.device("cuda:0")
