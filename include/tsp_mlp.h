@@ -188,8 +188,9 @@ tsp_status_t tsp_mlp_backward(tsp_mlp_t h, int64_t T, const void* X, const void*
  * KiB, n = 2F / 256 for SwiGLU, F / 256 for GeLU). TSP_ERR_INVALID_ARG for a
  * NULL argument or T outside [0, T_max].
  *
- * tsp_mlp_forward_train: tsp_mlp_forward (Y bit for bit the same as
- * tsp_mlp_forward's with the same tile settings for the down product) that
+ * tsp_mlp_forward_train: tsp_mlp_forward (Y bit for bit that of a
+ * tsp_mlp_forward on the tiled path with gate/up tile shape 0, the automatic
+ * choice at large T, and the same down tile setting) that
  * also writes the pre-activations to `saved`, a caller-owned device buffer of
  * saved_bytes >= tsp_mlp_saved_bytes(T) bytes, 16-byte aligned, overlapping
  * neither X nor Y. Its layout is private to the library. It always runs the
