@@ -35,6 +35,13 @@
  * (no exceptions, no aborts). Arguments are checked before any HIP call; on a
  * failed check nothing is launched and nothing is allocated.
  * tsp_last_error() returns a message for the calling thread's last failure.
+ *
+ * Graphs: tsp_mlp_forward, tsp_mlp_forward_static, tsp_mlp_forward_train and,
+ * after a first call on the handle (which allocates the backward workspace),
+ * tsp_mlp_backward and tsp_mlp_backward_saved only launch kernels on the
+ * given stream (with kernel timing off), so they can be captured into a HIP
+ * graph on that stream and replayed; a replay reads the buffers' contents at
+ * replay time.
  */
 #ifndef TSP_MLP_H
 #define TSP_MLP_H
