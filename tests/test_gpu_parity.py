@@ -381,6 +381,33 @@ def test_full_long70b():
     _full("70b-long-swiglu-bf16-T16384-d8192-f28672-P8", 512)   # all 164 outlier rows + 348 random rows
 
 
+def test_tokens_beyond_32bit_offsets():
+    """T x d = 2^30 bf16 tokens (X of 2 GiB): the gate/up kernel's token loads
+    then take 64-bit addresses instead of 32-bit buffer offsets (the path no
+    other workload reaches). Sampled rows across the whole range, the first
+    and the last included, against the oracle."""
+    w = Workload("big", T=131072, d=8192, f=1024, P=2, act="swiglu", dtype="bf16", seed=48, r0=1)
+    assert w.T * w.d * 2 >= 1 << 31
+    say("[gpu] T=131072 d=8192 (X of 2 GiB): generating inputs")
+    inp = make_inputs(w)
+    from sharded_transformer_mlp_amd.binding import TspMLP
+    dev = torch.device("cuda:0")
+    say("[gpu] T=131072 d=8192: forward on the GPU")
+    mlp = TspMLP(inp.w_gate.to(dev), inp.w_up.to(dev), inp.w_down.to(dev), w.P, order=w.order(), act=w.act,
+                 T_max=w.T)
+    y = mlp.forward(inp.x.to(dev))
+    torch.cuda.synchronize()
+    rows = sample_rows(w.T, 64, seed=49, must_include=torch.tensor([0, 65535, 65536, w.T - 1]))
+    assert bool(torch.isfinite(y).all())
+    got = y[rows.to(dev)].cpu().double().numpy()
+    mlp.close()
+    del y
+    yref = oracle.mlp_forward(_np(inp.x[rows]), _np(inp.w_gate), _np(inp.w_up), _np(inp.w_down), w.P,
+                              w.order(), w.act)
+    emax, el2 = check(w, got, yref, "T=131072 d=8192")
+    say(f"[gpu]   e_max={emax:.3e} e_L2={el2}")
+
+
 def test_ceiling_probes_are_plausible():
     """The measurement probes run and return rates inside physical bounds
     (MI355X datasheet: 8 TB/s HBM, 2.5 PFLOP/s dense bf16)."""
