@@ -162,6 +162,49 @@ def test_backward_full_size_sampled(name):
         assert np.all(np.isfinite(g)) and e2 <= EL2 and em <= EMAX, name
 
 
+def test_backward_beyond_32bit_offsets():
+    """T = 131072 tokens of d = 8192 (X, dY and their transposes 2 GiB each):
+    every backward kernel then takes 64-bit addresses instead of 32-bit
+    buffer offsets for its operands (dH, the recomputed gate/up product and
+    the grouped weight-gradient launch). dX on sampled token rows (the first
+    and the last included) and the weight gradients on sampled hidden
+    columns, against the oracle."""
+    w = Workload("big", T=131072, d=8192, f=1024, P=2, act="swiglu", dtype="bf16", seed=69, r0=1)
+    assert w.T * w.d * 2 >= 1 << 31
+    say("[gpu] backward T=131072 d=8192: generating inputs")
+    inp, dy = make_inputs(w), make_output_grad(w)
+    from sharded_transformer_mlp_amd.binding import TspMLP
+    dev = torch.device("cuda:0")
+    mlp = TspMLP(inp.w_gate.to(dev), inp.w_up.to(dev), inp.w_down.to(dev), w.P, order=w.order(), act=w.act,
+                 T_max=w.T)
+    say("[gpu] backward T=131072 d=8192 on the GPU")
+    g = mlp.backward(inp.x.to(dev), dy.to(dev))
+    torch.cuda.synchronize()
+    rows = sample_rows(w.T, 16, seed=93, must_include=torch.tensor([0, 65536, w.T - 1])).numpy()
+    cols = np.sort(np.random.default_rng(94).choice(w.f, 8, replace=False))
+    for k in KEYS:
+        assert bool(torch.isfinite(g[k]).all()), k
+    got = {"dX rows": g["dX"][torch.from_numpy(rows).to(dev)].cpu().double().numpy(),
+           "dW_gate cols": g["dW_gate"][:, cols].cpu().double().numpy(),
+           "dW_up cols": g["dW_up"][:, cols].cpu().double().numpy(),
+           "dW_down rows": g["dW_down"][cols, :].cpu().double().numpy()}
+    mlp.close()
+    del g
+    say("[gpu] backward T=131072 d=8192: oracle on sampled rows and columns")
+    X, dY = _np(inp.x), _np(dy)
+    ref_rows = oracle.mlp_backward(X[rows], _np(inp.w_gate), _np(inp.w_up), _np(inp.w_down), dY[rows], w.P,
+                                   w.order(), w.act)["dX"]
+    refc = oracle.mlp_backward_columns(X, _np(inp.w_gate), _np(inp.w_up), _np(inp.w_down), dY, cols, w.act)
+    pairs = {"dX rows": ref_rows, "dW_gate cols": refc["dW_gate"], "dW_up cols": refc["dW_up"],
+             "dW_down rows": refc["dW_down"]}
+    for name, r in pairs.items():
+        gg = got[name]
+        e2 = float(np.linalg.norm(gg - r) / np.linalg.norm(r))
+        em = float(np.max(np.abs(gg - r)) / np.max(np.abs(r)))
+        say(f"[gpu]   {name}: e_L2 {e2:.2e} e_max {em:.2e}")
+        assert e2 <= EL2 and em <= EMAX, name
+
+
 def test_backward_unsupported_and_invalid():
     from sharded_transformer_mlp_amd.binding import TSP_ERR_INVALID_ARG, TSP_ERR_UNSUPPORTED, TspError, TspMLP
     dev = torch.device("cuda:0")
