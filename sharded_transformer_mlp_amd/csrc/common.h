@@ -63,8 +63,7 @@ __device__ inline int xcd_remap(int bid, int nwg) {
 
 // Token-tile-grouped raster over a (tokens x features) tile grid: GT token
 // tiles share each feature tile, consecutive ids walk the token tiles first.
-__device__ inline void raster(int L, int n_f, int n_t, int& ttile, int& flin) {
-    constexpr int GT = 8;
+__device__ inline void raster(int L, int n_f, int n_t, int& ttile, int& flin, int GT = 8) {
     const int group = L / (GT * n_f);
     const int first = group * GT;
     const int gt = min(GT, n_t - first);

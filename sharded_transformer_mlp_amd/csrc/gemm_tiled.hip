@@ -398,7 +398,7 @@ __global__ __launch_bounds__(256) void gateup_w16(Bf16Args a, int n_ft_shard, in
     __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
     poison_lds(lds, sizeof(lds));
     int ttile, flin;
-    raster(xcd_remap(blockIdx.x, gridDim.x), a.P * n_ft_shard, n_tt, ttile, flin);
+    raster(xcd_remap(blockIdx.x, gridDim.x), a.P * n_ft_shard, n_tt, ttile, flin, a.gt);
     const int s = flin / n_ft_shard;
     const int ftile = flin - s * n_ft_shard;
     const int64_t a_rs = (int64_t)(a.d >> 4) * 512;
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(256) void down_w16(Bf16Args a, int n_ft, int n_tt, 
     const int lin = xcd_remap(blockIdx.x, gridDim.x);
     const int g = lin / n_tiles;
     int ttile, ftile;
-    raster(lin - g * n_tiles, n_ft, n_tt, ttile, ftile);
+    raster(lin - g * n_tiles, n_ft, n_tt, ttile, ftile, a.gt);
     const int spp = a.F >> 5;
     const int steps_per_group = a.P / split;
     const int64_t a_rs = (int64_t)(a.F >> 4) * 512;
@@ -626,10 +626,17 @@ hipError_t launch_gateup_tiled(const Bf16Args& a, int cfg, hipStream_t st) {
             // slab (8 rows of 32 x d-element blocks) must each span < 2^31 bytes
             const bool buf = (int64_t)a.T * a.d * 2 < (int64_t(1) << 31) && (int64_t)a.d * 512 < (int64_t(1) << 31);
             const bool blk = a.nbt > 0;
+            // raster groups sized so that the token slabs the eight XCDs'
+            // current groups stream (8 x GT x 256 rows x d bf16) take at most
+            // half of the 256 MB last-level cache: GT = 8 at d = 4096, 4 at
+            // d = 8192 (measured: 70B long gate/up -2.7 % against 8, Llama
+            // shape unchanged)
+            Bf16Args b = a;
+            b.gt = std::max(2, std::min(8, 32768 / a.d));
 #define TSP_GU(ACT, BUF, BLK)                                                                             \
     do {                                                                                                  \
-        if (a.save) hipLaunchKernelGGL((gateup_w16<ACT, BUF, BLK, true>), grid, dim3(256), 0, st, a, n_ft_shard, n_tt); \
-        else hipLaunchKernelGGL((gateup_w16<ACT, BUF, BLK, false>), grid, dim3(256), 0, st, a, n_ft_shard, n_tt);     \
+        if (a.save) hipLaunchKernelGGL((gateup_w16<ACT, BUF, BLK, true>), grid, dim3(256), 0, st, b, n_ft_shard, n_tt); \
+        else hipLaunchKernelGGL((gateup_w16<ACT, BUF, BLK, false>), grid, dim3(256), 0, st, b, n_ft_shard, n_tt);     \
     } while (0)
             if (a.swiglu) {
                 if (buf) { if (blk) TSP_GU(1, true, true); else TSP_GU(1, true, false); }
@@ -660,7 +667,11 @@ hipError_t launch_down_tiled(const Bf16Args& a, int cfg, int split, hipStream_t 
             // nbt 1 KiB token blocks; row-major H: T x f)
             const bool buf = (int64_t)a.F * 512 < (int64_t(1) << 31) &&
                              (a.nbt ? (int64_t)a.nbt * 1024 : (int64_t)a.T * a.f * 2) < (int64_t(1) << 31);
-#define TSP_DN(BLK, BUF) hipLaunchKernelGGL((down_w16<BLK, BUF>), grid, dim3(256), 0, st, a, n_ft, n_tt, split)
+            // raster groups of 4 token tiles (measured against 8: Llama down
+            // -0.7 %, GeLU -1.7 %, 70B long -1.6 %)
+            Bf16Args b = a;
+            b.gt = 4;
+#define TSP_DN(BLK, BUF) hipLaunchKernelGGL((down_w16<BLK, BUF>), grid, dim3(256), 0, st, b, n_ft, n_tt, split)
             if (a.nbt) { if (buf) TSP_DN(true, true); else TSP_DN(true, false); }
             else { if (buf) TSP_DN(false, true); else TSP_DN(false, false); }
 #undef TSP_DN

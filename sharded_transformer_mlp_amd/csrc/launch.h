@@ -28,6 +28,9 @@ struct Bf16Args {
     // gate and up pre-activations, fp32) in the saved-activation layout (see
     // w16::save_acc), gateup_saved_bytes(T, F, P, swiglu) bytes.
     float* save = nullptr;
+    // Token tiles per raster group of the tile shape 0 kernels (set from the
+    // shape by launch_gateup_tiled and launch_down_tiled)
+    int gt = 8;
 };
 
 struct F32Args {
