@@ -159,3 +159,36 @@ def test_backward_and_training_pair_graph_replays(name, w):
         assert torch.equal(got_y, y_ref), f"{name}: training forward replay {rep} differs"
     del graph_bwd, graph_pair
     mlp.close()
+
+
+def test_attention_forward_graph_replays():
+    """One rank's attention block (projection, attention over the context the
+    other ranks filled, output projection) captured and replayed on new rank
+    tokens: every replay bitwise equal to the eager forward."""
+    from sharded_transformer_mlp_amd.binding import TspAttn
+    from sharded_transformer_mlp_amd.inputs import AttnWorkload, make_attn_inputs
+    say("[gpu] graph: attention forward")
+    w = AttnWorkload("g", T=96, d=512, H=8, Hkv=4, dh=128, P=4, rank=2, seed=78, causal=True)
+    inp = make_attn_inputs(w)
+    dev = torch.device("cuda:0")
+    attn = TspAttn(inp.w_q.to(dev), inp.w_k.to(dev), inp.w_v.to(dev), inp.w_o.to(dev), w.H, w.Hkv, w.P,
+                   order=w.order(), causal=w.causal, T_max=w.T)
+    x_all = inp.x_all.to(dev)
+    for rho in range(w.P):
+        if rho != w.rank:
+            attn.project_kv(x_all[rho * w.T:(rho + 1) * w.T].contiguous(), rho)
+    x = x_all[w.rank * w.T:(w.rank + 1) * w.T].contiguous()
+    y = torch.empty(w.T, w.d, dtype=torch.float32, device=dev)
+    g = _capture(lambda: attn.forward(x, w.rank, y=y))
+    for rep in range(3):
+        xn = make_attn_inputs(w.with_(seed=3000 + rep)).x_all[:w.T].to(dev)
+        x.copy_(xn)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = y.clone()
+        ref = attn.forward(x, w.rank)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), f"attention replay {rep} differs from the eager forward"
+    del g
+    attn.close()
