@@ -97,7 +97,9 @@ tsp_status_t tsp_attn_project_kv(tsp_attn_t h, int64_t T, int32_t rank, const vo
  * in the context), attention over the context, and the output projection,
  * head group by head group in the handle's order. Asynchronous on `stream`;
  * one forward or projection in flight per handle (they share the workspace
- * and the context). Y must not overlap X.
+ * and the context). Y must not overlap X. It only launches kernels on
+ * `stream` (with kernel timing off), so it can be captured into a HIP graph
+ * and replayed.
  */
 tsp_status_t tsp_attn_forward(tsp_attn_t h, int64_t T, int32_t rank, const void* X, float* Y,
                               hipStream_t stream);
