@@ -30,10 +30,17 @@ namespace tsp {
 // the V^T fragment is one 16-byte read. Scores are kept in log2 units (scale log2(e)/sqrt(dh))
 // and exponentiated with v_exp_f32.
 //
-// Context tiles reach LDS by DMA (global_load_lds, 16 bytes per lane, two
-// buffers): K as 64 rows of 256 bytes with the 16-byte chunk c of row r at
-// c ^ (r & 15), V^T as 128 rows of 128 bytes with chunk c at c ^ ((r >> 1) & 7);
-// both make the fragment reads of 16 rows hit distinct banks.
+// Context tiles reach LDS by DMA (buffer loads into LDS, 16 bytes per lane;
+// K in three buffers, V^T in two): K as 64 rows of 256 bytes with the 16-byte
+// chunk c of row r at c ^ (r & 15), V^T as 128 rows of 128 bytes with chunk c
+// at c ^ ((r >> 1) & 7); both make the fragment reads of 16 rows hit distinct
+// banks. All buffers (and the restart flag) live in one LDS array: with one
+// array per operand the compiler tells the arrays apart and, before every
+// fragment read, waits for the newest DMA into that array, i.e. for the next
+// tile's prefetch, in the middle of the current tile (13 % of the kernel's
+// time). The loop orders its reads itself: every tile ends with vmcnt(0) and
+// a barrier, and a buffer is reloaded only after the barrier that follows its
+// last read.
 //
 // Softmax with a fixed exponent reference per query instead of a running
 // maximum: the first block's maximum. O / l does not depend on the reference,
@@ -52,6 +59,8 @@ namespace tsp {
 
 constexpr int ATT_KROW = 128;   // K tile row (elements)
 constexpr int ATT_VROW = 64;    // V^T tile row (elements)
+constexpr int ATT_K_ELEMS = 3 * 64 * ATT_KROW;   // three K tiles
+constexpr int ATT_V_ELEMS = 2 * 128 * ATT_VROW;  // two V^T tiles
 
 __device__ __forceinline__ void att_vm_zero() {
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
@@ -74,10 +83,11 @@ __device__ inline f16x8 att_pack8(f32x4 lo, f32x4 hi) {
 constexpr int QT = 4;
 
 __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint16_t k_lds[3][64 * ATT_KROW];
-    __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][128 * ATT_VROW];
-    poison_lds(k_lds, sizeof(k_lds));
-    poison_lds(v_lds, sizeof(v_lds));
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[ATT_K_ELEMS + ATT_V_ELEMS + 128];
+    uint16_t* const k_lds = lds;
+    uint16_t* const v_lds = lds + ATT_K_ELEMS;
+    int* const restart_flag = reinterpret_cast<int*>(lds + ATT_K_ELEMS + ATT_V_ELEMS);
+    poison_lds(lds, (ATT_K_ELEMS + ATT_V_ELEMS) * 2);
 
     // heaviest query tiles first; consecutive workgroups (different XCDs)
     // take different key/value heads, so each XCD's L2 streams few contexts
@@ -133,7 +143,7 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
             (void*)(a.kc + (int64_t)kb * 64 * a.ldk + kv_col), (short)0, 0x7fffffff, kRawBufferWord3);
 #pragma unroll
         for (int i = 0; i < QT; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (TSP_LDS void*)&k_lds[buf][(w * QT + i) * 512], 16, k_off[i],
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (TSP_LDS void*)(k_lds + buf * 64 * ATT_KROW + (w * QT + i) * 512), 16, k_off[i],
                                                      0, 0, 0);
     };
     auto load_v = [&](int kb, int buf) {
@@ -141,11 +151,10 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
             (void*)(a.vt + kv_col * a.ldv + kb * 64), (short)0, 0x7fffffff, kRawBufferWord3);
 #pragma unroll
         for (int i = 0; i < QT; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (TSP_LDS void*)&v_lds[buf][(w * QT + i) * 512], 16, v_off[i],
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (TSP_LDS void*)(v_lds + buf * 128 * ATT_VROW + (w * QT + i) * 512), 16, v_off[i],
                                                      0, 0, 0);
     };
 
-    __shared__ int restart_flag;
     f32x4 o[8][QT];
     float m[QT], l[QT];
 #pragma unroll
@@ -160,7 +169,7 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
             kf[u] = *reinterpret_cast<const f16x8*>(
-                &k_lds[buf][((2 * h + u) * 16 + n16) * ATT_KROW + ((4 * ks + g) ^ n16) * 8]);
+                k_lds + buf * 64 * ATT_KROW + ((2 * h + u) * 16 + n16) * ATT_KROW + ((4 * ks + g) ^ n16) * 8);
     };
     // init[t]: the accumulators' start for ks == 0 (zero, or minus the
     // query's reference so that the scores come out already shifted)
@@ -227,7 +236,7 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
     // V^T fragment dt of half h (the 8 keys lane group g multiplies)
     auto read_v = [&](int buf, int h, int dt) {
         const int r = dt * 16 + n16;
-        return *reinterpret_cast<const f16x8*>(&v_lds[buf][r * ATT_VROW + ((4 * h + g) ^ ((r >> 1) & 7)) * 8]);
+        return *reinterpret_cast<const f16x8*>(v_lds + buf * 128 * ATT_VROW + r * ATT_VROW + ((4 * h + g) ^ ((r >> 1) & 7)) * 8);
     };
     // O^T += V^T P^T over half h of the V^T tile in buffer `buf`, fragments
     // read two ahead; vf holds the first two (read early by the caller)
@@ -278,7 +287,7 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
     n_full = min(n_full, min(nkb, a.S / 64));
 
     for (int attempt = 0; attempt < 2; ++attempt) {
-        if (tid == 0) restart_flag = 0;
+        if (tid == 0) *restart_flag = 0;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -351,9 +360,9 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
         bool over = false;
 #pragma unroll
         for (int t = 0; t < QT; ++t) over |= !(l[t] <= 65000.0f);
-        if (__any(over)) restart_flag = 1;
+        if (__any(over)) *restart_flag = 1;
         __syncthreads();
-        if (!restart_flag) break;                        // same value in every wave
+        if (!*restart_flag) break;                        // same value in every wave
         // rare: take every query's true maximum over all keys, start again
         for (int kb = 0; kb < nkb; ++kb) {
             load_k(kb, 0);
