@@ -45,11 +45,10 @@ def sources():
 
 # Per-source codegen options: the attention kernel keeps its MFMA results in
 # vector registers (its softmax reads every score; results in accumulation
-# registers were copied out one by one), and is scheduled for instruction-level
-# parallelism (its loop is not fenced by scheduling barriers; measured 1 %
-# faster than the default scheduler, bitwise equal). The 256 x 256 kernels,
-# whose loops are fenced, measured no gain or spilled with other schedulers.
-EXTRA_FLAGS = {"attn_core.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# registers were copied out one by one). Other scheduling strategies than the
+# default measured no gain or spilled registers, for the attention kernel at
+# two waves per SIMD and for the fenced 256 x 256 kernels.
+EXTRA_FLAGS = {"attn_core.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 # Every kernel's register use is reported by the compiler; a kernel that

@@ -17,9 +17,10 @@ namespace tsp {
 
 // ------------------------------------------------------------------ attention
 //
-// Workgroup: 4 waves, each 64 queries of one head against 64-key blocks of
-// the context; the 4 waves share the key/value head (hw heads x qs query
-// sub-tiles, hw * qs = 4), so one K tile and one V tile in LDS serve them all.
+// Workgroup: 16 / QT waves, each 16 QT queries of one head against 64-key
+// blocks of the context; the waves share the key/value head (hw heads x qs
+// 64-query sub-tiles, hw * qs = 4), so one K tile and one V tile in LDS serve
+// them all.
 // With v_mfma_f32_16x16x32_f16 a wave computes S^T = K Q^T (keys as rows:
 // lane l holds 4 consecutive keys of query l % 16), so a query's softmax
 // statistics sit in one lane column and reduce with two cross-lane steps; the
@@ -76,11 +77,12 @@ __device__ inline f16x8 att_pack8(f32x4 lo, f32x4 hi) {
 }
 
 // QT query tiles of 16 per wave, 16 / QT waves per workgroup: 64 query rows
-// per four waves either way. QT = 4 (one wave per SIMD) is kept: QT = 2 (two
-// waves per SIMD, one wave's softmax beside the other's MFMAs) measured 4 %
-// slower, the VALU and matrix work of a SIMD overlapping no better across
-// waves than within one.
-constexpr int QT = 4;
+// per four waves either way. QT = 2 is kept: two waves per SIMD (230 vector
+// registers each), one wave's softmax and fragment reads beside the other's
+// MFMAs, measured 4 % faster than QT = 4 (one wave per SIMD, 128 query rows
+// per SIMD in flight); each K or V^T fragment read then feeds two MFMAs
+// instead of four.
+constexpr int QT = 2;
 
 __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) uint16_t lds[ATT_K_ELEMS + ATT_V_ELEMS + 128];
