@@ -58,7 +58,6 @@ KERNEL_SOURCES = {
     "bwd_dh": ["backward.hip", "w16.h", "common.h"],
     "bwd_gateup": ["backward.hip", "w16.h", "common.h"],
     "bwd_dw_dx": ["backward.hip", "w16.h", "common.h"],
-    "bwd_transpose_in": ["backward.hip", "common.h"],
     "bwd_saved": ["backward.hip", "w16.h", "common.h"],
     "gateup_save": ["gemm_tiled.hip", "w16.h", "common.h"],
     "attn_qkv": ["attn.hip", "w16.h", "common.h"],
@@ -101,16 +100,14 @@ def kernel_work(w, kernel: str, T: int):
     es = 2 if w.dtype == "bf16" else 4
     n_gu = 2 if w.act == "swiglu" else 1
     d, f = w.d, w.f
-    if kernel == "bwd_dh":                  # dH = dY.Wd^T: Wd, dY in, fp32 dH out
-        return 2 * T * d * f, f * d * es + T * d * es + T * f * 4
+    if kernel == "bwd_dh":                  # dH = dY.Wd^T: Wd, dY in, fp32 dH out; the same launch copies X and dY transposed
+        return 2 * T * d * f, f * d * es + T * d * es + T * f * 4 + 2 * 2 * T * d * es
     if kernel == "bwd_gateup":              # recomputed gate/up product + backward epilogue
         return 2 * n_gu * T * d * f, n_gu * d * f * es + T * d * es + T * f * 4 + (n_gu + 1) * T * f * es
     if kernel == "bwd_dw_dx":               # weight gradients and dX = sum dG.Wg^T + dU.Wu^T, one launch
         return ((2 * n_gu + 2) * T * d * f + 2 * n_gu * T * d * f,
                 2 * T * d * es + (n_gu + 1) * T * f * es + (n_gu + 1) * d * f * 4      # dW: X, dY, dG/dU, H in, dW out
                 + n_gu * d * f * es + n_gu * T * f * es + T * d * 4)                  # dX: Wg/Wu, dG/dU in, dX out
-    if kernel == "bwd_transpose_in":        # copies of X and dY: each byte read and written once
-        return 0, 2 * 2 * T * d * es
     if kernel == "bwd_saved":               # the backward epilogue on saved pre-activations (no product)
         return 0, n_gu * T * f * 4 + T * f * 4 + (n_gu + 1) * T * f * es
     if kernel == "gateup_save":             # the gate/up product that also writes its pre-activations

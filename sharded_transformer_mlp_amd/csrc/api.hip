@@ -591,19 +591,18 @@ static tsp_status_t backward_impl(tsp_mlp_t h, int64_t T, const void* X, const v
         h->bwd_unpacked = true;
     }
 
-    tsp_status_t s = timed_launch(h, "bwd_transpose_in", st, [&] {
-        hipError_t e = tsp::launch_transpose_bf16(x16, (int)T, (int)d, (int)d, xt, Tp, 0, st);
-        return e != hipSuccess ? e : tsp::launch_transpose_bf16(dy16, (int)T, (int)d, (int)d, dyt, Tp, 1, st);
-    });
-    if (s != TSP_OK) return s;
-    // dH[t][c] = sum_n dY[t][n] Wd[c][n], natural hidden columns
+    // dH[t][c] = sum_n dY[t][n] Wd[c][n], natural hidden columns; the same
+    // launch transposes X (row-major X^T) and dY (dY^T in fragment blocks)
+    // for the weight gradients, on the CUs dH's last partial round leaves idle
+    const tsp::TransposeJob tps[2] = {{x16, xt, (int)T, (int)d, (int)d, Tp, 0},
+                                      {dy16, dyt, (int)T, (int)d, (int)d, Tp, 1}};
     tsp::NtArgs p{};
     p.a_base[0] = p.a_base[1] = wd16;
     p.b_base[0] = p.b_base[1] = dy16;
     p.lda = (int)d; p.ldb = (int)d; p.M = (int)f; p.N = (int)T;
     p.spp = (int)(d / 32); p.nseg = 1; p.kinds = 1;
     p.out = dh; p.ldc = f;
-    s = timed_launch(h, "bwd_dh", st, [&] { return tsp::launch_nt(&p, 1, st); });
+    tsp_status_t s = timed_launch(h, "bwd_dh", st, [&] { return tsp::launch_nt(&p, 1, st, tps, 2); });
     if (s != TSP_OK) return s;
     // recompute G, U (H) and form dG, dU, H in ring-ordered hidden columns
     tsp::Bf16Args a{};

@@ -16,7 +16,7 @@
 // operands' reduction index contiguous (RowSrc): the B operand row-major, the
 // A operand row-major (dH: Wd) or in 32 x 16 fragment blocks (dX: Wg, Wu
 // packed once from the records; the weight gradients: dG^T, dU^T written so
-// by the gate/up epilogue, dY^T by transpose_bf16). The token-reduced weight
+// by the gate/up epilogue, dY^T by the transposes of the dH launch). The token-reduced weight
 // gradients read transposed copies of X, dY, dG, dU and H (tokens padded with
 // zeros, or finite values facing zeros, to a multiple of 64).
 #include "common.h"
@@ -30,28 +30,39 @@ namespace tsp {
 // LDS, each thread moving 16 elements (two 16-byte accesses) each way. frag:
 // dst in 32 x 16 fragment blocks (rows c, reduction index r, ld_dst / 16
 // blocks per 32-row block), where a thread's two 8-token runs are the two
-// 16-byte lane slots (l, l + 32) of one block.
-__global__ __launch_bounds__(256) void transpose_bf16(const uint16_t* __restrict__ src, int R, int ld_src,
-                                                      uint16_t* __restrict__ dst, int ld_dst, int frag) {
-    __shared__ uint16_t tile[64][64 + 2];           // 33-word rows: the column reads spread over the banks
-    const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+// 16-byte lane slots (l, l + 32) of one block. The tiles run as extra
+// workgroups of a grouped NT launch (tp_aux), so that they fill the CUs the
+// product's last partial round leaves idle instead of taking a launch of
+// their own.
+typedef uint16_t TpTile[64][64 + 2];                // 33-word rows: the column reads spread over the banks
+
+// Tile (cb, rb) of job j: thread's 16 source elements into v[0..1] (zeros past R).
+__device__ __forceinline__ void tp_load(const TransposeJob& j, int cb, int rb, u32x4 (&v)[2]) {
     const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
-    const int r = r0 + tr;
-    u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
-    if (r < R) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(src + (int64_t)r * ld_src + c0 + tc);
-        v0 = p[0];
-        v1 = p[1];
+    const int r = rb * 64 + tr;
+    v[0] = u32x4{0u, 0u, 0u, 0u};
+    v[1] = u32x4{0u, 0u, 0u, 0u};
+    if (r < j.R) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(j.src + (int64_t)r * j.ld_src + cb * 64 + tc);
+        v[0] = p[0];
+        v[1] = p[1];
     }
+}
+__device__ __forceinline__ void tp_put(TpTile& tile, const u32x4 (&v)[2]) {
+    const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        tile[tr][tc + 2 * e] = (uint16_t)(v0[e] & 0xffffu);
-        tile[tr][tc + 2 * e + 1] = (uint16_t)(v0[e] >> 16);
-        tile[tr][tc + 8 + 2 * e] = (uint16_t)(v1[e] & 0xffffu);
-        tile[tr][tc + 8 + 2 * e + 1] = (uint16_t)(v1[e] >> 16);
+        tile[tr][tc + 2 * e] = (uint16_t)(v[0][e] & 0xffffu);
+        tile[tr][tc + 2 * e + 1] = (uint16_t)(v[0][e] >> 16);
+        tile[tr][tc + 8 + 2 * e] = (uint16_t)(v[1][e] & 0xffffu);
+        tile[tr][tc + 8 + 2 * e + 1] = (uint16_t)(v[1][e] >> 16);
     }
-    __syncthreads();
-    // thread: output row c0 + tr, tokens r0 + tc .. + 15
+}
+// after tp_put of the whole tile and a barrier: thread writes output row
+// c0 + tr, tokens r0 + tc .. + 15
+__device__ __forceinline__ void tp_store(const TpTile& tile, const TransposeJob& j, int cb, int rb) {
+    const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;
+    const int c0 = cb * 64, r0 = rb * 64;
     u32x4 o0, o1;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -59,14 +70,60 @@ __global__ __launch_bounds__(256) void transpose_bf16(const uint16_t* __restrict
         o1[e] = (uint32_t)tile[tc + 8 + 2 * e][tr] | ((uint32_t)tile[tc + 8 + 2 * e + 1][tr] << 16);
     }
     const int64_t row = c0 + tr;
-    if (frag) {
-        u32x4* q = reinterpret_cast<u32x4*>(dst + ((row >> 5) * (ld_dst >> 4) + ((r0 + tc) >> 4)) * 512 + (row & 31) * 8);
+    if (j.frag) {
+        u32x4* q = reinterpret_cast<u32x4*>(j.dst + ((row >> 5) * (j.R_pad >> 4) + ((r0 + tc) >> 4)) * 512 +
+                                            (row & 31) * 8);
         q[0] = o0;                                      // lane slot row % 32: tokens r0 + tc .. + 7
         q[32] = o1;                                     // lane slot row % 32 + 32: the next 8
     } else {
-        u32x4* q = reinterpret_cast<u32x4*>(dst + row * ld_dst + r0 + tc);
+        u32x4* q = reinterpret_cast<u32x4*>(j.dst + row * j.R_pad + r0 + tc);
         q[0] = o0;
         q[1] = o1;
+    }
+}
+
+// Aux workgroup `id` of n_aux: tiles id, id + n_aux, ... of the jobs' tiles
+// taken in order (job 0's C/64 x R_pad/64, then job 1's). TP_DEPTH tiles'
+// loads are in flight at a time; the LDS tile alternates between two
+// buffers, so one barrier per tile separates a buffer's writes from its reads
+// and (two tiles on) its reads from its next writes. The trip count depends
+// on id and the sizes only: every wave of the workgroup reaches every barrier.
+constexpr int TP_DEPTH = 4;
+__device__ __forceinline__ void tp_aux(const TransposeJob j0, const TransposeJob j1, int n_tp, int n_aux, int id,
+                                       uint16_t* lds) {
+    TpTile* tiles = reinterpret_cast<TpTile*>(lds);
+    const int n0 = (j0.C / 64) * (j0.R_pad / 64);
+    const int total = n0 + (n_tp > 1 ? (j1.C / 64) * (j1.R_pad / 64) : 0);
+    // tile t: job, column block cb, row block rb
+    auto locate = [&](int t, int& job, int& cb, int& rb) {
+        job = t < n0 ? 0 : 1;
+        const int u = t < n0 ? t : t - n0;
+        const int ncb = (job ? j1.C : j0.C) / 64;
+        rb = u / ncb;
+        cb = u - rb * ncb;
+    };
+    auto load = [&](int t, u32x4 (&v)[2]) {
+        int job, cb, rb;
+        locate(t, job, cb, rb);
+        tp_load(job ? j1 : j0, cb, rb, v);
+    };
+    u32x4 v[TP_DEPTH][2];
+#pragma unroll
+    for (int k = 0; k < TP_DEPTH; ++k)
+        if (id + k * n_aux < total) load(id + k * n_aux, v[k]);
+    for (int base = id; base < total; base += TP_DEPTH * n_aux) {
+#pragma unroll
+        for (int k = 0; k < TP_DEPTH; ++k) {
+            const int t = base + k * n_aux;
+            if (t < total) {                            // uniform over the workgroup
+                int job, cb, rb;
+                locate(t, job, cb, rb);
+                tp_put(tiles[k & 1], v[k]);
+                __syncthreads();
+                tp_store(tiles[k & 1], job ? j1 : j0, cb, rb);
+                if (t + TP_DEPTH * n_aux < total) load(t + TP_DEPTH * n_aux, v[k]);
+            }
+        }
     }
 }
 
@@ -92,11 +149,15 @@ __global__ __launch_bounds__(256) void nt_w16(NtGroup grp) {
     __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
     poison_lds(lds, sizeof(lds));
     const int bid = blockIdx.x;
+    if (bid >= grp.aux_first) {                         // a transpose workgroup (launch_nt's tps)
+        tp_aux(grp.tp[0], grp.tp[1], grp.n_tp, grp.n_aux, bid - grp.aux_first, lds);
+        return;
+    }
     const int gi = bid < grp.first[1] ? 0 : (bid < grp.first[2] ? 1 : (bid < grp.first[3] ? 2 : 3));
     const NtArgs& p = gi == 0 ? grp.p[0] : (gi == 1 ? grp.p[1] : (gi == 2 ? grp.p[2] : grp.p[3]));
     const int n_mt = p.M / BM, n_nt = (p.N + BN - 1) / BN;
     const int first = gi == 0 ? grp.first[0] : (gi == 1 ? grp.first[1] : (gi == 2 ? grp.first[2] : grp.first[3]));
-    const int next = gi == 0 ? grp.first[1] : (gi == 1 ? grp.first[2] : (gi == 2 ? grp.first[3] : (int)gridDim.x));
+    const int next = gi == 0 ? grp.first[1] : (gi == 1 ? grp.first[2] : (gi == 2 ? grp.first[3] : grp.aux_first));
     const int lin = xcd_remap(bid - first, next - first);
     if (lin >= n_mt * n_nt) return;                     // padding of the product's id range to a multiple of 8
     int ntile, mtile;
@@ -288,15 +349,7 @@ __global__ __launch_bounds__(256) void gateup_bwd_w16(Bf16Args a, BwdArgs b, int
 // ------------------------------------------------------------------ launchers
 static inline int64_t cdiv64(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
-hipError_t launch_transpose_bf16(const uint16_t* src, int R, int C, int ld_src, uint16_t* dst, int R_pad, int frag,
-                                 hipStream_t st) {
-    if (C % 64 || R_pad % 64 || R > R_pad) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(transpose_bf16, dim3((unsigned)(C / 64), (unsigned)(R_pad / 64)), dim3(256), 0, st, src, R,
-                       ld_src, dst, R_pad, frag ? 1 : 0);
-    return hipGetLastError();
-}
-
-hipError_t launch_nt(const NtArgs* probs, int n, hipStream_t st) {
+hipError_t launch_nt(const NtArgs* probs, int n, hipStream_t st, const TransposeJob* tps, int n_tp) {
     using namespace w16;
     if (n < 1 || n > kMaxNt) return hipErrorInvalidValue;
     NtGroup grp{};
@@ -322,6 +375,32 @@ hipError_t launch_nt(const NtArgs* probs, int n, hipStream_t st) {
     }
     for (int i = n; i < kMaxNt; ++i) grp.first[i] = (int)tiles;
     if (tiles > INT32_MAX / 2) return hipErrorInvalidValue;
+    // transposes: as many workgroups as the products' last round leaves CUs
+    // idle (a full round's worth when that is under 64)
+    if (n_tp < 0 || n_tp > kMaxTp || (n_tp > 0 && !tps)) return hipErrorInvalidValue;
+    grp.n_tp = n_tp;
+    grp.aux_first = (int)tiles;
+    grp.n_aux = 0;
+    if (n_tp > 0) {
+        int64_t tp_tiles = 0;
+        for (int i = 0; i < n_tp; ++i) {
+            const TransposeJob& j = tps[i];
+            if (!j.src || !j.dst || j.R < 0 || j.C < 64 || j.C % 64 || j.R_pad % 64 || j.R > j.R_pad || j.R_pad < 64 ||
+                j.ld_src < j.C || j.ld_src % 8)
+                return hipErrorInvalidValue;
+            grp.tp[i] = j;
+            tp_tiles += (int64_t)(j.C / 64) * (j.R_pad / 64);
+        }
+        if (tp_tiles > INT32_MAX / 2) return hipErrorInvalidValue;
+        int dev = 0, n_cu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        n_cu = std::max(n_cu, 1);
+        const int idle = (int)((n_cu - tiles % n_cu) % n_cu);
+        grp.n_aux = (int)std::min<int64_t>(idle >= 64 ? idle : n_cu, tp_tiles);
+        tiles += grp.n_aux;
+    }
     const dim3 grid((unsigned)tiles);
     if (probs[0].a_frag) {
         if (buf) hipLaunchKernelGGL((nt_w16<true, true>), grid, dim3(256), 0, st, grp);

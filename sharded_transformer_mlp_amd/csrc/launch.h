@@ -115,20 +115,32 @@ struct BwdArgs {
     // saved (Bf16Args::save) for the same weights, T and X
     const float* saved = nullptr;
 };
-// frag: dst in 32 x 16 fragment blocks (C rows x R_pad reduction indices)
-// instead of row-major C x R_pad.
-hipError_t launch_transpose_bf16(const uint16_t* src, int R, int C, int ld_src, uint16_t* dst, int R_pad, int frag,
-                                 hipStream_t st);
+// dst[c][r] = src[r][c] (R x C bf16 source, row stride ld_src) for r < R,
+// 0 for R <= r < R_pad; frag: dst in 32 x 16 fragment blocks (C rows x R_pad
+// reduction indices) instead of row-major C x R_pad. C % 64 == 0, R_pad % 64
+// == 0. Runs as extra workgroups of a grouped NT launch (launch_nt).
+struct TransposeJob {
+    const uint16_t* src;
+    uint16_t* dst;
+    int R, C, ld_src, R_pad, frag;
+};
+constexpr int kMaxTp = 2;
 // Row-major M x K (row stride ld) into 32 x 16 fragment blocks (M % 32 == 0,
 // K % 16 == 0, ld % 8 == 0).
 hipError_t launch_pack_frag_bf16(const uint16_t* src, int64_t ld, int M, int K, uint16_t* dst, hipStream_t st);
 // Up to four products in one launch; first[i] is product i's first tile.
 constexpr int kMaxNt = 4;
+// Transposes (up to kMaxTp) may ride along: workgroup ids from aux_first on
+// each walk the jobs' 64 x 64 tiles, n_aux apart. They come after every
+// product tile, so they take the CUs that the products' last partial round
+// leaves idle.
 struct NtGroup {
     NtArgs p[kMaxNt];
     int first[kMaxNt];
+    TransposeJob tp[kMaxTp];
+    int n_tp, aux_first, n_aux;
 };
-hipError_t launch_nt(const NtArgs* probs, int n, hipStream_t st);
+hipError_t launch_nt(const NtArgs* probs, int n, hipStream_t st, const TransposeJob* tps = nullptr, int n_tp = 0);
 hipError_t launch_gateup_bwd(const Bf16Args& a, const BwdArgs& b, hipStream_t st);
 // Bytes of the saved gate/up accumulators for T tokens: one 256 KiB tile per
 // (256-token tile, 256-row block of a shard's packed gate/up rows).
