@@ -252,12 +252,18 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
         }
     };
     // half n+1's scores on the matrix cores while the VALU turns half n's
-    // into probabilities, then half n's P.V
+    // into probabilities, then half n's P.V. That first part runs at raised
+    // wave priority and the P.V MFMAs at the normal one: when the SIMD's other
+    // wave is in its P.V burst, this wave's score MFMAs, fragment reads and
+    // softmax (the chain the next P.V waits on) issue first (measured 1 %
+    // faster, same results; the reverse, raised priority over the P.V burst,
+    // 1 % slower)
     // cur_shifted: cur's scores already have the reference subtracted; the
     // next half's always do (init = minus the reference)
     auto step = [&](int kbuf_next, int h_next, f32x4 (&cur)[2][QT], f32x4 (&nxt)[2][QT], int vbuf, int h,
                     bool cur_shifted, const float (&negref)[QT]) {
         f16x8 pb[QT], kf[2][2], vf[3];
+        __builtin_amdgcn_s_setprio(1);
         read_k(0, kbuf_next, h_next, kf[0]);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -269,6 +275,7 @@ __global__ __launch_bounds__(64 * (16 / QT)) void attn_fwd(AttnArgs a) {
             s_mfma(ks, kf[ks & 1], nxt, negref);
             if (ks % (4 / QT) == 0) softmax_t(cur, ks / (4 / QT), pb, cur_shifted);
         }
+        __builtin_amdgcn_s_setprio(0);
         pv(vbuf, h, pb, vf);
     };
     auto last_step = [&](f32x4 (&cur)[2][QT], int vbuf, int h, bool shifted) {
