@@ -112,3 +112,21 @@ def test_attention_kernel_work_adds_up_to_the_block():
               AttnWorkload("x", T=96, d=512, H=16, Hkv=4, dh=128, P=4, rank=3, seed=0, causal=False)):
         total = sum(bench.attn_kernel_work(w, k)[0] for k in ("attn_qkv", "attn_core", "attn_out"))
         assert total == ao.attention_flops(w.T, w.d, w.H, w.Hkv, w.dh, w.P, w.rank, w.causal)
+
+
+def test_backward_kernel_work_adds_up_to_the_gradients():
+    """The algorithmic flops the backward bench prices its two product launches
+    with (dH; the weight gradients and dX in one launch) add up to the
+    oracle's count of the backward's gradient products, and the dH launch's
+    bytes include the transposed copies of X and dY that ride in it."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import oracle
+    from sharded_transformer_mlp_amd.inputs import Workload, workload
+    for w in (workload("llama8b"), workload("gelu"),
+              Workload("x", T=300, d=512, f=2048, P=4, act="swiglu", dtype="bf16", seed=0)):
+        total = sum(bench.kernel_work(w, k, w.T)[0] for k in ("bwd_dh", "bwd_dw_dx"))
+        assert total == oracle.backward_flops(w.T, w.d, w.f, w.act)
+        _, dh_bytes = bench.kernel_work(w, "bwd_dh", w.T)
+        es = 2
+        assert dh_bytes == w.f * w.d * es + w.T * w.d * es + w.T * w.f * 4 + 4 * w.T * w.d * es
